@@ -1,0 +1,166 @@
+"""CPU oracle of the chunked LZSS coder (FZGPUModules "fz::GPULZStage" page).
+
+TEST INFRASTRUCTURE ONLY.  The test suite, the package smoke check and the
+benchmark's CPU-baseline leg are the only callers allowed.  The product
+package never imports this module, and this module imports nothing from the
+product package: the two share no code.
+
+The arithmetic lives in ``gpulz_oracle.c`` (plain single-threaded C, built
+with gcc into ``liboracle.so`` next to it).  This file only marshals numpy
+buffers through ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gpulz_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+OK, EINVAL, ECAP, ECORRUPT = 0, -1, -2, -3
+HEADER_BYTES = 32
+ENTRY_BYTES = 8
+RAW_BIT = 0x80000000
+
+
+def build(verbose: bool = False) -> str:
+    """Compile liboracle.so with gcc (always recompiles)."""
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-shared", "-fPIC", _SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    global _lib
+    _lib = None
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    u8p = ctypes.c_void_p
+    lib.oracle_max_stream_size.argtypes = [ctypes.c_uint64, ctypes.c_uint32]
+    lib.oracle_max_stream_size.restype = ctypes.c_uint64
+    lib.oracle_hash.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
+    lib.oracle_hash.restype = ctypes.c_uint32
+    lib.oracle_near_match.argtypes = [u8p, ctypes.c_uint32, ctypes.c_uint32,
+                                      ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32)]
+    lib.oracle_near_match.restype = None
+    lib.oracle_level1_candidates.argtypes = [u8p, ctypes.c_uint32, u8p, u8p]
+    lib.oracle_level1_candidates.restype = None
+    lib.oracle_encode_chunk.argtypes = [u8p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                        ctypes.c_uint32, ctypes.POINTER(ctypes.c_uint32),
+                                        ctypes.POINTER(ctypes.c_uint32), u8p,
+                                        ctypes.POINTER(ctypes.c_uint32)]
+    lib.oracle_encode_chunk.restype = ctypes.c_int
+    lib.oracle_encode.argtypes = [u8p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
+                                  ctypes.c_uint32, u8p, ctypes.c_uint64]
+    lib.oracle_encode.restype = ctypes.c_int64
+    lib.oracle_decode.argtypes = [u8p, ctypes.c_uint64, u8p, ctypes.c_uint64]
+    lib.oracle_decode.restype = ctypes.c_int64
+    lib.oracle_stream_info.argtypes = [u8p, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64),
+                                       ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint32),
+                                       ctypes.POINTER(ctypes.c_uint32)]
+    lib.oracle_stream_info.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data) if a.size else None
+
+
+def _bytes(buf) -> np.ndarray:
+    a = np.ascontiguousarray(np.frombuffer(buf, dtype=np.uint8) if isinstance(buf, (bytes, bytearray))
+                             else np.asarray(buf))
+    return a.view(np.uint8).reshape(-1)
+
+
+def max_stream_size(n: int, chunk_size: int) -> int:
+    return int(_load().oracle_max_stream_size(n, chunk_size))
+
+
+def hash2(w0: int, w1: int) -> int:
+    return int(_load().oracle_hash(w0, w1))
+
+
+def near_match(x: np.ndarray, p: int) -> tuple[int, int]:
+    """(L, O) of the exact near-window search at element p of chunk x (uint32)."""
+    x = np.ascontiguousarray(x, dtype=np.uint32)
+    L, O = ctypes.c_uint32(), ctypes.c_uint32()
+    _load().oracle_near_match(_ptr(x), x.size, p, ctypes.byref(L), ctypes.byref(O))
+    return L.value, O.value
+
+
+def level1_candidates(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per-position level-1 candidate offsets (0 = none) and the final table."""
+    x = np.ascontiguousarray(x, dtype=np.uint32)
+    cand = np.zeros(x.size, dtype=np.uint32)
+    table = np.zeros(2048, dtype=np.uint32)
+    _load().oracle_level1_candidates(_ptr(x), x.size, _ptr(cand), _ptr(table))
+    return cand, table
+
+
+def encode_chunk(chunk: bytes | np.ndarray, chunk_size: int, word_size: int, level: int):
+    """Encode one chunk -> (flag_size, data_size, payload bytes)."""
+    a = _bytes(chunk)
+    f, d, pb = ctypes.c_uint32(), ctypes.c_uint32(), ctypes.c_uint32()
+    pay = np.zeros(chunk_size, dtype=np.uint8)
+    st = _load().oracle_encode_chunk(_ptr(a), a.size, chunk_size, word_size, level,
+                                     ctypes.byref(f), ctypes.byref(d), _ptr(pay), ctypes.byref(pb))
+    if st != OK:
+        raise ValueError(f"oracle_encode_chunk status {st}")
+    return f.value, d.value, pay[:pb.value].tobytes()
+
+
+def encode(data, chunk_size: int, word_size: int, level: int) -> np.ndarray:
+    """Encode a whole buffer; returns the stream as a uint8 array."""
+    a = _bytes(data)
+    cap = max_stream_size(a.size, chunk_size)
+    if cap == 0:
+        raise ValueError("unsupported chunk_size")
+    out = np.empty(cap, dtype=np.uint8)
+    r = _load().oracle_encode(_ptr(a), a.size, chunk_size, word_size, level, _ptr(out), cap)
+    if r < 0:
+        raise ValueError(f"oracle_encode status {r}")
+    return out[:r]
+
+
+def decode_status(stream, cap: int | None = None) -> tuple[int, np.ndarray]:
+    """Decode; returns (status_or_size, output array).  Never raises on corruption."""
+    s = _bytes(stream)
+    if cap is None:
+        info = stream_info(s)
+        cap = info[0] if info is not None else 0
+    out = np.zeros(max(cap, 1), dtype=np.uint8)
+    r = int(_load().oracle_decode(_ptr(s) if s.size else ctypes.c_void_p(1), s.size, _ptr(out), cap))
+    return r, out[: max(r, 0)]
+
+
+def decode(stream) -> np.ndarray:
+    r, out = decode_status(stream)
+    if r < 0:
+        raise ValueError(f"oracle_decode status {r}")
+    return out
+
+
+def stream_info(stream):
+    """(original_size, stream_bytes, chunk_size, word_size) or None if the header is invalid."""
+    s = _bytes(stream)
+    n, t = ctypes.c_uint64(), ctypes.c_uint64()
+    cs, ws = ctypes.c_uint32(), ctypes.c_uint32()
+    st = _load().oracle_stream_info(_ptr(s) if s.size else ctypes.c_void_p(1), s.size, ctypes.byref(n),
+                                    ctypes.byref(t), ctypes.byref(cs), ctypes.byref(ws))
+    if st != OK:
+        return None
+    return n.value, t.value, cs.value, ws.value
