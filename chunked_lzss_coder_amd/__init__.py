@@ -1,0 +1,177 @@
+"""Python binding of the gfx950 chunked LZSS coder (``libgpulz.so``).
+
+Argument marshalling only: every step of encode and decode runs in the HIP
+kernels behind the C ABI declared in ``include/gpulz.h``.  PyTorch supplies
+device memory and the current HIP stream.  If the shared library has not been
+built, every call raises; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgpulz.so")
+
+OK, ERR_INVALID_ARG, ERR_CAPACITY, ERR_CORRUPT, ERR_HIP = 0, -1, -2, -3, -4
+STATUS_OK, STATUS_CAPACITY, STATUS_CORRUPT = 0, 2, 3
+SYMBOLS = ("gpulz_max_compressed_size", "gpulz_encode_workspace_size", "gpulz_decode_workspace_size",
+           "gpulz_encode", "gpulz_decode", "gpulz_stream_info", "gpulz_encode_timed", "gpulz_decode_timed")
+
+_lib = None
+
+
+class GpulzError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgpulz.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    try:  # bind to the HIP runtime torch already uses (same soname), never a second one
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(LIB_PATH):
+        raise GpulzError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(LIB_PATH)
+    u64, u32, vp = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p
+    L.gpulz_max_compressed_size.argtypes = [u64, u32]
+    L.gpulz_max_compressed_size.restype = u64
+    L.gpulz_encode_workspace_size.argtypes = [u64, u32]
+    L.gpulz_encode_workspace_size.restype = u64
+    L.gpulz_decode_workspace_size.argtypes = [u64]
+    L.gpulz_decode_workspace_size.restype = u64
+    L.gpulz_encode.argtypes = [vp, u64, u32, u32, u32, vp, u64, vp, vp, u64, vp]
+    L.gpulz_encode.restype = ctypes.c_int
+    L.gpulz_decode.argtypes = [vp, u64, vp, u64, vp, vp, vp, u64, vp]
+    L.gpulz_decode.restype = ctypes.c_int
+    L.gpulz_stream_info.argtypes = [vp, u64, ctypes.POINTER(u64), ctypes.POINTER(u64), ctypes.POINTER(u32),
+                                    ctypes.POINTER(u32)]
+    L.gpulz_stream_info.restype = ctypes.c_int
+    L.gpulz_encode_timed.argtypes = L.gpulz_encode.argtypes + [vp, vp]
+    L.gpulz_encode_timed.restype = ctypes.c_int
+    L.gpulz_decode_timed.argtypes = L.gpulz_decode.argtypes + [vp, vp]
+    L.gpulz_decode_timed.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != OK:
+        raise GpulzError(f"{what} returned {rc}")
+
+
+def max_compressed_size(n_bytes: int, chunk_size: int) -> int:
+    return int(lib().gpulz_max_compressed_size(n_bytes, chunk_size))
+
+
+def encode_workspace_size(n_bytes: int, chunk_size: int) -> int:
+    return int(lib().gpulz_encode_workspace_size(n_bytes, chunk_size))
+
+
+def decode_workspace_size(in_bytes: int) -> int:
+    return int(lib().gpulz_decode_workspace_size(in_bytes))
+
+
+def _ptr(t) -> int | None:
+    return t.data_ptr() if t is not None and t.numel() > 0 else None
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _u8_view(t):
+    import torch
+    if not t.is_cuda:
+        raise GpulzError("input must be a CUDA (HIP) tensor")
+    t = t.contiguous()
+    return t.view(torch.uint8).reshape(-1) if t.dtype != torch.uint8 else t.reshape(-1)
+
+
+def encode_into(d_in, chunk_size: int, word_size: int, match_level: int, out, out_bytes, workspace,
+                stream=None, events=None) -> None:
+    """Enqueue gpulz_encode with caller-provided buffers (no allocation).
+    events: optional (start, stop) raw hipEvent_t handles, recorded around the
+    chunk encode kernel (gpulz_encode_timed)."""
+    src = _u8_view(d_in)
+    args = (_ptr(src), src.numel(), chunk_size, word_size, match_level, _ptr(out), out.numel(),
+            _ptr(out_bytes), _ptr(workspace), workspace.numel(), _stream(stream))
+    if events is None:
+        _check(lib().gpulz_encode(*args), "gpulz_encode")
+    else:
+        _check(lib().gpulz_encode_timed(*args, events[0], events[1]), "gpulz_encode_timed")
+
+
+def encode(d_in, chunk_size: int = 2048, word_size: int = 4, match_level: int = 0, stream=None):
+    """Encode a CUDA tensor (any dtype, its bytes are coded).
+
+    Returns (stream_buffer uint8 tensor of the worst-case size, out_bytes
+    uint64 tensor on the device).  The stream is the first out_bytes bytes."""
+    import torch
+    src = _u8_view(d_in)
+    cap = max_compressed_size(src.numel(), chunk_size)
+    if cap == 0:
+        raise GpulzError(f"unsupported chunk_size {chunk_size}")
+    dev = src.device
+    out = torch.empty(cap, dtype=torch.uint8, device=dev)
+    out_bytes = torch.zeros(1, dtype=torch.uint64, device=dev)
+    ws = torch.empty(max(encode_workspace_size(src.numel(), chunk_size), 1), dtype=torch.uint8, device=dev)
+    encode_into(src, chunk_size, word_size, match_level, out, out_bytes, ws, stream)
+    return out, out_bytes
+
+
+def decode_into(d_stream, in_bytes: int, out, out_bytes, status, workspace, stream=None, events=None) -> None:
+    """Enqueue gpulz_decode with caller-provided buffers (no allocation).
+    events: optional (start, stop) raw hipEvent_t handles, recorded around the
+    chunk decode kernel (gpulz_decode_timed)."""
+    s = _u8_view(d_stream)
+    if in_bytes > s.numel():
+        raise GpulzError("in_bytes exceeds the stream buffer")
+    args = (_ptr(s), in_bytes, _ptr(out), out.numel(), _ptr(out_bytes), _ptr(status), _ptr(workspace),
+            workspace.numel(), _stream(stream))
+    if events is None:
+        _check(lib().gpulz_decode(*args), "gpulz_decode")
+    else:
+        _check(lib().gpulz_decode_timed(*args, events[0], events[1]), "gpulz_decode_timed")
+
+
+def decode(d_stream, in_bytes: int | None = None, out_capacity: int | None = None, stream=None):
+    """Decode a stream held in a CUDA uint8 tensor.
+
+    out_capacity: bytes to allocate for the output; if None the 32-byte
+    header is copied to the host once to size it.  Returns (out uint8 tensor,
+    out_bytes uint64 device tensor, status uint32 device tensor)."""
+    import torch
+    s = _u8_view(d_stream)
+    in_bytes = s.numel() if in_bytes is None else in_bytes
+    if out_capacity is None:
+        info = stream_info(s[:32].cpu().numpy().tobytes())
+        if info is None:
+            raise GpulzError("not a gpulz stream")
+        out_capacity = info[0]
+    dev = s.device
+    out = torch.empty(max(out_capacity, 1), dtype=torch.uint8, device=dev)[:out_capacity]
+    out_bytes = torch.zeros(1, dtype=torch.uint64, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(decode_workspace_size(in_bytes), 1), dtype=torch.uint8, device=dev)
+    decode_into(s, in_bytes, out, out_bytes, status, ws, stream)
+    return out, out_bytes, status
+
+
+def stream_info(prefix: bytes):
+    """(original_size, stream_bytes, chunk_size, word_size) from a host copy of
+    the first 32+ bytes, or None if they are not a valid header."""
+    buf = ctypes.create_string_buffer(bytes(prefix), len(prefix))
+    n, t = ctypes.c_uint64(), ctypes.c_uint64()
+    cs, ws = ctypes.c_uint32(), ctypes.c_uint32()
+    rc = lib().gpulz_stream_info(ctypes.cast(buf, ctypes.c_void_p), len(prefix), ctypes.byref(n), ctypes.byref(t),
+                                 ctypes.byref(cs), ctypes.byref(ws))
+    if rc != OK:
+        return None
+    return n.value, t.value, cs.value, ws.value

@@ -1,0 +1,173 @@
+// abi.hip -- the extern "C" entry points declared in include/gpulz.h.
+// Host-side argument checks happen before anything is enqueued; the rest is
+// workspace carving and kernel launches on the caller's stream.
+#include "gpulz.h"
+#include "gpulz_timing.h"
+
+#include "common.h"
+
+using namespace gpulz;
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+inline uint64_t round_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+inline uint64_t num_chunks_of(uint64_t n, uint32_t cs) { return n / cs + ((n % cs) != 0); }
+constexpr uint64_t kStagingSlack = 256;  // realigning copies read a few bytes past a slot
+
+struct EncLayoutHost {
+  uint64_t staging, entries, offsets, tiles, total;
+};
+
+EncLayoutHost enc_layout(uint64_t chunks, uint32_t cs) {
+  const uint64_t tiles = (chunks + kTile - 1) / kTile;
+  EncLayoutHost L;
+  L.staging = 0;
+  L.entries = L.staging + round_up(chunks * cs + kStagingSlack);
+  L.offsets = L.entries + round_up(chunks * 8u);
+  L.tiles = L.offsets + round_up(chunks * 8u);
+  L.total = L.tiles + round_up((tiles ? tiles : 1) * 8u);
+  return L;
+}
+
+struct DecLayoutHost {
+  uint64_t params, offsets, tiles, total;
+};
+
+DecLayoutHost dec_layout(uint64_t chunks_cap) {
+  const uint64_t tiles = (chunks_cap + kTile - 1) / kTile;
+  DecLayoutHost L;
+  L.params = 0;
+  L.offsets = round_up(sizeof(DecodeParams));
+  L.tiles = L.offsets + round_up(chunks_cap * 8u);
+  L.total = L.tiles + round_up((tiles ? tiles : 1) * 8u);
+  return L;
+}
+
+uint64_t dec_chunks_bound(uint64_t in_bytes) { return in_bytes >= kHeaderBytes ? (in_bytes - kHeaderBytes) / 8u : 0u; }
+
+}  // namespace
+
+extern "C" {
+
+uint64_t gpulz_max_compressed_size(uint64_t n_bytes, uint32_t chunk_size) {
+  if (!chunk_size_ok(chunk_size)) return 0;
+  return (uint64_t)kHeaderBytes + (uint64_t)kEntryBytes * num_chunks_of(n_bytes, chunk_size) + n_bytes;
+}
+
+uint64_t gpulz_encode_workspace_size(uint64_t n_bytes, uint32_t chunk_size) {
+  if (!chunk_size_ok(chunk_size)) return 0;
+  return enc_layout(num_chunks_of(n_bytes, chunk_size), chunk_size).total;
+}
+
+uint64_t gpulz_decode_workspace_size(uint64_t in_bytes) { return dec_layout(dec_chunks_bound(in_bytes)).total; }
+
+int gpulz_encode_timed(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, uint32_t word_size,
+                       uint32_t match_level, void* d_out, uint64_t out_capacity, uint64_t* d_out_bytes,
+                       void* d_workspace, uint64_t workspace_bytes, hipStream_t stream, hipEvent_t ev_start,
+                       hipEvent_t ev_stop) {
+  if (!chunk_size_ok(chunk_size) || !word_size_ok(word_size) || match_level > 1u) return GPULZ_ERR_INVALID_ARG;
+  if ((n_bytes > 0 && d_in == nullptr) || d_out == nullptr || d_out_bytes == nullptr || d_workspace == nullptr)
+    return GPULZ_ERR_INVALID_ARG;
+  const uint64_t chunks = num_chunks_of(n_bytes, chunk_size);
+  if (chunks > 0xFFFFFFFFull) return GPULZ_ERR_INVALID_ARG;
+  if (out_capacity < gpulz_max_compressed_size(n_bytes, chunk_size)) return GPULZ_ERR_CAPACITY;
+  const EncLayoutHost L = enc_layout(chunks, chunk_size);
+  if (workspace_bytes < L.total) return GPULZ_ERR_CAPACITY;
+  uint8_t* ws = (uint8_t*)d_workspace;
+
+  EncodeArgs ea;
+  ea.in = (const uint8_t*)d_in;
+  ea.n = n_bytes;
+  ea.cs = chunk_size;
+  ea.ws = word_size;
+  ea.level = match_level;
+  ea.num_chunks = (uint32_t)chunks;
+  ea.staging = ws + L.staging;
+  ea.entries = (uint2*)(ws + L.entries);
+  if (ev_start && hipEventRecord(ev_start, stream) != hipSuccess) return GPULZ_ERR_HIP;
+  if (launch_encode_chunks(ea, stream) != hipSuccess) return GPULZ_ERR_HIP;
+  if (ev_stop && hipEventRecord(ev_stop, stream) != hipSuccess) return GPULZ_ERR_HIP;
+
+  CompactArgs ca;
+  ca.staging = ea.staging;
+  ca.entries = ea.entries;
+  ca.offsets = (uint64_t*)(ws + L.offsets);
+  ca.tile_sums = (uint64_t*)(ws + L.tiles);
+  ca.out = (uint8_t*)d_out;
+  ca.out_bytes = d_out_bytes;
+  ca.n = n_bytes;
+  ca.cs = chunk_size;
+  ca.ws = word_size;
+  ca.num_chunks = (uint32_t)chunks;
+  ca.num_tiles = (uint32_t)((chunks + kTile - 1) / kTile);
+  if (launch_compact(ca, stream) != hipSuccess) return GPULZ_ERR_HIP;
+  return GPULZ_OK;
+}
+
+int gpulz_encode(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, uint32_t word_size, uint32_t match_level,
+                 void* d_out, uint64_t out_capacity, uint64_t* d_out_bytes, void* d_workspace,
+                 uint64_t workspace_bytes, hipStream_t stream) {
+  return gpulz_encode_timed(d_in, n_bytes, chunk_size, word_size, match_level, d_out, out_capacity, d_out_bytes,
+                            d_workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+int gpulz_decode_timed(const void* d_in, uint64_t in_bytes, void* d_out, uint64_t out_capacity,
+                       uint64_t* d_out_bytes, uint32_t* d_status, void* d_workspace, uint64_t workspace_bytes,
+                       hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (d_in == nullptr || d_out_bytes == nullptr || d_status == nullptr || d_workspace == nullptr)
+    return GPULZ_ERR_INVALID_ARG;
+  if (out_capacity > 0 && d_out == nullptr) return GPULZ_ERR_INVALID_ARG;
+  if (in_bytes < kHeaderBytes) return GPULZ_ERR_CORRUPT;
+  uint64_t cap = dec_chunks_bound(in_bytes);
+  const uint64_t by_out = num_chunks_of(out_capacity, 1024u);
+  if (by_out < cap) cap = by_out;
+  if (cap > 0xFFFFFFFFull) cap = 0xFFFFFFFFull;
+  const DecLayoutHost L = dec_layout(dec_chunks_bound(in_bytes));
+  if (workspace_bytes < L.total) return GPULZ_ERR_CAPACITY;
+  uint8_t* ws = (uint8_t*)d_workspace;
+  DecodeArgs da;
+  da.in = (const uint8_t*)d_in;
+  da.in_bytes = in_bytes;
+  da.out = (uint8_t*)d_out;
+  da.out_capacity = out_capacity;
+  da.out_bytes = d_out_bytes;
+  da.status = d_status;
+  da.params = (DecodeParams*)(ws + L.params);
+  da.offsets = (uint64_t*)(ws + L.offsets);
+  da.tile_sums = (uint64_t*)(ws + L.tiles);
+  da.chunks_cap = (uint32_t)cap;
+  da.tiles_cap = (uint32_t)((cap + kTile - 1) / kTile);
+  da.ev_start = ev_start;
+  da.ev_stop = ev_stop;
+  if (launch_decode(da, stream) != hipSuccess) return GPULZ_ERR_HIP;
+  return GPULZ_OK;
+}
+
+int gpulz_decode(const void* d_in, uint64_t in_bytes, void* d_out, uint64_t out_capacity, uint64_t* d_out_bytes,
+                 uint32_t* d_status, void* d_workspace, uint64_t workspace_bytes, hipStream_t stream) {
+  return gpulz_decode_timed(d_in, in_bytes, d_out, out_capacity, d_out_bytes, d_status, d_workspace,
+                            workspace_bytes, stream, nullptr, nullptr);
+}
+
+int gpulz_stream_info(const void* h_prefix, uint64_t bytes, uint64_t* original_size, uint64_t* stream_bytes,
+                      uint32_t* chunk_size, uint32_t* word_size) {
+  if (h_prefix == nullptr || bytes < kHeaderBytes) return GPULZ_ERR_CORRUPT;
+  const uint8_t* s = (const uint8_t*)h_prefix;
+  auto u32 = [&](int o) {
+    return (uint32_t)s[o] | ((uint32_t)s[o + 1] << 8) | ((uint32_t)s[o + 2] << 16) | ((uint32_t)s[o + 3] << 24);
+  };
+  auto u64 = [&](int o) { return (uint64_t)u32(o) | ((uint64_t)u32(o + 4) << 32); };
+  const uint32_t ws = s[5], cs = u32(8), nc = u32(12);
+  const uint64_t n = u64(16), pb = u64(24);
+  if (u32(0) != kMagic || s[4] != kVersion || s[6] != 0 || s[7] != 0) return GPULZ_ERR_CORRUPT;
+  if (!word_size_ok(ws) || !chunk_size_ok(cs)) return GPULZ_ERR_CORRUPT;
+  if (num_chunks_of(n, cs) != nc || pb > n) return GPULZ_ERR_CORRUPT;
+  if (original_size) *original_size = n;
+  if (stream_bytes) *stream_bytes = (uint64_t)kHeaderBytes + (uint64_t)kEntryBytes * nc + pb;
+  if (chunk_size) *chunk_size = cs;
+  if (word_size) *word_size = ws;
+  return GPULZ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,152 @@
+// common.h -- internal constants, device helpers and launcher declarations of
+// the gfx950 chunked LZSS coder.  Stream format: see include/gpulz.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gpulz {
+
+// ---- stream format ------------------------------------------------------
+constexpr uint32_t kMagic = 0x315A4C47u;  // "GLZ1"
+constexpr uint32_t kVersion = 1u;
+constexpr uint32_t kHeaderBytes = 32u;
+constexpr uint32_t kEntryBytes = 8u;
+constexpr uint32_t kRawBit = 0x80000000u;
+
+// ---- method constants (GPULZStage page) ---------------------------------
+constexpr uint32_t kWindow = 32u;     // near window: offsets 1..32 (window paragraph)
+constexpr uint32_t kMaxLen = 255u;    // one-byte length field (long-match paragraph)
+constexpr uint32_t kMaxFar = 255u;    // one-byte offset field: level-1 reach (level table)
+constexpr uint32_t kSubBlocks = 8u;   // level-1 sub-block walk (hashed-table paragraph)
+constexpr uint32_t kHashBits = 11u;   // table size: not on the pages; 2048 buckets
+constexpr uint32_t kHashSize = 1u << kHashBits;
+
+// ---- launch geometry ----------------------------------------------------
+constexpr int kBlock = 256;           // threads per workgroup (4 wave64)
+constexpr int kWaves = kBlock / 64;
+constexpr uint32_t kTile = 1024;      // chunks per size-scan tile
+constexpr uint32_t kMaxGrid = 1u << 20;
+
+// Status codes mirrored from the public header.
+constexpr uint32_t kStatusOk = 0u;
+constexpr uint32_t kStatusCapacity = 2u;
+constexpr uint32_t kStatusCorrupt = 3u;
+
+__host__ __device__ inline bool chunk_size_ok(uint32_t cs) {
+  return cs == 1024u || cs == 2048u || cs == 4096u;
+}
+__host__ __device__ inline bool word_size_ok(uint32_t ws) {
+  return ws == 1u || ws == 2u || ws == 4u;
+}
+
+// Payload bytes a size-table entry stands for.
+__host__ __device__ inline uint32_t entry_payload(uint32_t f, uint32_t d) {
+  return f != 0u ? f + d : ((d & kRawBit) ? (d & ~kRawBit) : 0u);
+}
+
+// Level-1 bucket of the two-word key (w0, w1): Fibonacci multiplicative hash
+// of the 64-bit key w0 | w1<<32, top kHashBits bits.  The pages give no hash
+// function; this choice only affects which candidates the encoder sees.
+__device__ __forceinline__ uint32_t bucket_of(uint32_t w0, uint32_t w1) {
+  uint64_t key = (uint64_t)w0 | ((uint64_t)w1 << 32);
+  return (uint32_t)((key * 0x9E3779B97F4A7C15ull) >> (64u - kHashBits));
+}
+
+// ---- block-wide helpers (blockDim.x == kBlock) ---------------------------
+// Exclusive scan of one value per thread.  `sh` needs kWaves elements of T.
+template <typename T>
+__device__ __forceinline__ T block_exclusive_scan(T v, T* total, T* sh) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  T inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    T nb = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += nb;
+  }
+  if (lane == 63) sh[wid] = inc;
+  __syncthreads();
+  T pre = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    T t = sh[w];
+    pre += (w < wid) ? t : T(0);
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return pre + inc - v;
+}
+
+template <typename T>
+__device__ __forceinline__ T block_sum(T v, T* sh) {
+  T tot;
+  block_exclusive_scan(v, &tot, sh);
+  return tot;
+}
+
+// 4 bytes starting at p (any alignment) from a buffer whose readable bytes
+// end at lim; p-3 must still be readable.  Bytes at or past lim read as 0.
+__device__ __forceinline__ uint32_t load4_unaligned(const uint8_t* p, const uint8_t* lim) {
+  const uintptr_t a = (uintptr_t)p, a0 = a & ~(uintptr_t)3;
+  const uint32_t sh = (uint32_t)(a & 3u);
+  if (a0 + 8u <= (uintptr_t)lim) {
+    const uint32_t* w = (const uint32_t*)a0;
+    uint32_t lo = w[0];
+    uint32_t hi = sh ? w[1] : 0u;
+    return __builtin_amdgcn_alignbyte(hi, lo, sh);
+  }
+  uint32_t v = 0;
+  for (uint32_t b = 0; b < 4u; ++b)
+    if (p + b < lim) v |= (uint32_t)p[b] << (8u * b);
+  return v;
+}
+
+// ---- launchers (host side, one per kernel family) -------------------------
+struct EncodeArgs {
+  const uint8_t* in;
+  uint64_t n;
+  uint32_t cs, ws, level;
+  uint32_t num_chunks;
+  uint8_t* staging;     // num_chunks * cs (+ slack), fixed stride cs
+  uint2* entries;       // num_chunks size-table entries
+};
+hipError_t launch_encode_chunks(const EncodeArgs& a, hipStream_t stream);
+
+struct CompactArgs {
+  const uint8_t* staging;
+  const uint2* entries;
+  uint64_t* offsets;    // num_chunks payload offsets (workspace)
+  uint64_t* tile_sums;  // num_tiles
+  uint8_t* out;
+  uint64_t* out_bytes;
+  uint64_t n;
+  uint32_t cs, ws, num_chunks, num_tiles;
+};
+hipError_t launch_compact(const CompactArgs& a, hipStream_t stream);
+
+struct DecodeParams {  // device-resident, written by the header kernel
+  uint64_t n;
+  uint64_t payload_bytes;
+  uint64_t payload_base;  // byte offset of the first payload in the stream
+  uint32_t cs, ws, num_chunks, status;
+};
+
+struct DecodeArgs {
+  const uint8_t* in;
+  uint64_t in_bytes;
+  uint8_t* out;
+  uint64_t out_capacity;
+  uint64_t* out_bytes;
+  uint32_t* status;
+  DecodeParams* params;
+  uint64_t* offsets;    // chunks_cap
+  uint64_t* tile_sums;  // tiles_cap
+  uint32_t chunks_cap;  // host bound on num_chunks
+  uint32_t tiles_cap;
+  hipEvent_t ev_start;  // optional, recorded around the chunk decode kernel
+  hipEvent_t ev_stop;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace gpulz

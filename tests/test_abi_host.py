@@ -1,0 +1,119 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point the header declares, sizes its buffers as documented and
+rejects bad arguments before touching the device."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
+
+
+@pytest.fixture(scope="module")
+def g():
+    import chunked_lzss_coder_amd as g
+    if not os.path.exists(g.LIB_PATH):
+        from chunked_lzss_coder_amd import build
+        build.build()
+    return g
+
+
+def declared_symbols():
+    txt = "".join(open(h).read() for h in HEADERS)
+    return sorted(set(re.findall(r"GPULZ_API\s+\w+\s+(gpulz_\w+)\s*\(", txt)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_symbols() == sorted(["gpulz_decode", "gpulz_decode_workspace_size", "gpulz_encode",
+                                         "gpulz_encode_workspace_size", "gpulz_max_compressed_size",
+                                         "gpulz_stream_info", "gpulz_encode_timed", "gpulz_decode_timed"])
+
+
+def test_library_exports_every_declared_symbol(g):
+    lib = g.lib()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert sorted(g.SYMBOLS) == declared_symbols()
+    # nothing else with C linkage leaks out
+    out = os.popen(f"nm -D --defined-only {g.LIB_PATH}").read()
+    exported = sorted(set(re.findall(r"\bT (gpulz_\w+)", out)))
+    assert exported == declared_symbols()
+
+
+@pytest.mark.parametrize("cs", [1024, 2048, 4096])
+def test_max_compressed_size(g, cs):
+    for n in [0, 1, cs - 1, cs, cs + 1, 26_214_400, 2 << 30]:
+        chunks = -(-n // cs)
+        assert g.max_compressed_size(n, cs) == 32 + 8 * chunks + n
+    assert g.max_compressed_size(100, 3000) == 0
+    assert g.max_compressed_size(100, 512) == 0
+
+
+def test_workspace_sizes(g):
+    assert g.encode_workspace_size(1 << 20, 2048) >= (1 << 20) + 512 * 16
+    assert g.encode_workspace_size(1 << 20, 777) == 0
+    assert g.decode_workspace_size(32 + 8 * 1000) >= 1000 * 8
+    assert g.decode_workspace_size(0) > 0
+
+
+def test_stream_info_matches_oracle_streams(g, oracle_mod):
+    rng = np.random.default_rng(0)
+    for cs, ws, n in [(2048, 4, 5000), (1024, 1, 0), (4096, 2, 9000)]:
+        a = rng.integers(0, 4, size=n, dtype=np.uint8)
+        s = oracle_mod.encode(a, cs, ws, 0)
+        assert g.stream_info(s[:32].tobytes()) == (n, s.size, cs, ws)
+        assert g.stream_info(s[:31].tobytes()) is None
+        bad = s[:32].copy()
+        bad[0] ^= 1
+        assert g.stream_info(bad.tobytes()) is None
+
+
+def _call_encode(g, ptr_in, n, cs, ws, level, ptr_out, cap, ptr_nb, ptr_ws, wsb):
+    return g.lib().gpulz_encode(ptr_in, n, cs, ws, level, ptr_out, cap, ptr_nb, ptr_ws, wsb, None)
+
+
+def test_encode_rejects_bad_arguments_before_launch(g):
+    # fake non-null pointers: every call below must return before using them
+    p = ctypes.c_void_p(0x1000)
+    big = 1 << 40
+    assert _call_encode(g, p, 100, 3000, 4, 0, p, big, p, p, big) == g.ERR_INVALID_ARG
+    assert _call_encode(g, p, 100, 2048, 3, 0, p, big, p, p, big) == g.ERR_INVALID_ARG
+    assert _call_encode(g, p, 100, 2048, 4, 2, p, big, p, p, big) == g.ERR_INVALID_ARG
+    assert _call_encode(g, None, 100, 2048, 4, 0, p, big, p, p, big) == g.ERR_INVALID_ARG
+    assert _call_encode(g, p, 100, 2048, 4, 0, None, big, p, p, big) == g.ERR_INVALID_ARG
+    assert _call_encode(g, p, 100, 2048, 4, 0, p, big, None, p, big) == g.ERR_INVALID_ARG
+    assert _call_encode(g, p, 100, 2048, 4, 0, p, big, p, None, big) == g.ERR_INVALID_ARG
+    need = g.max_compressed_size(100, 2048)
+    assert _call_encode(g, p, 100, 2048, 4, 0, p, need - 1, p, p, big) == g.ERR_CAPACITY
+    wsn = g.encode_workspace_size(100, 2048)
+    assert _call_encode(g, p, 100, 2048, 4, 0, p, need, p, p, wsn - 1) == g.ERR_CAPACITY
+
+
+def test_decode_rejects_bad_arguments_before_launch(g):
+    p = ctypes.c_void_p(0x1000)
+    big = 1 << 40
+    dec = g.lib().gpulz_decode
+    assert dec(None, 100, p, big, p, p, p, big, None) == g.ERR_INVALID_ARG
+    assert dec(p, 100, p, big, None, p, p, big, None) == g.ERR_INVALID_ARG
+    assert dec(p, 100, p, big, p, None, p, big, None) == g.ERR_INVALID_ARG
+    assert dec(p, 100, p, big, p, p, None, big, None) == g.ERR_INVALID_ARG
+    assert dec(p, 100, None, 10, p, p, p, big, None) == g.ERR_INVALID_ARG
+    assert dec(p, 31, p, big, p, p, p, big, None) == g.ERR_CORRUPT
+    need = g.decode_workspace_size(1000)
+    assert dec(p, 1000, p, big, p, p, p, need - 1, None) == g.ERR_CAPACITY
+
+
+def test_product_package_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "chunked_lzss_coder_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in txt and "from oracle" not in txt, f
+                assert "gpulz_oracle" not in txt and "liboracle" not in txt, f
