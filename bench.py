@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 chunked LZSS coder on one MI355X.
+
+A step is one pass of the whole hot path over the workload: for every match
+level, gpulz_encode (chunk encode + size scan + stream assembly) followed by
+gpulz_decode of the stream it produced, inputs resident in HBM.
+
+Prints ONE JSON line.  ``value`` is the level-0 encode throughput in decimal
+GB/s of uncompressed input (whole gpulz_encode call); decode GB/s and the
+compression ratio of every level sit beside it.  ``roofline`` reports the
+dominant kernel (the chunk encode kernel) against the HBM peak, with its
+duration taken from HIP events recorded around that kernel alone, and
+``cpu_baseline`` the CPU oracle (single thread) on the same bytes.
+
+Default workload: 2D Lorenzo residual codes of a 1800x3600 field
+(25,920,000 bytes of uint32 words), chunk_size 2048, word_size 4, levels 0
+and 1.  ``--workload 4 --levels 0`` runs the 2 GiB stress stream at level 0.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+_ROOT = os.path.dirname(os.path.abspath(__file__))
+if _ROOT not in sys.path:
+    sys.path.insert(0, _ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (torch.cuda.Event only sees torch's stream;
+    these are handed to the library, which records them on its stream)."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (binds the HIP runtime torch uses)
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def pair(self):
+        evs = []
+        for _ in range(2):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.events.append(e)
+            evs.append(e)
+        return tuple(evs)
+
+    def ms(self, pair) -> float:
+        f = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(f), pair[0], pair[1]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(f.value)
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
+
+
+def cpu_baseline(w, level, gpu_stream_bytes: bytes):
+    """Oracle leg: time the single-threaded CPU oracle on the same bytes and
+    check the GPU stream against its stream."""
+    import numpy as np
+
+    import oracle
+    oracle.build()
+    n = w.n
+    # bounded sample: the whole workload if it is small, else a prefix of
+    # whole chunks worth about 64 MiB (the oracle is chunk-independent)
+    limit = 64 << 20
+    take = n if n <= limit else (limit // w.chunk_size) * w.chunk_size
+    sample = w.data[:take]
+    t0 = time.perf_counter()
+    ref = oracle.encode(sample, w.chunk_size, w.word_size, level)
+    t_enc = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    back = oracle.decode(ref)
+    t_dec = time.perf_counter() - t0
+    ok_rt = bool(np.array_equal(back, sample))
+    identical = None
+    if take == n:
+        identical = bool(ref.tobytes() == gpu_stream_bytes)
+    return {
+        "value": round(take / t_enc / 1e9, 6),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"level-{level} encode of {'the whole workload' if take == n else 'the first %d bytes' % take}"
+                   f" ({take} bytes), single-threaded C oracle"),
+        "decode_gbps": round(take / t_dec / 1e9, 6),
+        "encode_s": round(t_enc, 3),
+        "decode_s": round(t_dec, 3),
+        "round_trip": ok_rt,
+    }, identical
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=1, help="workload index 0..4 (default 1)")
+    ap.add_argument("--levels", type=str, default=None, help="comma-separated match levels (default: workload's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this coder runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(chunks shard across GPUs with one scan of per-shard sizes, not built here)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import chunked_lzss_coder_amd as g
+    from chunked_lzss_coder_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    g.lib()
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    w = synth.workload(args.workload)
+    log(f"workload {w.name}: {w.n} bytes, cs {w.chunk_size}, ws {w.word_size}, sha256 {w.sha256()[:16]}, "
+        f"generated in {time.perf_counter() - t0:.1f}s")
+    levels = tuple(int(x) for x in args.levels.split(",")) if args.levels else tuple(sorted(w.levels))
+    cs, ws = w.chunk_size, w.word_size
+    n = w.n
+    x = torch.from_numpy(w.data.copy()).to(dev)
+    cap = g.max_compressed_size(n, cs)
+    ev = HipEvents()
+
+    bufs = {}
+    for lv in levels:
+        out = torch.empty(cap, dtype=torch.uint8, device=dev)
+        nb = torch.zeros(1, dtype=torch.uint64, device=dev)
+        ews = torch.empty(g.encode_workspace_size(n, cs), dtype=torch.uint8, device=dev)
+        dout = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+        dnb = torch.zeros(1, dtype=torch.uint64, device=dev)
+        st = torch.zeros(1, dtype=torch.int32, device=dev)
+        dws = torch.empty(g.decode_workspace_size(cap), dtype=torch.uint8, device=dev)
+        bufs[lv] = (out, nb, ews, dout, dnb, st, dws)
+
+    # first pass: sizes, round trip (outside any timed region)
+    stream_bytes = {}
+    for lv in levels:
+        out, nb, ews, dout, dnb, st, dws = bufs[lv]
+        g.encode_into(x, cs, ws, lv, out, nb, ews)
+        torch.cuda.synchronize()
+        stream_bytes[lv] = int(nb.item())
+        g.decode_into(out, stream_bytes[lv], dout, dnb, st, dws)
+        torch.cuda.synchronize()
+        if int(st.item()) != 0 or int(dnb.item()) != n or not torch.equal(dout[:n], x):
+            print(f"bench.py: level {lv} round trip failed (status {int(st.item())})", file=sys.stderr)
+            return 1
+
+    def step(record):
+        for lv in levels:
+            out, nb, ews, dout, dnb, st, dws = bufs[lv]
+            ce = ev.pair() if record is not None else None
+            ke = ev.pair() if record is not None else None
+            cd = ev.pair() if record is not None else None
+            kd = ev.pair() if record is not None else None
+            s = torch.cuda.current_stream()
+            if ce:
+                ev.hip.hipEventRecord(ce[0], ctypes.c_void_p(s.cuda_stream))
+            g.encode_into(x, cs, ws, lv, out, nb, ews, events=ke)
+            if ce:
+                ev.hip.hipEventRecord(ce[1], ctypes.c_void_p(s.cuda_stream))
+                ev.hip.hipEventRecord(cd[0], ctypes.c_void_p(s.cuda_stream))
+            g.decode_into(out, stream_bytes[lv], dout, dnb, st, dws, events=kd)
+            if cd:
+                ev.hip.hipEventRecord(cd[1], ctypes.c_void_p(s.cuda_stream))
+            if record is not None:
+                record.append((lv, ce, ke, cd, kd))
+
+    ev.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done; timing {args.steps} steps")
+    rec = []
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(rec)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    res = {}
+    for lv in levels:
+        rows = [r for r in rec if r[0] == lv]
+        enc_ms = [ev.ms(r[1]) for r in rows]
+        kenc_ms = [ev.ms(r[2]) for r in rows]
+        dec_ms = [ev.ms(r[3]) for r in rows]
+        kdec_ms = [ev.ms(r[4]) for r in rows]
+        me, mke, md, mkd = (float(np.mean(v)) for v in (enc_ms, kenc_ms, dec_ms, kdec_ms))
+        sb = stream_bytes[lv]
+        chunks = -(-n // cs)
+        algo = n + 8 * chunks + (sb - 32 - 8 * chunks)  # read input, write table rows + payloads
+        res[lv] = {
+            "encode_gbps": round(n / (me * 1e-3) / 1e9, 3),
+            "decode_gbps": round(n / (md * 1e-3) / 1e9, 3),
+            "ratio": round(n / sb, 4),
+            "stream_bytes": sb,
+            "encode_ms": round(me, 4),
+            "decode_ms": round(md, 4),
+            "encode_ms_median": round(float(np.median(enc_ms)), 4),
+            "decode_ms_median": round(float(np.median(dec_ms)), 4),
+            "encode_kernel_ms": round(mke, 4),
+            "decode_kernel_ms": round(mkd, 4),
+            "encode_kernel_hbm_gbps": round(algo / (mke * 1e-3) / 1e9, 2),
+            "decode_kernel_hbm_gbps": round(algo / (mkd * 1e-3) / 1e9, 2),
+            "algorithmic_bytes": algo,
+            "round_trip": True,
+        }
+    ev.close()
+
+    lv0 = levels[0]
+    r0 = res[lv0]
+    roof = {
+        "bound": "hbm",
+        "kernel": "encode_chunks_kernel (level %d)" % lv0,
+        "achieved": r0["encode_kernel_hbm_gbps"],
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(r0["encode_kernel_hbm_gbps"] / HBM_PEAK_GBPS, 5),
+        "traffic": None,
+        "kernel_ms": r0["encode_kernel_ms"],
+        "algorithmic_bytes_per_launch": r0["algorithmic_bytes"],
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        out = bufs[lv0][0]
+        gpu_stream = out[:stream_bytes[lv0]].cpu().numpy().tobytes()
+        cpu, identical = cpu_baseline(w, lv0, gpu_stream)
+        r0["byte_identical"] = identical
+        log(f"cpu oracle: {cpu['value']} GB/s encode ({cpu['encode_s']} s), byte_identical={identical}")
+
+    ms_per_step = wall * 1e3 / max(args.steps, 1)
+    line = {
+        "metric": "encode/decode GB/s (uncompressed) + compression ratio, word4 chunk2048, 1 GPU",
+        "value": r0["encode_gbps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32" if ws == 4 else ("u16" if ws == 2 else "u8"),
+        "data": "synthetic",
+        "config": {"workload": w.name, "bytes": n, "chunk_size": cs, "word_size": ws, "levels": list(levels),
+                   "sha256": w.sha256()},
+        "encode_gbps": r0["encode_gbps"],
+        "decode_gbps": r0["decode_gbps"],
+        "ratio": r0["ratio"],
+        "levels": {str(k): v for k, v in res.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -13,20 +13,16 @@ namespace {
 constexpr uint64_t kAlign = 256;
 inline uint64_t round_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline uint64_t num_chunks_of(uint64_t n, uint32_t cs) { return n / cs + ((n % cs) != 0); }
-constexpr uint64_t kStagingSlack = 256;  // realigning copies read a few bytes past a slot
 
 struct EncLayoutHost {
-  uint64_t staging, entries, offsets, tiles, total;
+  uint64_t ctl, flags, total;
 };
 
-EncLayoutHost enc_layout(uint64_t chunks, uint32_t cs) {
-  const uint64_t tiles = (chunks + kTile - 1) / kTile;
+EncLayoutHost enc_layout(uint64_t chunks) {
   EncLayoutHost L;
-  L.staging = 0;
-  L.entries = L.staging + round_up(chunks * cs + kStagingSlack);
-  L.offsets = L.entries + round_up(chunks * 8u);
-  L.tiles = L.offsets + round_up(chunks * 8u);
-  L.total = L.tiles + round_up((tiles ? tiles : 1) * 8u);
+  L.ctl = 0;
+  L.flags = round_up(encode_ctl_bytes());
+  L.total = L.flags + round_up((chunks ? chunks : 1) * 8u);
   return L;
 }
 
@@ -57,7 +53,7 @@ uint64_t gpulz_max_compressed_size(uint64_t n_bytes, uint32_t chunk_size) {
 
 uint64_t gpulz_encode_workspace_size(uint64_t n_bytes, uint32_t chunk_size) {
   if (!chunk_size_ok(chunk_size)) return 0;
-  return enc_layout(num_chunks_of(n_bytes, chunk_size), chunk_size).total;
+  return enc_layout(num_chunks_of(n_bytes, chunk_size)).total;
 }
 
 uint64_t gpulz_decode_workspace_size(uint64_t in_bytes) { return dec_layout(dec_chunks_bound(in_bytes)).total; }
@@ -72,7 +68,7 @@ int gpulz_encode_timed(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, 
   const uint64_t chunks = num_chunks_of(n_bytes, chunk_size);
   if (chunks > 0xFFFFFFFFull) return GPULZ_ERR_INVALID_ARG;
   if (out_capacity < gpulz_max_compressed_size(n_bytes, chunk_size)) return GPULZ_ERR_CAPACITY;
-  const EncLayoutHost L = enc_layout(chunks, chunk_size);
+  const EncLayoutHost L = enc_layout(chunks);
   if (workspace_bytes < L.total) return GPULZ_ERR_CAPACITY;
   uint8_t* ws = (uint8_t*)d_workspace;
 
@@ -83,25 +79,14 @@ int gpulz_encode_timed(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, 
   ea.ws = word_size;
   ea.level = match_level;
   ea.num_chunks = (uint32_t)chunks;
-  ea.staging = ws + L.staging;
-  ea.entries = (uint2*)(ws + L.entries);
+  ea.out = (uint8_t*)d_out;
+  ea.out_bytes = d_out_bytes;
+  ea.flags = (uint64_t*)(ws + L.flags);
+  ea.ctl = ws + L.ctl;
+  if (launch_encode_init(ea, stream) != hipSuccess) return GPULZ_ERR_HIP;
   if (ev_start && hipEventRecord(ev_start, stream) != hipSuccess) return GPULZ_ERR_HIP;
   if (launch_encode_chunks(ea, stream) != hipSuccess) return GPULZ_ERR_HIP;
   if (ev_stop && hipEventRecord(ev_stop, stream) != hipSuccess) return GPULZ_ERR_HIP;
-
-  CompactArgs ca;
-  ca.staging = ea.staging;
-  ca.entries = ea.entries;
-  ca.offsets = (uint64_t*)(ws + L.offsets);
-  ca.tile_sums = (uint64_t*)(ws + L.tiles);
-  ca.out = (uint8_t*)d_out;
-  ca.out_bytes = d_out_bytes;
-  ca.n = n_bytes;
-  ca.cs = chunk_size;
-  ca.ws = word_size;
-  ca.num_chunks = (uint32_t)chunks;
-  ca.num_tiles = (uint32_t)((chunks + kTile - 1) / kTile);
-  if (launch_compact(ca, stream) != hipSuccess) return GPULZ_ERR_HIP;
   return GPULZ_OK;
 }
 

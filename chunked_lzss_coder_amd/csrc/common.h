@@ -108,22 +108,14 @@ struct EncodeArgs {
   uint64_t n;
   uint32_t cs, ws, level;
   uint32_t num_chunks;
-  uint8_t* staging;     // num_chunks * cs (+ slack), fixed stride cs
-  uint2* entries;       // num_chunks size-table entries
-};
-hipError_t launch_encode_chunks(const EncodeArgs& a, hipStream_t stream);
-
-struct CompactArgs {
-  const uint8_t* staging;
-  const uint2* entries;
-  uint64_t* offsets;    // num_chunks payload offsets (workspace)
-  uint64_t* tile_sums;  // num_tiles
-  uint8_t* out;
+  uint8_t* out;         // the stream
   uint64_t* out_bytes;
-  uint64_t n;
-  uint32_t cs, ws, num_chunks, num_tiles;
+  uint64_t* flags;      // num_chunks look-back words (workspace)
+  void* ctl;            // ticket counter and error flag (workspace)
 };
-hipError_t launch_compact(const CompactArgs& a, hipStream_t stream);
+uint64_t encode_ctl_bytes();
+hipError_t launch_encode_init(const EncodeArgs& a, hipStream_t stream);
+hipError_t launch_encode_chunks(const EncodeArgs& a, hipStream_t stream);
 
 struct DecodeParams {  // device-resident, written by the header kernel
   uint64_t n;

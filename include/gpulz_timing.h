@@ -6,8 +6,9 @@
  * same results, same errors) and in addition records ev_start on `stream`
  * immediately before the per-chunk kernel is enqueued and ev_stop
  * immediately after it:
- *   gpulz_encode_timed: around the chunk encode kernel (search, parse,
- *                       staging), excluding the size scan and stream assembly;
+ *   gpulz_encode_timed: around the fused chunk encode kernel (search, parse,
+ *                       offsets, stream assembly), excluding the small
+ *                       kernel that clears the look-back state;
  *   gpulz_decode_timed: around the chunk decode kernel, excluding the header
  *                       check and the size scan.
  * The caller creates both events (hipEventCreate) and reads them with
