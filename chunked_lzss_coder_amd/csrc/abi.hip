@@ -11,18 +11,21 @@ using namespace gpulz;
 namespace {
 
 constexpr uint64_t kAlign = 256;
+constexpr uint64_t kStagingSlack = 256;  // realigning copies read a few bytes past a slot
 inline uint64_t round_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline uint64_t num_chunks_of(uint64_t n, uint32_t cs) { return n / cs + ((n % cs) != 0); }
 
 struct EncLayoutHost {
-  uint64_t ctl, flags, total;
+  uint64_t ctl, tiles, staging, total;
 };
 
-EncLayoutHost enc_layout(uint64_t chunks) {
+// control block | compaction tile flags | one cs-byte payload slot per chunk
+EncLayoutHost enc_layout(uint64_t chunks, uint32_t cs) {
   EncLayoutHost L;
   L.ctl = 0;
-  L.flags = round_up(encode_ctl_bytes());
-  L.total = L.flags + round_up((chunks ? chunks : 1) * 8u);
+  L.tiles = round_up(encode_ctl_bytes());
+  L.staging = L.tiles + round_up((encode_tiles((uint32_t)chunks) + 1u) * 8u);
+  L.total = L.staging + round_up(chunks * cs + kStagingSlack);
   return L;
 }
 
@@ -53,7 +56,7 @@ uint64_t gpulz_max_compressed_size(uint64_t n_bytes, uint32_t chunk_size) {
 
 uint64_t gpulz_encode_workspace_size(uint64_t n_bytes, uint32_t chunk_size) {
   if (!chunk_size_ok(chunk_size)) return 0;
-  return enc_layout(num_chunks_of(n_bytes, chunk_size)).total;
+  return enc_layout(num_chunks_of(n_bytes, chunk_size), chunk_size).total;
 }
 
 uint64_t gpulz_decode_workspace_size(uint64_t in_bytes) { return dec_layout(dec_chunks_bound(in_bytes)).total; }
@@ -68,7 +71,8 @@ int gpulz_encode_timed(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, 
   const uint64_t chunks = num_chunks_of(n_bytes, chunk_size);
   if (chunks > 0xFFFFFFFFull) return GPULZ_ERR_INVALID_ARG;
   if (out_capacity < gpulz_max_compressed_size(n_bytes, chunk_size)) return GPULZ_ERR_CAPACITY;
-  const EncLayoutHost L = enc_layout(chunks);
+  if (chunks > 0xFFFFFFFFull - 1024u) return GPULZ_ERR_INVALID_ARG;
+  const EncLayoutHost L = enc_layout(chunks, chunk_size);
   if (workspace_bytes < L.total) return GPULZ_ERR_CAPACITY;
   uint8_t* ws = (uint8_t*)d_workspace;
 
@@ -81,12 +85,13 @@ int gpulz_encode_timed(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, 
   ea.num_chunks = (uint32_t)chunks;
   ea.out = (uint8_t*)d_out;
   ea.out_bytes = d_out_bytes;
-  ea.flags = (uint64_t*)(ws + L.flags);
+  ea.staging = ws + L.staging;
+  ea.tile_flags = (uint64_t*)(ws + L.tiles);
   ea.ctl = ws + L.ctl;
-  if (launch_encode_init(ea, stream) != hipSuccess) return GPULZ_ERR_HIP;
   if (ev_start && hipEventRecord(ev_start, stream) != hipSuccess) return GPULZ_ERR_HIP;
   if (launch_encode_chunks(ea, stream) != hipSuccess) return GPULZ_ERR_HIP;
   if (ev_stop && hipEventRecord(ev_stop, stream) != hipSuccess) return GPULZ_ERR_HIP;
+  if (launch_compact(ea, stream) != hipSuccess) return GPULZ_ERR_HIP;
   return GPULZ_OK;
 }
 

@@ -108,14 +108,16 @@ struct EncodeArgs {
   uint64_t n;
   uint32_t cs, ws, level;
   uint32_t num_chunks;
-  uint8_t* out;         // the stream
+  uint8_t* out;          // the stream
   uint64_t* out_bytes;
-  uint64_t* flags;      // num_chunks look-back words (workspace)
-  void* ctl;            // ticket counter and error flag (workspace)
+  uint8_t* staging;      // num_chunks * cs bytes (+ slack): one payload slot per chunk
+  uint64_t* tile_flags;  // one look-back word per compaction tile
+  void* ctl;             // error flag
 };
 uint64_t encode_ctl_bytes();
-hipError_t launch_encode_init(const EncodeArgs& a, hipStream_t stream);
+uint64_t encode_tiles(uint32_t num_chunks);
 hipError_t launch_encode_chunks(const EncodeArgs& a, hipStream_t stream);
+hipError_t launch_compact(const EncodeArgs& a, hipStream_t stream);
 
 struct DecodeParams {  // device-resident, written by the header kernel
   uint64_t n;

@@ -1,12 +1,12 @@
 // encode.hip -- chunked LZSS encode for gfx950, one fused pass.
 //
-// A "team" of WPC wave64s owns one chunk at a time (WPC = 1 for chunks of up
-// to 1024 elements, so most of the work needs no workgroup barrier).  Teams
-// take chunks in ticket order from an atomic counter and assemble the stream
-// themselves: once a chunk's payload size is known it is published and the
-// chunk's output offset is found by a decoupled look-back over its
-// predecessors' published sizes, so flags and data go straight from LDS to
-// their final place in the stream (no staging area, no second pass).
+// A "team" of WPC wave64s owns one chunk (WPC = 1 for chunks of up to 1024
+// elements, so most of the work needs no workgroup barrier; a workgroup holds
+// CPW teams).  Teams assemble the stream themselves: once a chunk's payload
+// size is known it is published and the chunk's output offset is found by a
+// decoupled look-back over its predecessors' published sizes, so flags and
+// data go straight from LDS to their final place in the stream (no staging
+// area, no second pass).
 //
 // Per chunk (GPULZStage page paragraphs in brackets):
 //   1. load the chunk (zero padded past its real bytes) into LDS as E words;
@@ -14,10 +14,11 @@
 //   2. omask[p], bit o-1 = (x[p] == x[p-o]), o = 1..32 [exact-search
 //      paragraph]: each lane holds 8 consecutive positions and the 32 words
 //      before them in registers, so the 256 comparisons per lane read LDS once;
-//   3. doubling table S_k[p] = AND of omask over [p, p+k), k = 1..128, and a
-//      binary descent per position giving the exact longest run L <= 255 of
-//      any offset and the smallest offset reaching it [exact-search and
-//      long-match paragraphs];
+//   3. a base-4 doubling table S_k[p] = AND of omask over [p, p+k) for
+//      k = 1, 4, 16, 64, and a 4-round descent per position (up to three
+//      steps of k per round, so L <= 255) giving the exact longest run of any
+//      offset, capped at 255, and the smallest offset reaching it
+//      [exact-search and long-match paragraphs];
 //   4. level 1: 2048-bucket table of position+1 per sub-block, lookups and
 //      atomicMax inserts separated by barriers [hashed-table paragraphs];
 //   5. greedy parse [provenance paragraph], in parallel: every 8-position
@@ -26,7 +27,9 @@
 //      segments then fixes the real entry of each segment;
 //   6. item counts from popcounts (two item sizes only) -> flag bytes F and
 //      data bytes D; raw when F + D >= real bytes [raw-fallback paragraph];
-//   7. look-back for the output offset, size-table row, payload bytes.
+//   7. the size is published first, the payload is built in LDS, and only
+//      then does the look-back wait for the output offset; then the size-table
+//      row and the payload bytes are written.
 #include "common.h"
 
 namespace gpulz {
@@ -71,22 +74,25 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
 
 // Decoupled look-back over the chunks' published payload sizes (one wave).
 // Each flag is one 64-bit word {state:2, value:62}, written with one atomic
-// store, so a reader never sees a state without its value.  Returns the
-// exclusive prefix (output offset of chunk c's payload).
+// store, so a reader never sees a state without its value.  Nothing else is
+// published through a flag, so relaxed device-scope atomics suffice: they go
+// to the device coherence point without the L2 writeback / invalidate that
+// release / acquire ordering costs on a part with one L2 per XCD.
+// Returns the exclusive prefix (output offset of chunk c's payload).
 __device__ uint64_t look_back(uint64_t* flags, uint32_t c, uint64_t agg, uint32_t* err) {
   const uint32_t lane = lane_id();
   if (c == 0) {
-    if (lane == 0) __hip_atomic_store(&flags[0], kFlagIncl | agg, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) __hip_atomic_store(&flags[0], kFlagIncl | agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return 0;
   }
-  if (lane == 0) __hip_atomic_store(&flags[c], kFlagAgg | agg, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) __hip_atomic_store(&flags[c], kFlagAgg | agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   uint64_t prefix = 0;
   int64_t j = (int64_t)c - 1;
   uint32_t spins = 0;
   while (true) {
     const int64_t idx = j - (int64_t)lane;
     uint64_t f = kFlagIncl;  // before chunk 0: an inclusive prefix of 0
-    if (idx >= 0) f = __hip_atomic_load(&flags[idx], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+    if (idx >= 0) f = __hip_atomic_load(&flags[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint64_t incl = __ballot((f >> 62) == 2u);
     const uint64_t inval = __ballot((f >> 62) == 0u);
     const uint32_t first = incl ? (uint32_t)__builtin_ctzll(incl) : 64u;
@@ -104,7 +110,7 @@ __device__ uint64_t look_back(uint64_t* flags, uint32_t c, uint64_t agg, uint32_
     j -= 64;
   }
   if (lane == 0)
-    __hip_atomic_store(&flags[c], kFlagIncl | (prefix + agg), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&flags[c], kFlagIncl | (prefix + agg), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return prefix;
 }
 
@@ -134,23 +140,24 @@ __device__ __forceinline__ void put_le(uint8_t* p, uint64_t v, int nb) {
 }
 
 struct EncCtl {
-  uint32_t ticket;
-  uint32_t error;
-  uint32_t pad[62];
+  uint32_t error;  // set if a look-back ever gave up waiting
+  uint32_t pad[63];
 };
 
-template <int WS, int E>
+constexpr uint32_t kCTile = 64;  // chunks per compaction tile
+__host__ __device__ inline uint32_t num_tiles_of(uint32_t chunks) { return (chunks + kCTile - 1u) / kCTile; }
+
+template <int WS, int E, int LEVEL>
 struct Lay {
   static constexpr uint32_t CS = (uint32_t)E * WS;
   static constexpr uint32_t NW64 = E / 64;  // 64-position words
   static constexpr uint32_t NSEG = E / 8;   // 8-position parse segments
-  // word offsets inside the per-chunk region, after X[E]:
-  //   phase A: LV = 8 doubling levels of E words
-  //   phase B: LO (E) | XQ (E) | hash table (2048) or
-  //            LO (E) | XQ (E) | ISB (E/32) | LMB (E/32) | FLG (E/32) | STG (CS/4 + 4)
-  static constexpr uint32_t RB = 2u * E;
-  static constexpr uint32_t R =
-      (cmax(cmax(8u * E, RB + kHashSize), RB + 3u * (E / 32u) + CS / 4u + 8u) + 3u) & ~3u;
+  // Word offsets inside the per-chunk region, after X[E]:
+  //   search: LV = S_1 | S_4 | S_16 | S_64 (4 x E words)
+  //   level 1: LO (E) | hash table (2048)
+  //   parse:   LO (E) | XQ (E) | ISB (E/32) | LMB (E/32) | FLG (E/32) | STG (CS/4 + 8)
+  static constexpr uint32_t RP = 2u * E + 3u * (E / 32u) + CS / 4u + 8u;
+  static constexpr uint32_t R = (cmax(cmax(4u * E, LEVEL ? (uint32_t)E + kHashSize : 0u), RP) + 3u) & ~3u;
   static constexpr uint32_t MISC = 2u * (E / 64u + 1u) + 8u;
   static constexpr uint32_t TOTAL = (E + R + MISC + 3u) & ~3u;  // words per chunk, 16-byte multiple
 };
@@ -158,100 +165,90 @@ struct Lay {
 template <int WS, int E, int LEVEL, int WPC, int CPW>
 __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* __restrict__ in, uint64_t n,
                                                                  uint32_t num_chunks, uint8_t* __restrict__ out,
-                                                                 uint64_t* __restrict__ out_bytes,
-                                                                 uint64_t* __restrict__ flags,
-                                                                 EncCtl* __restrict__ ctl) {
-  using L = Lay<WS, E>;
+                                                                 uint8_t* __restrict__ staging,
+                                                                 uint64_t* __restrict__ tile_flags,
+                                                                 uint32_t num_tiles, EncCtl* __restrict__ ctl) {
+  using L = Lay<WS, E, LEVEL>;
   constexpr uint32_t CS = L::CS;
-  constexpr uint32_t TL = 64u * WPC;          // lanes per team
-  constexpr uint32_t PPL = E / TL;            // positions per lane (strided)
+  constexpr uint32_t TL = 64u * WPC;  // lanes per team
+  constexpr uint32_t PPL = E / TL;    // positions per lane (strided p = g + i*TL)
+  constexpr uint32_t NR = E / 64u;    // 64-position words
   constexpr uint32_t MM = min_match<WS>();
   static_assert(WPC == 1 || CPW == 1, "a team is one wave or the whole workgroup");
   static_assert(E % (8 * TL) == 0 || E == 256, "omask passes");
   __shared__ __attribute__((aligned(16))) uint32_t lds_all[CPW * L::TOTAL];
   const uint32_t team = threadIdx.x / TL;
-  const uint32_t g = threadIdx.x % TL;        // lane within the team
+  const uint32_t g = threadIdx.x % TL;  // lane within the team
   const uint32_t lane = lane_id();
   uint32_t* X = lds_all + team * L::TOTAL;
   uint32_t* LV = X + E;
   uint32_t* LO = LV;
   uint32_t* XQ = LV + E;
-  uint32_t* T = LV + L::RB;
-  uint32_t* ISB = LV + L::RB;
+  uint32_t* T = LV + E;
+  uint32_t* ISB = LV + 2u * E;
   uint32_t* LMB = ISB + E / 32u;
   uint32_t* FLG = LMB + E / 32u;
   uint8_t* STG = (uint8_t*)(FLG + E / 32u);
   uint32_t* MISC = LV + L::R;
-  uint32_t* KB = MISC;                        // items before 64-position word w
-  uint32_t* MB = MISC + (E / 64u + 1u);       // matches before word w
-  uint32_t* SC = MB + (E / 64u + 1u);         // scalars
-  const uint64_t* IS64 = (const uint64_t*)ISB;
-  const uint64_t* LM64 = (const uint64_t*)LMB;
+  uint32_t* KB = MISC;                   // items before 64-position word w
+  uint32_t* MB = MISC + (E / 64u + 1u);  // matches before word w
+  uint32_t* SC = MB + (E / 64u + 1u);    // scalars
   uint8_t* table = out + kHeaderBytes;
-  uint8_t* payload = table + (uint64_t)kEntryBytes * num_chunks;
 
-  while (true) {
-    // ---- ticket -------------------------------------------------------------------
-    uint32_t c;
-    if (WPC == 1) {
-      uint32_t t = 0;
-      if (lane == 0) t = atomicAdd(&ctl->ticket, 1u);
-      c = __builtin_amdgcn_readfirstlane(t);
-    } else {
-      if (g == 0) SC[0] = atomicAdd(&ctl->ticket, 1u);
-      __syncthreads();
-      c = SC[0];
-      __syncthreads();
-    }
-    if (c >= num_chunks) break;
-    const uint64_t base = (uint64_t)c * CS;
-    const uint32_t bc = (uint32_t)((n - base) < CS ? (n - base) : CS);
-    const uint8_t* src = in + base;
+  // ---- chunk of this team -----------------------------------------------------------
+  const uint32_t c = blockIdx.x * (uint32_t)CPW + team;
+  if (c >= num_chunks) return;
+  const uint64_t base = (uint64_t)c * CS;
+  const uint32_t bc = (uint32_t)((n - base) < CS ? (n - base) : CS);
+  const uint8_t* src = in + base;
 
-    // ---- 1. load + zero vote ---------------------------------------------------------
-    uint32_t any = 0;
-    if (bc == CS && (((uintptr_t)src) & 15u) == 0) {
-      const uint4* s4 = (const uint4*)src;
-      for (uint32_t i = g; i < CS / 16u; i += TL) {
-        const uint4 v = s4[i];
-        any |= v.x | v.y | v.z | v.w;
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        if (WS == 4) {
-          *(uint4*)(X + 4 * i) = v;
-        } else if (WS == 2) {
+  // ---- 1. load + zero vote ---------------------------------------------------------
+  uint32_t any = 0;
+  if (bc == CS && (((uintptr_t)src) & 15u) == 0) {
+    const uint4* s4 = (const uint4*)src;
+    for (uint32_t i = g; i < CS / 16u; i += TL) {
+      const uint4 v = s4[i];
+      any |= v.x | v.y | v.z | v.w;
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      if (WS == 4) {
+        *(uint4*)(X + 4 * i) = v;
+      } else if (WS == 2) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            X[8 * i + 2 * j] = w[j] & 0xFFFFu;
-            X[8 * i + 2 * j + 1] = w[j] >> 16;
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) X[16 * i + 4 * j + b] = (w[j] >> (8 * b)) & 0xFFu;
+        for (int j = 0; j < 4; ++j) {
+          X[8 * i + 2 * j] = w[j] & 0xFFFFu;
+          X[8 * i + 2 * j + 1] = w[j] >> 16;
         }
-      }
-    } else {
-      for (uint32_t i = g; i < (uint32_t)E; i += TL) {
-        uint32_t w = 0;
+      } else {
 #pragma unroll
-        for (int b = 0; b < WS; ++b) {
-          const uint32_t j = i * WS + b;
-          if (j < bc) w |= (uint32_t)src[j] << (8 * b);
-        }
-        X[i] = w;
-        any |= w;
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) X[16 * i + 4 * j + b] = (w[j] >> (8 * b)) & 0xFFu;
       }
     }
-    bool nonzero;
-    if (WPC == 1) {
-      nonzero = __ballot(any != 0u) != 0ull;
-      wave_sync();
-    } else {
-      nonzero = __syncthreads_or(any != 0u);
+  } else {
+    for (uint32_t i = g; i < (uint32_t)E; i += TL) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int b = 0; b < WS; ++b) {
+        const uint32_t j = i * WS + b;
+        if (j < bc) w |= (uint32_t)src[j] << (8 * b);
+      }
+      X[i] = w;
+      any |= w;
     }
-    uint32_t K = 0, M = 0;
-    if (nonzero) {
+  }
+  bool nonzero;
+  if (WPC == 1) {
+    nonzero = __ballot(any != 0u) != 0ull;
+    wave_sync();
+  } else {
+    nonzero = __syncthreads_or(any != 0u);
+  }
+
+  uint32_t K = 0, M = 0;
+  uint64_t isw[WPC == 1 ? NR : 1], lmw[WPC == 1 ? NR : 1];  // item / match-capable bits (one wave)
+  uint32_t kb[WPC == 1 ? NR : 1], mb[WPC == 1 ? NR : 1];
+  if (nonzero) {
     // ---- 2. omask: 8 consecutive positions per lane, window in registers -------------
     {
       constexpr uint32_t PPASS = (E == 256 ? 4u : 8u);  // positions per lane per pass
@@ -293,16 +290,19 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
     }
     team_sync<WPC>();
 
-    // ---- 3. doubling table + descent ---------------------------------------------------
+    // ---- 3. base-4 doubling table S_4, S_16, S_64 and a 4-round descent ------------
+    // S_k[p] = AND of omask over [p, p+k) when p + k <= E, else 0.
 #pragma unroll
-    for (uint32_t lv = 1; lv < 8; ++lv) {
-      const uint32_t half = 1u << (lv - 1);
+    for (uint32_t lv = 1; lv < 4; ++lv) {
+      const uint32_t k = 1u << (2 * lv), step = k >> 2;
       const uint32_t* prev = LV + (lv - 1) * E;
       uint32_t* cur = LV + lv * E;
 #pragma unroll
       for (uint32_t i = 0; i < PPL; ++i) {
         const uint32_t p = g + i * TL;
-        cur[p] = (p + half < (uint32_t)E) ? (prev[p] & prev[p + half]) : 0u;
+        uint32_t v = 0;
+        if (p + k <= (uint32_t)E) v = prev[p] & prev[p + step] & prev[p + 2 * step] & prev[p + 3 * step];
+        cur[p] = v;
       }
       team_sync<WPC>();
     }
@@ -310,18 +310,27 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
 #pragma unroll
     for (uint32_t i = 0; i < PPL; ++i) {
       const uint32_t p = g + i * TL;
-      uint32_t surv = LV[7 * E + p], Ln = 0;
-      if (surv) Ln = 128;
-      else surv = ~0u;
+      uint32_t surv = ~0u, Ln = 0;
+      // digits of L in base 4, most significant first: at most 3 steps of k per
+      // round, so L <= 3 * (64 + 16 + 4 + 1) = 255, the length cap
 #pragma unroll
-      for (int lv = 6; lv >= 0; --lv) {
-        const uint32_t k = 1u << lv;
-        if (p + Ln + k <= (uint32_t)E) {
-          const uint32_t t = surv & LV[(uint32_t)lv * E + p + Ln];
-          if (t) {
-            surv = t;
-            Ln += k;
-          }
+      for (int lv = 3; lv >= 0; --lv) {
+        const uint32_t k = 1u << (2 * lv);
+        const uint32_t* S = LV + (uint32_t)lv * E;
+        const uint32_t q0 = p + Ln, q1 = q0 + k, q2 = q1 + k;
+        const uint32_t a = q0 < (uint32_t)E ? S[q0] : 0u;
+        const uint32_t b = q1 < (uint32_t)E ? S[q1] : 0u;
+        const uint32_t d = q2 < (uint32_t)E ? S[q2] : 0u;
+        const uint32_t t1 = surv & a, t2 = t1 & b, t3 = t2 & d;
+        if (t3) {
+          surv = t3;
+          Ln += 3u * k;
+        } else if (t2) {
+          surv = t2;
+          Ln += 2u * k;
+        } else if (t1) {
+          surv = t1;
+          Ln += k;
         }
       }
       lo[i] = Ln ? (Ln | (((uint32_t)__builtin_ctz(surv) + 1u) << 8)) : 0u;
@@ -334,7 +343,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
     // ---- 4. level 1 ----------------------------------------------------------------------
     if (LEVEL == 1) {
       for (uint32_t i = g; i < kHashSize; i += TL) T[i] = 0u;
-      team_sync<WPC>();  // T overlays dead doubling levels
+      team_sync<WPC>();  // T overlays dead table levels
       constexpr uint32_t SB = E / kSubBlocks;
 #pragma unroll 1
       for (uint32_t s = 0; s < kSubBlocks; ++s) {
@@ -386,149 +395,213 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
                                       ex[3] | (im[3] << 16));
       *(uint4*)(XQ + p0 + 4) = make_uint4(ex[4] | (im[4] << 16), ex[5] | (im[5] << 16),
                                           ex[6] | (im[6] << 16), ex[7] | (im[7] << 16));
-      ((uint8_t*)LMB)[sg] = (uint8_t)lmb;
-      ((uint8_t*)ISB)[sg] = 0;
+      if (WPC > 1) {
+        ((uint8_t*)LMB)[sg] = (uint8_t)lmb;
+        ((uint8_t*)ISB)[sg] = 0;
+      }
     }
     team_sync<WPC>();
-    // (b) hop chain: the real entry of every segment the parse passes through
-    if (g == 0) {
+    // (b) hops: the parse's real entry into every segment it passes through
+    if constexpr (WPC == 1) {
+      // exits held in registers (lane j of word i = position 64i + j); the hop
+      // position P is uniform, so each hop is one readlane
+      uint32_t xqr[NR];
+#pragma unroll
+      for (uint32_t i = 0; i < NR; ++i) {
+        const uint32_t p = 64u * i + lane;
+        xqr[i] = XQ[p];
+        lmw[i] = __ballot((LO[p] & 0xFFu) >= MM);
+      }
       uint32_t P = 0;
-      while (P < (uint32_t)E) {
-        const uint32_t xq = XQ[P];
-        ((uint8_t*)ISB)[P >> 3] = (uint8_t)(xq >> 16);
-        P = xq & 0xFFFFu;
-      }
-    }
-    team_sync<WPC>();
-
-    // ---- 6. counts, payload size ------------------------------------------------------------
-    if (g < 64u) {
-      uint32_t kc = 0, mc = 0;
-      if (g < L::NW64) {
-        const uint64_t is = IS64[g];
-        kc = __builtin_popcountll(is);
-        mc = __builtin_popcountll(is & LM64[g]);
-      }
-      uint32_t ki = kc, mi = mc;
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t a = __shfl_up(ki, d, 64), b = __shfl_up(mi, d, 64);
-        if (lane >= (uint32_t)d) {
-          ki += a;
-          mi += b;
+      for (uint32_t i = 0; i < NR; ++i) {
+        uint64_t acc = 0;
+        while (P < 64u * (i + 1u)) {
+          const uint32_t xq = __builtin_amdgcn_readlane(xqr[i], P & 63u);
+          acc |= (uint64_t)(xq >> 16) << (P & 56u);
+          P = xq & 0xFFFFu;
         }
+        isw[i] = acc;
       }
-      if (g < L::NW64) {
-        KB[g] = ki - kc;
-        MB[g] = mi - mc;
+      // ---- 6. counts -------------------------------------------------------------------
+#pragma unroll
+      for (uint32_t i = 0; i < NR; ++i) {
+        kb[i] = K;
+        mb[i] = M;
+        K += (uint32_t)__builtin_popcountll(isw[i]);
+        M += (uint32_t)__builtin_popcountll(isw[i] & lmw[i]);
       }
-      if (g == L::NW64 - 1u) {
-        SC[1] = ki;
-        SC[2] = mi;
-      }
-    }
-    team_sync<WPC>();
-    K = SC[1];
-    M = SC[2];
-    }  // nonzero
-    const uint32_t F = (K + 7u) / 8u;
-    const uint32_t D = (uint32_t)WS * (K - M) + 2u * M;
-    const bool raw = nonzero && F + D >= bc;
-    const uint32_t size = !nonzero ? 0u : (raw ? bc : F + D);
-
-    // ---- 7. offset, entry, payload ----------------------------------------------------------
-    if (g < 64u) {
-      const uint64_t pre = look_back(flags, c, size, &ctl->error);
+    } else {
       if (g == 0) {
-        SC[4] = (uint32_t)pre;
-        SC[5] = (uint32_t)(pre >> 32);
-        const uint2 ent = !nonzero ? make_uint2(0u, 0u) : (raw ? make_uint2(0u, kRawBit | bc) : make_uint2(F, D));
-        uint8_t* row = table + kEntryBytes * (uint64_t)c;
-        if ((((uintptr_t)row) & 7u) == 0) {
-          *(uint2*)row = ent;
-        } else {
-          put_le(row, ent.x, 4);
-          put_le(row + 4, ent.y, 4);
-        }
-        if (c == num_chunks - 1u) {
-          const uint64_t pb = pre + size;
-          put_le(out + 0, kMagic, 4);
-          out[4] = (uint8_t)kVersion;
-          out[5] = (uint8_t)WS;
-          out[6] = 0;
-          out[7] = 0;
-          put_le(out + 8, CS, 4);
-          put_le(out + 12, num_chunks, 4);
-          put_le(out + 16, n, 8);
-          put_le(out + 24, pb, 8);
-          *out_bytes = __hip_atomic_load(&ctl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                           ? 0ull
-                           : (uint64_t)kHeaderBytes + (uint64_t)kEntryBytes * num_chunks + pb;
+        uint32_t P = 0;
+        while (P < (uint32_t)E) {
+          const uint32_t xq = XQ[P];
+          ((uint8_t*)ISB)[P >> 3] = (uint8_t)(xq >> 16);
+          P = xq & 0xFFFFu;
         }
       }
-    }
-    if (nonzero && !raw) {
-      for (uint32_t i = g; i < E / 32u; i += TL) FLG[i] = 0u;
-    }
-    team_sync<WPC>();
-    const uint64_t pre = (uint64_t)SC[4] | ((uint64_t)SC[5] << 32);
-    uint8_t* dst = payload + pre;
-    if (raw) {
-      // the real bytes, read back from the LDS copy of the chunk
-      if (WS == 4) {
-        lds_to_global(dst, (const uint8_t*)X, bc, g, TL);
-      } else {
-        uint8_t* xb = STG;  // repack the words as bytes first
-        for (uint32_t i = g; i < CS / 4u; i += TL) {
-          uint32_t v;
-          if (WS == 2) v = X[2 * i] | (X[2 * i + 1] << 16);
-          else v = X[4 * i] | (X[4 * i + 1] << 8) | (X[4 * i + 2] << 16) | (X[4 * i + 3] << 24);
-          ((uint32_t*)xb)[i] = v;
+      team_sync<WPC>();
+      // ---- 6. counts (first wave) --------------------------------------------------------
+      const uint64_t* IS64 = (const uint64_t*)ISB;
+      const uint64_t* LM64 = (const uint64_t*)LMB;
+      if (g < 64u) {
+        uint32_t kc = 0, mc = 0;
+        if (g < NR) {
+          const uint64_t is = IS64[g];
+          kc = __builtin_popcountll(is);
+          mc = __builtin_popcountll(is & LM64[g]);
         }
-        team_sync<WPC>();
-        lds_to_global(dst, xb, bc, g, TL);
-      }
-    } else if (nonzero) {
+        uint32_t ki = kc, mi = mc;
 #pragma unroll
-      for (uint32_t i = 0; i < PPL; ++i) {
-        const uint32_t p = g + i * TL;
-        const uint32_t wi = p >> 6;
-        const uint64_t is = IS64[wi];
-        const uint64_t ms = is & LM64[wi];
-        const uint64_t bit = 1ull << (p & 63u);
-        if (!(is & bit)) continue;
-        const uint64_t below = bit - 1ull;
-        const uint32_t k = KB[wi] + (uint32_t)__builtin_popcountll(is & below);
-        const uint32_t m = MB[wi] + (uint32_t)__builtin_popcountll(ms & below);
-        const uint32_t off = (uint32_t)WS * (k - m) + 2u * m;
-        if (ms & bit) {
+        for (int d = 1; d < 64; d <<= 1) {
+          const uint32_t a = __shfl_up(ki, d, 64), b = __shfl_up(mi, d, 64);
+          if (lane >= (uint32_t)d) {
+            ki += a;
+            mi += b;
+          }
+        }
+        if (g < NR) {
+          KB[g] = ki - kc;
+          MB[g] = mi - mc;
+        }
+        if (g == NR - 1u) {
+          SC[1] = ki;
+          SC[2] = mi;
+        }
+      }
+      team_sync<WPC>();
+      K = SC[1];
+      M = SC[2];
+    }
+  }  // nonzero
+  const uint32_t F = (K + 7u) / 8u;
+  const uint32_t D = (uint32_t)WS * (K - M) + 2u * M;
+  const bool raw = nonzero && F + D >= bc;
+  const uint32_t size = !nonzero ? 0u : (raw ? bc : F + D);
+
+  // ---- 7. size-table row, payload into the chunk's staging slot --------------------
+  // Flags first (bit k of the bitmap = item k is a match), then the data bytes
+  // right after them, so the slot holds the payload exactly as it will appear
+  // in the stream; the compaction kernel moves it to its final offset.
+  uint32_t* STG32 = (uint32_t*)STG;
+  uint32_t* slot = (uint32_t*)(staging + base);
+  if (nonzero && !raw) {
+    for (uint32_t i = g; i < (F + 3u) / 4u; i += TL) STG32[i] = 0u;
+    team_sync<WPC>();
+    if constexpr (WPC == 1) {
+#pragma unroll
+      for (uint32_t i = 0; i < NR; ++i) {
+        const uint64_t is = isw[i], ms = is & lmw[i];
+        if ((ms >> lane) & 1ull) {
+          const uint32_t k = kb[i] + mbcnt64(is);
+          atomicOr(&STG32[k >> 5], 1u << (k & 31u));
+        }
+      }
+      team_sync<WPC>();
+#pragma unroll
+      for (uint32_t i = 0; i < NR; ++i) {
+        const uint32_t p = 64u * i + lane;
+        const uint64_t is = isw[i], ms = is & lmw[i];
+        if (!((is >> lane) & 1ull)) continue;
+        const uint32_t k = kb[i] + mbcnt64(is);
+        const uint32_t m = mb[i] + mbcnt64(ms);
+        const uint32_t off = F + (uint32_t)WS * (k - m) + 2u * m;
+        if ((ms >> lane) & 1ull) {
           const uint32_t v = LO[p];
           STG[off] = (uint8_t)v;
           STG[off + 1] = (uint8_t)(v >> 8);
-          atomicOr(&FLG[k >> 5], 1u << (k & 31u));
         } else {
           const uint32_t v = X[p];
 #pragma unroll
           for (int b = 0; b < WS; ++b) STG[off + b] = (uint8_t)(v >> (8 * b));
         }
       }
+    } else {
+      const uint64_t* IS64 = (const uint64_t*)ISB;
+      const uint64_t* LM64 = (const uint64_t*)LMB;
+#pragma unroll
+      for (uint32_t i = 0; i < PPL; ++i) {
+        const uint32_t p = g + i * TL;
+        const uint32_t wi = p >> 6;
+        const uint64_t is = IS64[wi], ms = is & LM64[wi];
+        const uint64_t bit = 1ull << (p & 63u);
+        if (ms & bit) {
+          const uint32_t k = KB[wi] + (uint32_t)__builtin_popcountll(is & (bit - 1ull));
+          atomicOr(&STG32[k >> 5], 1u << (k & 31u));
+        }
+      }
       team_sync<WPC>();
-      lds_to_global(dst, (const uint8_t*)FLG, F, g, TL);
-      lds_to_global(dst + F, STG, D, g, TL);
+#pragma unroll
+      for (uint32_t i = 0; i < PPL; ++i) {
+        const uint32_t p = g + i * TL;
+        const uint32_t wi = p >> 6;
+        const uint64_t is = IS64[wi], ms = is & LM64[wi];
+        const uint64_t bit = 1ull << (p & 63u);
+        if (!(is & bit)) continue;
+        const uint64_t below = bit - 1ull;
+        const uint32_t k = KB[wi] + (uint32_t)__builtin_popcountll(is & below);
+        const uint32_t m = MB[wi] + (uint32_t)__builtin_popcountll(ms & below);
+        const uint32_t off = F + (uint32_t)WS * (k - m) + 2u * m;
+        if (ms & bit) {
+          const uint32_t v = LO[p];
+          STG[off] = (uint8_t)v;
+          STG[off + 1] = (uint8_t)(v >> 8);
+        } else {
+          const uint32_t v = X[p];
+#pragma unroll
+          for (int b = 0; b < WS; ++b) STG[off + b] = (uint8_t)(v >> (8 * b));
+        }
+      }
     }
-    team_sync<WPC>();  // LDS is reused by the next chunk
+    team_sync<WPC>();
+    for (uint32_t i = g; i < (F + D + 3u) / 4u; i += TL) slot[i] = STG32[i];
+  } else if (raw) {
+    if (WS == 4) {
+      for (uint32_t i = g; i < CS / 4u; i += TL) slot[i] = X[i];
+    } else {
+      for (uint32_t i = g; i < CS / 4u; i += TL) {  // repack the words as bytes
+        uint32_t v;
+        if (WS == 2) v = X[2 * i] | (X[2 * i + 1] << 16);
+        else v = X[4 * i] | (X[4 * i + 1] << 8) | (X[4 * i + 2] << 16) | (X[4 * i + 3] << 24);
+        slot[i] = v;
+      }
+    }
+  }
+  if (g == 0) {
+    const uint2 ent = !nonzero ? make_uint2(0u, 0u) : (raw ? make_uint2(0u, kRawBit | bc) : make_uint2(F, D));
+    uint8_t* row = table + kEntryBytes * (uint64_t)c;
+    if ((((uintptr_t)row) & 7u) == 0) {
+      *(uint2*)row = ent;
+    } else {
+      put_le(row, ent.x, 4);
+      put_le(row + 4, ent.y, 4);
+    }
+    // the first team of workgroup b clears the compaction kernel's tile flag b
+    // (there are never more tiles than workgroups), workgroup 0 the error flag
+    if (team == 0 && blockIdx.x < num_tiles) tile_flags[blockIdx.x] = 0ull;
+    if (team == 0 && blockIdx.x == 0) ctl->error = 0u;
   }
 }
 
-__global__ void encode_init_kernel(uint64_t* __restrict__ flags, uint32_t num_chunks, EncCtl* __restrict__ ctl,
-                                   uint8_t* __restrict__ out, uint64_t* __restrict__ out_bytes, uint64_t n,
-                                   uint32_t cs, uint32_t ws) {
-  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < num_chunks) flags[i] = 0ull;
-  if (i == 0) {
-    ctl->ticket = 0u;
-    ctl->error = 0u;
-    if (num_chunks == 0) {  // empty input: the header is the whole stream
+// Compaction: one workgroup per tile of kCTile chunks.  Reads the tile's
+// size-table rows, scans the payload sizes, finds the tile's output offset
+// by decoupled look-back over the tiles before it, then moves every payload
+// from its staging slot to its place in the stream.  The last tile writes
+// the header and the stream length.
+__global__ __launch_bounds__(kBlock) void compact_kernel(const uint8_t* __restrict__ staging, uint32_t cs,
+                                                         uint32_t ws, uint64_t n, uint32_t num_chunks,
+                                                         uint32_t num_tiles, uint8_t* __restrict__ out,
+                                                         uint64_t* __restrict__ out_bytes,
+                                                         uint64_t* __restrict__ tile_flags,
+                                                         EncCtl* __restrict__ ctl) {
+  __shared__ uint32_t sz[kCTile];
+  __shared__ uint32_t off[kCTile];
+  __shared__ uint64_t tile_pre;
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const uint8_t* table = out + kHeaderBytes;
+  uint8_t* payload = out + kHeaderBytes + (uint64_t)kEntryBytes * num_chunks;
+  if (num_chunks == 0) {  // empty input: the header is the whole stream
+    if (tid == 0) {
       put_le(out + 0, kMagic, 4);
       out[4] = (uint8_t)kVersion;
       out[5] = (uint8_t)ws;
@@ -540,18 +613,115 @@ __global__ void encode_init_kernel(uint64_t* __restrict__ flags, uint32_t num_ch
       put_le(out + 24, 0ull, 8);
       *out_bytes = kHeaderBytes;
     }
+    return;
+  }
+  const uint32_t t = blockIdx.x;
+  const uint64_t c0 = (uint64_t)t * kCTile;
+  if (wave == 0) {
+    // sizes of the tile's chunks (one per lane), their scan, and the look-back
+    static_assert(kCTile == 64, "one chunk per lane of the first wave");
+    const uint64_t c = c0 + lane;
+    uint32_t size = 0;
+    if (c < num_chunks) {
+      const uint8_t* row = table + kEntryBytes * c;
+      uint2 e;
+      if ((((uintptr_t)table) & 7u) == 0) {
+        e = *(const uint2*)row;
+      } else {
+        e.x = (uint32_t)row[0] | ((uint32_t)row[1] << 8) | ((uint32_t)row[2] << 16) | ((uint32_t)row[3] << 24);
+        e.y = (uint32_t)row[4] | ((uint32_t)row[5] << 8) | ((uint32_t)row[6] << 16) | ((uint32_t)row[7] << 24);
+      }
+      // a row never stands for more than the chunk's real bytes; the clamp
+      // keeps every write inside the stream even if a row were wrong
+      const uint64_t start = c * cs;
+      const uint32_t bc = (uint32_t)((n - start) < cs ? (n - start) : cs);
+      const uint32_t s0 = entry_payload(e.x, e.y);
+      size = s0 < bc ? s0 : bc;
+    }
+    uint32_t inc = size;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t v = __shfl_up(inc, d, 64);
+      if (lane >= (uint32_t)d) inc += v;
+    }
+    sz[lane] = size;
+    off[lane] = inc - size;
+    const uint64_t tot = (uint64_t)__shfl(inc, 63, 64);
+    const uint64_t pre = look_back(tile_flags, t, tot, &ctl->error);
+    if (lane == 0) {
+      tile_pre = pre;
+      if (t == num_tiles - 1u) {
+        const uint64_t pb = pre + tot;
+        put_le(out + 0, kMagic, 4);
+        out[4] = (uint8_t)kVersion;
+        out[5] = (uint8_t)ws;
+        out[6] = 0;
+        out[7] = 0;
+        put_le(out + 8, cs, 4);
+        put_le(out + 12, num_chunks, 4);
+        put_le(out + 16, n, 8);
+        put_le(out + 24, pb, 8);
+        *out_bytes = __hip_atomic_load(&ctl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         ? 0ull
+                         : (uint64_t)kHeaderBytes + (uint64_t)kEntryBytes * num_chunks + pb;
+      }
+    }
+  }
+  __syncthreads();
+  const uint64_t pre = tile_pre;
+  // Each wave moves kCTile / kWaves chunks, kU at a time: the loads of kU
+  // chunks are issued before any of their stores, so their latencies overlap.
+  constexpr uint32_t PW = kCTile / kWaves, kU = 8;
+  for (uint32_t j0 = wave * PW; j0 < (wave + 1) * PW; j0 += kU) {
+    uint32_t lo[kU], hi[kU], head[kU], nbody[kU], size[kU];
+    uint8_t* dst[kU];
+    const uint8_t* sb[kU];
+#pragma unroll
+    for (uint32_t u = 0; u < kU; ++u) {
+      const uint32_t j = j0 + u;
+      const uint64_t c = c0 + j;
+      size[u] = c < num_chunks ? sz[j] : 0u;
+      sb[u] = staging + c * cs;
+      dst[u] = payload + pre + off[j];
+      uint32_t h = (uint32_t)((4u - ((uintptr_t)dst[u] & 3u)) & 3u);
+      head[u] = h > size[u] ? size[u] : h;
+      nbody[u] = (size[u] - head[u]) / 4u;
+      lo[u] = hi[u] = 0;
+      if (lane < nbody[u]) {
+        const uint32_t* sw = (const uint32_t*)sb[u];
+        const uint32_t s = head[u] + 4u * lane;
+        lo[u] = sw[s >> 2];
+        if (head[u]) hi[u] = sw[(s >> 2) + 1u];
+      }
+    }
+#pragma unroll
+    for (uint32_t u = 0; u < kU; ++u) {
+      if (size[u] == 0) continue;
+      const uint32_t h = head[u], nb = nbody[u];
+      if (lane < h) dst[u][lane] = sb[u][lane];
+      uint32_t* dw = (uint32_t*)(dst[u] + h);
+      if (lane < nb) dw[lane] = __builtin_amdgcn_alignbyte(hi[u], lo[u], h);
+      const uint32_t* sw = (const uint32_t*)sb[u];
+      for (uint32_t q = lane + 64u; q < nb; q += 64u) {  // payloads longer than 256 bytes
+        const uint32_t s = h + 4u * q;
+        const uint32_t l2 = sw[s >> 2];
+        const uint32_t h2 = h ? sw[(s >> 2) + 1u] : 0u;
+        dw[q] = __builtin_amdgcn_alignbyte(h2, l2, h);
+      }
+      const uint32_t t0 = h + 4u * nb;
+      if (t0 + lane < size[u]) dst[u][t0 + lane] = sb[u][t0 + lane];
+    }
   }
 }
 
 template <int WS, int E, int LEVEL>
 hipError_t launch_one(const EncodeArgs& a, hipStream_t stream) {
   constexpr int WPC = E <= 1024 ? 1 : E / 1024;
-  constexpr int CPW = E <= 512 ? 4 : (E <= 1024 ? 2 : 1);
+  constexpr int CPW = E <= 1024 ? 2 : 1;
   constexpr uint32_t threads = 64u * WPC * CPW;
-  const uint32_t want = (a.num_chunks + CPW - 1) / CPW;
-  const uint32_t grid = want < kMaxGrid ? want : kMaxGrid;
+  const uint32_t grid = (a.num_chunks + CPW - 1) / CPW;  // one chunk per team
   hipLaunchKernelGGL((encode_kernel<WS, E, LEVEL, WPC, CPW>), dim3(grid), dim3(threads), 0, stream, a.in, a.n,
-                     a.num_chunks, a.out, a.out_bytes, a.flags, (EncCtl*)a.ctl);
+                     a.num_chunks, a.out, a.staging, a.tile_flags, num_tiles_of(a.num_chunks), (EncCtl*)a.ctl);
   return hipGetLastError();
 }
 
@@ -563,12 +733,12 @@ hipError_t launch_level(const EncodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 uint64_t encode_ctl_bytes() { return sizeof(EncCtl); }
+uint64_t encode_tiles(uint32_t num_chunks) { return num_tiles_of(num_chunks); }
 
-hipError_t launch_encode_init(const EncodeArgs& a, hipStream_t stream) {
-  const uint32_t per = 256;
-  const uint32_t blocks = a.num_chunks == 0 ? 1u : (a.num_chunks + per - 1) / per;
-  hipLaunchKernelGGL(encode_init_kernel, dim3(blocks), dim3(per), 0, stream, a.flags, a.num_chunks,
-                     (EncCtl*)a.ctl, a.out, a.out_bytes, a.n, a.cs, a.ws);
+hipError_t launch_compact(const EncodeArgs& a, hipStream_t stream) {
+  const uint32_t tiles = num_tiles_of(a.num_chunks);
+  hipLaunchKernelGGL(compact_kernel, dim3(tiles ? tiles : 1u), dim3(kBlock), 0, stream, a.staging, a.cs, a.ws, a.n,
+                     a.num_chunks, tiles, a.out, a.out_bytes, a.tile_flags, (EncCtl*)a.ctl);
   return hipGetLastError();
 }
 

@@ -6,9 +6,10 @@
  * same results, same errors) and in addition records ev_start on `stream`
  * immediately before the per-chunk kernel is enqueued and ev_stop
  * immediately after it:
- *   gpulz_encode_timed: around the fused chunk encode kernel (search, parse,
- *                       offsets, stream assembly), excluding the small
- *                       kernel that clears the look-back state;
+ *   gpulz_encode_timed: around the chunk encode kernel (search, parse,
+ *                       size-table rows, payloads into staging slots),
+ *                       excluding the compaction kernel that scans the sizes
+ *                       and moves the payloads to their stream offsets;
  *   gpulz_decode_timed: around the chunk decode kernel, excluding the header
  *                       check and the size scan.
  * The caller creates both events (hipEventCreate) and reads them with
