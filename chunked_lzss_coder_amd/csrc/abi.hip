@@ -30,16 +30,17 @@ EncLayoutHost enc_layout(uint64_t chunks, uint32_t cs) {
 }
 
 struct DecLayoutHost {
-  uint64_t params, offsets, tiles, total;
+  uint64_t params, loc, tile_sums, tile_err, total;
 };
 
+// parameters | per-chunk offsets within scan tiles (u32) | tile totals | tile error flags
 DecLayoutHost dec_layout(uint64_t chunks_cap) {
-  const uint64_t tiles = (chunks_cap + kTile - 1) / kTile;
   DecLayoutHost L;
   L.params = 0;
-  L.offsets = round_up(sizeof(DecodeParams));
-  L.tiles = L.offsets + round_up(chunks_cap * 8u);
-  L.total = L.tiles + round_up((tiles ? tiles : 1) * 8u);
+  L.loc = round_up(decode_params_bytes());
+  L.tile_sums = L.loc + round_up((chunks_cap ? chunks_cap : 1) * 4u);
+  L.tile_err = L.tile_sums + round_up(256u * 8u);
+  L.total = L.tile_err + round_up(256u * 4u);
   return L;
 }
 
@@ -123,11 +124,11 @@ int gpulz_decode_timed(const void* d_in, uint64_t in_bytes, void* d_out, uint64_
   da.out_capacity = out_capacity;
   da.out_bytes = d_out_bytes;
   da.status = d_status;
-  da.params = (DecodeParams*)(ws + L.params);
-  da.offsets = (uint64_t*)(ws + L.offsets);
-  da.tile_sums = (uint64_t*)(ws + L.tiles);
+  da.params = ws + L.params;
+  da.loc = (uint32_t*)(ws + L.loc);
+  da.tile_sums = (uint64_t*)(ws + L.tile_sums);
+  da.tile_err = (uint32_t*)(ws + L.tile_err);
   da.chunks_cap = (uint32_t)cap;
-  da.tiles_cap = (uint32_t)((cap + kTile - 1) / kTile);
   da.ev_start = ev_start;
   da.ev_stop = ev_stop;
   if (launch_decode(da, stream) != hipSuccess) return GPULZ_ERR_HIP;

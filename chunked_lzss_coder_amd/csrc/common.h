@@ -119,13 +119,6 @@ uint64_t encode_tiles(uint32_t num_chunks);
 hipError_t launch_encode_chunks(const EncodeArgs& a, hipStream_t stream);
 hipError_t launch_compact(const EncodeArgs& a, hipStream_t stream);
 
-struct DecodeParams {  // device-resident, written by the header kernel
-  uint64_t n;
-  uint64_t payload_bytes;
-  uint64_t payload_base;  // byte offset of the first payload in the stream
-  uint32_t cs, ws, num_chunks, status;
-};
-
 struct DecodeArgs {
   const uint8_t* in;
   uint64_t in_bytes;
@@ -133,14 +126,16 @@ struct DecodeArgs {
   uint64_t out_capacity;
   uint64_t* out_bytes;
   uint32_t* status;
-  DecodeParams* params;
-  uint64_t* offsets;    // chunks_cap
-  uint64_t* tile_sums;  // tiles_cap
+  void* params;         // device-resident stream parameters
+  uint32_t* loc;        // chunks_cap payload offsets within their scan tile
+  uint64_t* tile_sums;  // <= 256 scan tiles
+  uint32_t* tile_err;   // <= 256 scan tiles
   uint32_t chunks_cap;  // host bound on num_chunks
-  uint32_t tiles_cap;
   hipEvent_t ev_start;  // optional, recorded around the chunk decode kernel
   hipEvent_t ev_stop;
 };
+uint32_t decode_tile_chunks(uint32_t chunks_cap);
+uint64_t decode_params_bytes();
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace gpulz

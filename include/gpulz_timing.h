@@ -10,8 +10,8 @@
  *                       size-table rows, payloads into staging slots),
  *                       excluding the compaction kernel that scans the sizes
  *                       and moves the payloads to their stream offsets;
- *   gpulz_decode_timed: around the chunk decode kernel, excluding the header
- *                       check and the size scan.
+ *   gpulz_decode_timed: around the chunk decode kernel, excluding the kernel
+ *                       that checks the header and scans the size table.
  * The caller creates both events (hipEventCreate) and reads them with
  * hipEventElapsedTime after the stream has reached them.  Null events are
  * allowed and are not recorded.

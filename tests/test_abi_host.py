@@ -58,7 +58,7 @@ def test_max_compressed_size(g, cs):
 def test_workspace_sizes(g):
     assert g.encode_workspace_size(1 << 20, 2048) >= 512 * 8
     assert g.encode_workspace_size(1 << 20, 777) == 0
-    assert g.decode_workspace_size(32 + 8 * 1000) >= 1000 * 8
+    assert g.decode_workspace_size(32 + 8 * 1000) >= 1000 * 4  # one u32 tile offset per chunk
     assert g.decode_workspace_size(0) > 0
 
 
