@@ -49,6 +49,58 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// ---- wave primitives on DPP lane moves (no lane-address registers) ------------------
+// Controls of the GFX9 DPP encoding: row_shr:n, row_bcast:15, row_bcast:31,
+// wave_shr:1.  A lane whose source is out of its row, or whose row is masked
+// off, receives 0.
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143, kWaveShr1 = 0x138;
+
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp0(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint64_t dpp0_64(uint64_t v) {
+  return (uint64_t)dpp0<CTRL, ROWS>((uint32_t)v) | ((uint64_t)dpp0<CTRL, ROWS>((uint32_t)(v >> 32)) << 32);
+}
+
+// Inclusive prefix sum over the 64 lanes: four shifts within each 16-lane
+// row, then row 0's total into row 1 (and row 2's into row 3), then lane 31
+// into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_add(uint32_t v) {
+  v += dpp0<kRowShr1>(v);
+  v += dpp0<kRowShr2>(v);
+  v += dpp0<kRowShr4>(v);
+  v += dpp0<kRowShr8>(v);
+  v += dpp0<kRowBcast15, 0xA>(v);
+  v += dpp0<kRowBcast31, 0xC>(v);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_incl_add64(uint64_t v) {
+  v += dpp0_64<kRowShr1>(v);
+  v += dpp0_64<kRowShr2>(v);
+  v += dpp0_64<kRowShr4>(v);
+  v += dpp0_64<kRowShr8>(v);
+  v += dpp0_64<kRowBcast15, 0xA>(v);
+  v += dpp0_64<kRowBcast31, 0xC>(v);
+  return v;
+}
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t wave_incl_max(uint32_t v) {
+  v = umax(v, dpp0<kRowShr1>(v));
+  v = umax(v, dpp0<kRowShr2>(v));
+  v = umax(v, dpp0<kRowShr4>(v));
+  v = umax(v, dpp0<kRowShr8>(v));
+  v = umax(v, dpp0<kRowBcast15, 0xA>(v));
+  v = umax(v, dpp0<kRowBcast31, 0xC>(v));
+  return v;
+}
+__device__ __forceinline__ uint32_t lane63(uint32_t v) { return (uint32_t)__builtin_amdgcn_readlane((int)v, 63); }
+__device__ __forceinline__ uint64_t lane63_64(uint64_t v) {
+  return (uint64_t)lane63((uint32_t)v) | ((uint64_t)lane63((uint32_t)(v >> 32)) << 32);
+}
+
 __device__ __forceinline__ uint2 read_row(const uint8_t* in, uint64_t c) {
   const uint8_t* e = in + kHeaderBytes + kEntryBytes * c;
   return make_uint2(ld_u32_bytes(e), ld_u32_bytes(e + 4));
@@ -148,38 +200,68 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(const uint8_t* __restrict_
 }
 
 // ---- per-chunk decode -------------------------------------------------------------
-// LDS per team: decoded bytes VAL (cs), source index per element SRC (2E),
-// item-start bitmap STB (E/32 words) and its popcount prefix SPRE, flag words
-// FW and their popcount prefix FPRE.
-constexpr uint32_t kWaveArena = 4096 + 2048 + 4 * (32 + 33 + 33 + 34) + 64;  // bytes, E <= 1024 per wave
-constexpr uint32_t kArena = kWaves * kWaveArena;
+// A workgroup's LDS is kWaves slots of kSlot bytes.  A chunk whose working set
+// fits one slot is decoded by one wave (kWaves chunks per workgroup at once);
+// a larger one by the whole workgroup in all slots.  A chunk's arena holds
+//   VAL  the decoded chunk (CS bytes);
+//   PB   the payload: flag bytes, then data bytes from a 4-byte boundary;
+//        after the items are read, SRC, a u16 source index per element;
+//   OB   per element, the offset of the match item starting there (0: none);
+//   STB  the item-start bitmap, one u64 per 64 elements.
+constexpr uint32_t kSlot = 5376;
+static_assert(kSlot % 16 == 0, "arenas must stay 16-byte aligned (64-bit LDS atomics)");
+constexpr uint32_t kArena = kWaves * kSlot;
 
-template <uint32_t TW>
-struct Team {
-  static constexpr uint32_t TL = 64u * TW;
-  __device__ static void sync() {
-    if (TW == 1) wave_sync();
-    else __syncthreads();
-  }
+template <uint32_t CS, uint32_t WS>
+struct Geo {
+  static constexpr uint32_t E = CS / WS;                       // elements per chunk
+  static constexpr uint32_t PBB = (CS > 2u * E ? CS : 2u * E) + 16u;
+  static constexpr uint32_t NEED = CS + PBB + E + E / 8u;
+  static constexpr uint32_t TW = NEED <= kSlot ? 1u : kWaves;  // waves per chunk
+  static constexpr uint32_t TL = 64u * TW;                     // lanes per chunk
+  static constexpr uint32_t J = E / TL;                        // elements per lane
+  static constexpr uint32_t NB = E / 64u;                      // 64-element blocks
+  static constexpr uint32_t RMAX = J + 1u;                     // items per lane, at most
+  static_assert(NEED <= TW * kSlot, "chunk working set exceeds its arena");
+  static_assert(E % TL == 0 && NB <= 64u && RMAX < 25u, "lane mapping");
 };
 
-// Exclusive scan of one value per team lane; total to *tot.  (TW == 1: DPP
-// shuffles in one wave; TW > 1: the workgroup scan.)
+template <uint32_t TW>
+__device__ __forceinline__ void team_sync() {
+  if constexpr (TW == 1) wave_sync();
+  else __syncthreads();
+}
+
+// Exclusive scan of one value per team lane; total to *tot.
 template <uint32_t TW>
 __device__ __forceinline__ uint32_t team_scan(uint32_t v, uint32_t* tot, uint32_t* sh) {
+  const uint32_t inc = wave_incl_add(v);
+  const uint32_t wt = lane63(inc);
   if constexpr (TW == 1) {
-    const uint32_t lane = lane_id();
-    uint32_t inc = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t t = __shfl_up(inc, d, 64);
-      if (lane >= (uint32_t)d) inc += t;
-    }
-    *tot = __shfl(inc, 63, 64);
+    *tot = wt;
     return inc - v;
   } else {
-    return block_exclusive_scan(v, tot, sh);
+    const uint32_t w = threadIdx.x >> 6;
+    if (lane_id() == 0) sh[w] = wt;
+    __syncthreads();
+    uint32_t pre = 0, t = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < TW; ++i) {
+      const uint32_t x = sh[i];
+      pre += i < w ? x : 0u;
+      t += x;
+    }
+    __syncthreads();
+    *tot = t;
+    return pre + inc - v;
   }
+}
+
+template <uint32_t TW>
+__device__ __forceinline__ uint32_t team_sum(uint32_t v, uint32_t* sh) {
+  uint32_t t;
+  team_scan<TW>(v, &t, sh);
+  return t;
 }
 
 template <uint32_t TW>
@@ -188,207 +270,277 @@ __device__ __forceinline__ bool team_any(bool v) {
   else return __syncthreads_or(v);
 }
 
+// d mod o for d < 256, 1 <= o < 256: the quotient of d + 1/2 by o is computed
+// in fp32 with an approximate reciprocal; it lies at least 1/(2o) >= 1/510
+// away from every integer, far beyond the reciprocal's error, so the
+// truncated quotient is exact.
+__device__ __forceinline__ uint32_t small_mod(uint32_t d, uint32_t o) {
+  const uint32_t q = (uint32_t)(((float)d + 0.5f) * __builtin_amdgcn_rcpf((float)o));
+  return d - q * o;
+}
+
 // Decode one coded chunk.  pay: its payload (F flag bytes, D data bytes) in
-// the stream; lim: end of the readable input.  Returns false on a rule
-// violation.  Writes the chunk's real bytes to dst.
-template <uint32_t TW>
-__device__ bool decode_coded(const uint8_t* pay, const uint8_t* lim, uint32_t F, uint32_t D, uint32_t cs,
-                             uint32_t ws, uint32_t bc, uint8_t* dst, uint8_t* arena, uint32_t* sh) {
-  using Tm = Team<TW>;
-  constexpr uint32_t TL = Tm::TL;
-  const uint32_t g = threadIdx.x % TL;
-  const uint32_t E = cs / ws;
-  const uint32_t EW = E / 32u;
-  const uint32_t NI = 8u * F;
-  const uint32_t NW = (F + 3u) / 4u;  // flag words
+// the stream; lim: end of the readable input; bc: the chunk's real bytes.
+// Writes them to dst; returns false on a rule violation.
+template <uint32_t CS, uint32_t WS>
+__device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* lim, uint32_t F, uint32_t D, uint32_t bc,
+                             uint8_t* dst, uint8_t* arena, uint32_t* sh) {
+  using G = Geo<CS, WS>;
+  constexpr uint32_t E = G::E, TW = G::TW, TL = G::TL, J = G::J, NB = G::NB;
+  const uint32_t g = threadIdx.x % TL, lane = lane_id();
   uint8_t* VAL = arena;
-  uint16_t* SRC = (uint16_t*)(arena + cs);
-  uint32_t* STB = (uint32_t*)(arena + cs + 2u * E);
-  uint32_t* SPRE = STB + EW;
-  uint32_t* FW = SPRE + EW + 1u;
-  uint32_t* FPRE = FW + NW + 1u;
-  const uint8_t* dat = pay + F;
+  uint8_t* PB = arena + CS;
+  uint16_t* SRC = (uint16_t*)PB;
+  uint8_t* OB = PB + G::PBB;
+  uint64_t* STB = (uint64_t*)(OB + E);
 
-  for (uint32_t w = g; w < NW; w += TL) {
-    uint32_t v = load4_unaligned(pay + 4u * w, lim);
-    const uint32_t nb = F - 4u * w;  // flag bytes in this word
-    if (nb < 4u) v &= (1u << (8u * nb)) - 1u;
-    FW[w] = v;
-  }
-  for (uint32_t w = g; w < EW; w += TL) STB[w] = 0u;
-  Tm::sync();
-  uint32_t mt_total = 0;
-  for (uint32_t w0 = 0; w0 < NW; w0 += TL) {
-    const uint32_t w = w0 + g;
-    const uint32_t c = w < NW ? (uint32_t)__builtin_popcount(FW[w]) : 0u;
-    uint32_t tot;
-    const uint32_t ex = team_scan<TW>(c, &tot, sh);
-    if (w < NW) FPRE[w] = mt_total + ex;
-    mt_total += tot;
-  }
-  Tm::sync();
-
-  // ---- a. items ----------------------------------------------------------------------
-  uint32_t outpos = 0, K = 0, covered = 0;
-  bool bad = false;
-  for (uint32_t k0 = 0; k0 < NI && outpos < E; k0 += TL) {
-    const uint32_t k = k0 + g;
-    const bool inb = k < NI;
-    uint32_t len = 0, O = 0, tp = 0;
-    bool mt = false, readable = false;
-    if (inb) {
-      const uint32_t w = k >> 5, b = k & 31u, fw = FW[w];
-      mt = (fw >> b) & 1u;
-      const uint32_t m = FPRE[w] + (uint32_t)__builtin_popcount(fw & ((1u << b) - 1u));
-      tp = ws * (k - m) + 2u * m;
-      readable = tp + (mt ? 2u : ws) <= D;
-      if (readable) {
-        if (mt) {
-          len = dat[tp];
-          O = dat[tp + 1u];
-        } else {
-          len = 1u;
-        }
-      }
-    }
-    uint32_t tot;
-    const uint32_t op = outpos + team_scan<TW>(len, &tot, sh);
-    const bool live = inb && op < E;
-    if (live) {
-      if (!readable) bad = true;
-      if (mt && (len == 0u || O == 0u || O > op || op + len > E)) bad = true;
-      if (!bad) {
-        atomicOr(&STB[op >> 5], 1u << (op & 31u));
-        if (!mt) {
-          const uint32_t v = load4_unaligned(dat + tp, lim);
-          if (ws == 4u) *(uint32_t*)(VAL + 4u * op) = v;
-          else if (ws == 2u) *(uint16_t*)(VAL + 2u * op) = (uint16_t)v;
-          else VAL[op] = (uint8_t)v;
-          SRC[op] = (uint16_t)op;
-        }
-      }
-    }
-    uint32_t nlive, llen;
-    team_scan<TW>(live ? 1u : 0u, &nlive, sh);
-    team_scan<TW>(live ? len : 0u, &llen, sh);
-    K += nlive;
-    covered += llen;
-    outpos += tot;
-  }
-  // the live items cover exactly E elements, consume exactly D data bytes,
-  // and no flag bit is set past the last one
+  // every live item covers at least one element: at most E items, so at most
+  // (E + 7) / 8 flag bytes
+  if (F > (E + 7u) / 8u) return false;
+  // ---- load the payload; clear the start bitmap and the offsets -------------------------
+  const uint32_t s0 = (4u - (F & 3u)) & 3u;  // data bytes start on a 4-byte boundary
   {
-    uint32_t mK;
-    if (K >= NI) {
-      mK = mt_total;
-    } else {
-      const uint32_t w = K >> 5, b = K & 31u;
-      mK = FPRE[w] + (uint32_t)__builtin_popcount(FW[w] & ((1u << b) - 1u));
-    }
-    if (covered != E || (K + 7u) / 8u != F || ws * (K - mK) + 2u * mK != D || mK != mt_total) bad = true;
+    const uint32_t nd = (s0 + F + D + 3u) / 4u;
+    for (uint32_t i = g; i < nd; i += TL) ((uint32_t*)PB)[i] = load4_unaligned(pay - s0 + 4u * i, lim);
+#pragma unroll
+    for (uint32_t i = g; i < E / 4u; i += TL) ((uint32_t*)OB)[i] = 0u;
+    if (g < NB) STB[g] = 0ull;
   }
-  if (team_any<TW>(bad)) return false;
-  Tm::sync();
+  const uint8_t* FL = PB + s0;      // flag bytes
+  const uint8_t* PD = PB + s0 + F;  // data bytes, 4-byte aligned
+  team_sync<TW>();
 
-  // ---- b. element sources, pointer jumping ----------------------------------------------
-  uint32_t spre_total = 0;
-  for (uint32_t w0 = 0; w0 < EW; w0 += TL) {
-    const uint32_t w = w0 + g;
-    const uint32_t c = w < EW ? (uint32_t)__builtin_popcount(STB[w]) : 0u;
-    uint32_t tot;
-    const uint32_t ex = team_scan<TW>(c, &tot, sh);
-    if (w < EW) SPRE[w] = spre_total + ex;
-    spre_total += tot;
+  // ---- a. items: lane g reads items [g*R, g*R + nit) one after another --------------------
+  // An item's data offset follows from the matches before it; two team scans
+  // (matches, then output lengths) place every item.
+  const uint32_t NI = 8u * F;
+  const uint32_t R = (NI + TL - 1u) / TL;  // <= RMAX
+  const uint32_t k0 = g * R;
+  const uint32_t nit = k0 < NI ? (NI - k0 < R ? NI - k0 : R) : 0u;
+  uint32_t fb = 0;  // this lane's flag bits, item k0 in bit 0
+  if (nit) {
+    const uint32_t b0 = k0 >> 3;
+#pragma unroll
+    for (uint32_t b = 0; b < 4u; ++b)
+      if (b0 + b < F) fb |= (uint32_t)FL[b0 + b] << (8u * b);
+    fb = (fb >> (k0 & 7u)) & ((1u << nit) - 1u);
   }
-  Tm::sync();
-  bool cover_bad = false;
-  for (uint32_t q = g; q < E; q += TL) {
-    const uint32_t w = q >> 5, b = q & 31u;
-    const uint32_t upto = b == 31u ? ~0u : ((2u << b) - 1u);
-    uint32_t bits = STB[w] & upto, ww = w;
-    const uint32_t cnt = SPRE[w] + (uint32_t)__builtin_popcount(bits);
-    while (bits == 0u && ww > 0u) bits = STB[--ww];  // a match reaches back at most 255 elements
-    if (bits == 0u) {  // element 0 always starts an item; this means no items cover q
-      cover_bad = true;
-      continue;
-    }
-    const uint32_t st = 32u * ww + 31u - (uint32_t)__builtin_clz(bits);
-    const uint32_t k = cnt - 1u;
-    const uint32_t fw = FW[k >> 5], kb = k & 31u;
-    if (!((fw >> kb) & 1u)) continue;  // literal: already in place
-    const uint32_t m = FPRE[k >> 5] + (uint32_t)__builtin_popcount(fw & ((1u << kb) - 1u));
-    const uint32_t tp = ws * (k - m) + 2u * m;
-    const uint32_t O = dat[tp + 1u];
-    SRC[q] = (uint16_t)(st - O + (q - st) % O);
-  }
-  if (spre_total != K || team_any<TW>(cover_bad)) return false;
-  Tm::sync();
-  bool unres = true;
-  for (int round = 0; round < 16 && unres; ++round) {
-    unres = false;
-    for (uint32_t q = g; q < E; q += TL) {
-      const uint32_t s = SRC[q];
-      if (s == q) continue;
-      const uint32_t s2 = SRC[s];
-      if (s2 == s) {
-        if (ws == 4u) *(uint32_t*)(VAL + 4u * q) = *(const uint32_t*)(VAL + 4u * s);
-        else if (ws == 2u) *(uint16_t*)(VAL + 2u * q) = *(const uint16_t*)(VAL + 2u * s);
-        else VAL[q] = VAL[s];
-        SRC[q] = (uint16_t)q;
-      } else {
-        SRC[q] = (uint16_t)s2;
-        unres = true;
+  uint32_t mt_total;
+  const uint32_t m0 = team_scan<TW>((uint32_t)__builtin_popcount(fb), &mt_total, sh);
+  const uint32_t tp0 = WS * (k0 - m0) + 2u * m0;
+  // item r of this lane: flag, data offset, output length (0 if unreadable)
+  auto item_len = [&](uint32_t tp, bool mt) -> uint32_t {
+    if (mt) return tp + 2u <= D ? (uint32_t)PD[tp] : 0u;
+    return tp + WS <= D ? 1u : 0u;
+  };
+  uint32_t sum = 0;
+  {
+    uint32_t tp = tp0;
+#pragma unroll 4
+    for (uint32_t r = 0; r < G::RMAX; ++r) {
+      if (r < nit) {
+        const bool mt = (fb >> r) & 1u;
+        sum += item_len(tp, mt);
+        tp += mt ? 2u : WS;
       }
     }
-    unres = team_any<TW>(unres);
-    Tm::sync();
   }
-  if (unres) return false;  // chains always end within log2(items)+1 rounds
+  uint32_t len_total;
+  uint32_t op = team_scan<TW>(sum, &len_total, sh);
+  uint32_t K = 0, MK = 0, bad = 0, ends = 0;
+  {
+    uint32_t tp = tp0;
+#pragma unroll 4
+    for (uint32_t r = 0; r < G::RMAX; ++r) {
+      if (r < nit) {
+        const bool mt = (fb >> r) & 1u;
+        const uint32_t len = item_len(tp, mt);
+        if (op < E) {  // live: starts before the chunk's end
+          ++K;
+          if (len == 0u) {
+            bad = 1u;  // unreadable, or a zero-length match
+          } else if (mt) {
+            ++MK;
+            const uint32_t O = PD[tp + 1u];
+            if (O == 0u || O > op || op + len > E) bad = 1u;
+            else OB[op] = (uint8_t)O;
+          } else {
+            uint32_t v;
+            if constexpr (WS == 4) {
+              v = (uint32_t)*(const uint16_t*)(PD + tp) | ((uint32_t)*(const uint16_t*)(PD + tp + 2u) << 16);
+              *(uint32_t*)(VAL + 4u * op) = v;
+            } else if constexpr (WS == 2) {
+              *(uint16_t*)(VAL + 2u * op) = *(const uint16_t*)(PD + tp);
+            } else {
+              VAL[op] = PD[tp];
+            }
+          }
+          if (len != 0u) atomicOr((unsigned long long*)&STB[op >> 6], 1ull << (op & 63u));
+          if (op + len == E) ends = 1u;
+        }
+        op += len;
+        tp += mt ? 2u : WS;
+      }
+    }
+  }
+  // the live items must cover exactly E elements, use exactly D data bytes
+  // and leave no match flag set after the last of them
+  {
+    // K, MK <= 4103 items and bad, ends <= 256 lanes: two 16-bit fields each
+    const uint32_t r0 = team_sum<TW>(K | (MK << 16), sh);
+    const uint32_t r1 = team_sum<TW>(bad | (ends << 16), sh);
+    const uint32_t Kt = r0 & 0xFFFFu, MKt = r0 >> 16, badt = r1 & 0xFFFFu, endst = r1 >> 16;
+    if (badt || endst != 1u || (Kt + 7u) / 8u != F || WS * (Kt - MKt) + 2u * MKt != D || MKt != mt_total)
+      return false;
+  }
+  team_sync<TW>();
+
+  // ---- b. element sources: start - O + (q - start) mod O, always < start -----------------
+  // lane l (< NB) holds the last item start in 64-element block l; an exclusive
+  // prefix maximum gives the last start before each block
+  uint32_t before;
+  {
+    uint32_t run = 0;
+    if (lane < NB) {
+      const uint64_t m = STB[lane];
+      run = m ? 64u * lane + 63u - (uint32_t)__builtin_clzll(m) : 0u;
+    }
+    before = dpp0<kWaveShr1>(wave_incl_max(run));
+  }
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(g >> 6);  // wave within the team
+  const uint64_t upto = lane == 63u ? ~0ull : ((2ull << lane) - 1ull);
+  if constexpr (TW == 1) {
+    // One wave: 64-element windows in order, lane i on element 64w + i.  A
+    // source before the window already holds its final value; one inside it
+    // is followed over the window's lanes (pointer jumping on lane indices;
+    // every link goes to a lower lane, so six rounds suffice) to a literal
+    // or to an element before the window.
+#pragma unroll 1
+    for (uint32_t w = 0; w < NB; ++w) {
+      const uint32_t base = 64u * w, q = base + lane;
+      const uint64_t m = STB[w] & upto;
+      const uint32_t st = m ? base + 63u - (uint32_t)__builtin_clzll(m)
+                            : (uint32_t)__builtin_amdgcn_readlane((int)before, (int)w);
+      const uint32_t O = OB[st];
+      const uint32_t e0 = O ? st - O + small_mod(q - st, O) : q;
+      const uint64_t lit = __ballot(O == 0u);
+      uint32_t link = 64u;  // 64: e is final
+      if (O && e0 >= base && !((lit >> (e0 - base)) & 1ull)) link = e0 - base;
+      uint32_t x = e0 | (link << 16);
+      for (uint32_t round = 0; __ballot(link < 64u); ++round) {
+        if (round == 6u) return false;  // unreachable for validated items
+        const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((link & 63u) << 2), (int)x);
+        if (link < 64u) {
+          x = y;
+          link = y >> 16;
+        }
+      }
+      const uint32_t e = x & 0xFFFFu;
+      if (e != q) {
+        if constexpr (WS == 4) *(uint32_t*)(VAL + 4u * q) = *(const uint32_t*)(VAL + 4u * e);
+        else if constexpr (WS == 2) *(uint16_t*)(VAL + 2u * q) = *(const uint16_t*)(VAL + 2u * e);
+        else VAL[q] = VAL[e];
+      }
+    }
+  } else {
+    uint32_t src[J];
+    uint32_t pend = 0;  // bit j: element j still points at a match element
+#pragma unroll
+    for (uint32_t j = 0; j < J; ++j) {
+      const uint32_t blk = wv + TW * j;  // element q's block, uniform in the wave
+      const uint32_t q = 64u * blk + lane;
+      const uint64_t m = STB[blk] & upto;
+      const uint32_t st = m ? 64u * blk + 63u - (uint32_t)__builtin_clzll(m)
+                            : (uint32_t)__builtin_amdgcn_readlane((int)before, (int)blk);
+      const uint32_t O = OB[st];
+      const uint32_t s = O ? st - O + small_mod(q - st, O) : q;
+      src[j] = s;
+      SRC[q] = (uint16_t)s;
+      if (O) pend |= 1u << j;
+    }
+    team_sync<TW>();
+    // pointer jumping: a source that is itself a literal ends the chain
+    for (uint32_t round = 0;; ++round) {
+      if (!team_any<TW>(pend != 0u)) break;
+      if (round == 16u) return false;  // chains resolve within log2(E) + 1 rounds
+#pragma unroll
+      for (uint32_t j = 0; j < J; ++j) {
+        if ((pend >> j) & 1u) {
+          const uint32_t s2 = SRC[src[j]];
+          if (s2 == src[j]) {
+            pend &= ~(1u << j);
+          } else {
+            src[j] = s2;
+            SRC[64u * (wv + TW * j) + lane] = (uint16_t)s2;
+          }
+        }
+      }
+      team_sync<TW>();
+    }
+    // copy every match element from its literal
+#pragma unroll
+    for (uint32_t j = 0; j < J; ++j) {
+      const uint32_t q = 64u * (wv + TW * j) + lane;
+      if (src[j] != q) {
+        if constexpr (WS == 4) *(uint32_t*)(VAL + 4u * q) = *(const uint32_t*)(VAL + 4u * src[j]);
+        else if constexpr (WS == 2) *(uint16_t*)(VAL + 2u * q) = *(const uint16_t*)(VAL + 2u * src[j]);
+        else VAL[q] = VAL[src[j]];
+      }
+    }
+  }
+  team_sync<TW>();
 
   // ---- c. store the real bytes; the padding must have decoded to zeros -----------------
-  const bool al = (((uintptr_t)dst) & 3u) == 0;
+  const uintptr_t da = (uintptr_t)dst;
   bool padbad = false;
-  for (uint32_t i = g; i < cs / 4u; i += TL) {
-    const uint32_t v = *(const uint32_t*)(VAL + 4u * i);
-    const uint32_t b0 = 4u * i;
-    if (b0 + 4u > bc) {
-      const uint32_t keep = b0 >= bc ? 0u : bc - b0;
-      if (keep < 4u && (v & (~0u << (8u * keep)))) padbad = true;
+  for (uint32_t i = g; i < CS / 16u; i += TL) {
+    const uint4 v = *(const uint4*)(VAL + 16u * i);
+    const uint32_t b0 = 16u * i;
+    if (b0 + 16u <= bc && (da & 15u) == 0u) {
+      *(uint4*)(dst + b0) = v;
+      continue;
     }
-    if (b0 >= bc) continue;
-    if (al && b0 + 4u <= bc) {
-      *(uint32_t*)(dst + b0) = v;
-    } else {
-      for (uint32_t b = 0; b < 4u; ++b)
-        if (b0 + b < bc) dst[b0 + b] = (uint8_t)(v >> (8u * b));
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (uint32_t t = 0; t < 4u; ++t) {
+      const uint32_t a = b0 + 4u * t;
+      if (a + 4u <= bc && (da & 3u) == 0u) {
+        *(uint32_t*)(dst + a) = w[t];
+      } else {
+        for (uint32_t bb = 0; bb < 4u; ++bb) {
+          const uint8_t x = (uint8_t)(w[t] >> (8u * bb));
+          if (a + bb < bc) dst[a + bb] = x;
+          else if (x) padbad = true;
+        }
+      }
     }
   }
   return !team_any<TW>(padbad);
 }
 
-template <uint32_t TW>
-__device__ void decode_group(const DecP& p, const uint8_t* in, const uint8_t* lim, uint8_t* out,
+template <uint32_t CS, uint32_t WS>
+__device__ __forceinline__ void decode_group(const DecP& p, const uint8_t* in, const uint8_t* lim, uint8_t* out,
                              const uint32_t* loc, const uint64_t* tile_sum, uint32_t* status, uint64_t* out_bytes,
                              uint8_t* arena_all, uint32_t* sh) {
-  constexpr uint32_t TL = 64u * TW;
-  constexpr uint32_t CPW = kWaves / TW;  // chunks per workgroup
+  using G = Geo<CS, WS>;
+  constexpr uint32_t TL = G::TL;
+  constexpr uint32_t CPW = kWaves / G::TW;  // chunks per workgroup
   const uint32_t team = threadIdx.x / TL, g = threadIdx.x % TL;
-  uint8_t* arena = arena_all + team * (kArena / CPW);
+  uint8_t* arena = arena_all + team * (G::TW * kSlot);
   const uint32_t ngroups = (p.nc + CPW - 1u) / CPW;
   for (uint32_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
     const uint64_t c = (uint64_t)grp * CPW + team;
-    if (c >= p.nc) continue;  // CPW > 1 only when TW == 1: no workgroup barrier below
+    if (c >= p.nc) continue;  // CPW > 1 only for one-wave teams: no workgroup barrier below
     const uint2 e = read_row(in, c);
-    const uint64_t start = c * p.cs;
-    const uint32_t bc = (uint32_t)((p.n - start) < p.cs ? (p.n - start) : p.cs);
+    const uint64_t start = c * CS;
+    const uint32_t bc = (uint32_t)((p.n - start) < CS ? (p.n - start) : CS);
     if (!row_ok(e, bc)) continue;  // reported by the scan kernel
     const uint32_t size = entry_payload(e.x, e.y);
     // payload offset = earlier tiles' totals + offset within the tile
     const uint32_t t = (uint32_t)(c / p.T);
     uint64_t tp = 0;
     for (uint32_t i = lane_id(); i < t; i += 64u) tp += tile_sum[i];
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) tp += __shfl_xor(tp, d, 64);
+    tp = lane63_64(wave_incl_add64(tp));
     const uint64_t off = tp + loc[c];
     if (off + size > p.pb) continue;  // sizes inconsistent with the header: reported by wave 0 below
     const uint8_t* pay = in + p.base + off;
@@ -409,17 +561,24 @@ __device__ void decode_group(const DecP& p, const uint8_t* in, const uint8_t* li
           for (uint32_t b = 0; b < 4u; ++b)
             if (4u * i + b < bc) dst[4u * i + b] = (uint8_t)(v >> (8u * b));
       }
-    } else if (e.x > (p.cs / p.ws + 7u) / 8u) {  // more flag bytes than a chunk has items
-      if (g == 0) raise_status(status, out_bytes, kStatusCorrupt);
     } else {
-      if (!decode_coded<TW>(pay, lim, e.x, e.y, p.cs, p.ws, bc, dst, arena, sh) && g == 0)
+      if (!decode_coded<CS, WS>(pay, lim, e.x, e.y, bc, dst, arena, sh) && g == 0)
         raise_status(status, out_bytes, kStatusCorrupt);
     }
-    Team<TW>::sync();
+    team_sync<G::TW>();
   }
 }
 
-__global__ __launch_bounds__(kBlock) void chunks_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes,
+template <uint32_t CS>
+__device__ __forceinline__ void decode_by_ws(const DecP& p, const uint8_t* in, const uint8_t* lim, uint8_t* out,
+                             const uint32_t* loc, const uint64_t* tile_sum, uint32_t* status, uint64_t* out_bytes,
+                             uint8_t* arena, uint32_t* sh) {
+  if (p.ws == 4u) decode_group<CS, 4>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh);
+  else if (p.ws == 2u) decode_group<CS, 2>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh);
+  else decode_group<CS, 1>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh);
+}
+
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(7))) void chunks_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes,
                                                         uint8_t* __restrict__ out, const DecP* __restrict__ P,
                                                         const uint32_t* __restrict__ loc,
                                                         const uint64_t* __restrict__ tile_sum,
@@ -439,17 +598,15 @@ __global__ __launch_bounds__(kBlock) void chunks_kernel(const uint8_t* __restric
       s += tile_sum[i];
       err |= tile_err[i];
     }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      s += __shfl_xor(s, d, 64);
-      err |= __shfl_xor(err, d, 64);
-    }
+    s = lane63_64(wave_incl_add64(s));
+    err = lane63(wave_incl_add(err));
     if (lane_id() == 0 && (s != p.pb || err)) raise_status(status, out_bytes, kStatusCorrupt);
   }
   const uint8_t* lim = in + in_bytes;
-  const uint32_t E = p.cs / p.ws;
-  if (E <= 1024u) decode_group<1>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh);
-  else decode_group<4>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh);
+  // the header kernel accepted cs and ws, so they are among these
+  if (p.cs == 1024u) decode_by_ws<1024>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh);
+  else if (p.cs == 2048u) decode_by_ws<2048>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh);
+  else decode_by_ws<4096>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh);
 }
 
 }  // namespace
