@@ -139,6 +139,30 @@ __device__ __forceinline__ void put_le(uint8_t* p, uint64_t v, int nb) {
   for (int i = 0; i < nb; ++i) p[i] = (uint8_t)(v >> (8 * i));
 }
 
+// acc = acc * 2^16 + (16 match bits, a[0] first): bit = (a[i] == v).  Each
+// compare writes a lane mask to an SGPR pair and an add-with-carry shifts it
+// into acc, two instructions per compare.  A VALU write of an SGPR must be at
+// least two instructions ahead of a VALU read of it as carry, so three pairs
+// rotate: every add reads the pair written three compares earlier.
+__device__ __forceinline__ void match_bits16(uint32_t& acc, const uint32_t* a, uint32_t v) {
+  uint64_t m0, m1, m2;
+#define GLZ_C(k, m) "v_cmp_eq_u32_e64 %[" #m "], %[a" #k "], %[v]\n"
+#define GLZ_A(m) "v_addc_co_u32_e64 %[acc], %[" #m "], %[acc], %[acc], %[" #m "]\n"
+  asm volatile(GLZ_C(0, m0) GLZ_C(1, m1) GLZ_C(2, m2)
+               GLZ_A(m0) GLZ_C(3, m0) GLZ_A(m1) GLZ_C(4, m1) GLZ_A(m2) GLZ_C(5, m2)
+               GLZ_A(m0) GLZ_C(6, m0) GLZ_A(m1) GLZ_C(7, m1) GLZ_A(m2) GLZ_C(8, m2)
+               GLZ_A(m0) GLZ_C(9, m0) GLZ_A(m1) GLZ_C(10, m1) GLZ_A(m2) GLZ_C(11, m2)
+               GLZ_A(m0) GLZ_C(12, m0) GLZ_A(m1) GLZ_C(13, m1) GLZ_A(m2) GLZ_C(14, m2)
+               GLZ_A(m0) GLZ_C(15, m0) GLZ_A(m1) GLZ_A(m2) GLZ_A(m0)
+               : [acc] "+v"(acc), [m0] "=&s"(m0), [m1] "=&s"(m1), [m2] "=&s"(m2)
+               : [v] "v"(v), [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]), [a4] "v"(a[4]),
+                 [a5] "v"(a[5]), [a6] "v"(a[6]), [a7] "v"(a[7]), [a8] "v"(a[8]), [a9] "v"(a[9]),
+                 [a10] "v"(a[10]), [a11] "v"(a[11]), [a12] "v"(a[12]), [a13] "v"(a[13]), [a14] "v"(a[14]),
+                 [a15] "v"(a[15]));
+#undef GLZ_C
+#undef GLZ_A
+}
+
 struct EncCtl {
   uint32_t error;  // set if a look-back ever gave up waiting
   uint32_t pad[63];
@@ -276,10 +300,10 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
         uint32_t om[PPASS];
 #pragma unroll
         for (uint32_t q = 0; q < PPASS; ++q) {
-          const uint32_t v = w[32 + q];
+          // offsets 32..17, then 16..1: bit o-1 compares w[32+q] with w[32+q-o]
           uint32_t m = 0;
-#pragma unroll
-          for (uint32_t o = 32; o >= 1; --o) m = m + m + (uint32_t)(w[32 + q - o] == v);
+          match_bits16(m, &w[q], w[32 + q]);
+          match_bits16(m, &w[q + 16], w[32 + q]);
           const uint32_t p = p0 + q;
           om[q] = p >= 32u ? m : (m & ((1u << p) - 1u));
         }
