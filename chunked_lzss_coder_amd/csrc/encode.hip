@@ -377,10 +377,28 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
           if (v == 0) continue;
           const uint32_t o = p - (v - 1u);  // entries come from earlier sub-blocks: o >= 1
           if (o > kMaxFar) continue;
+          // the candidate replaces the near match only if its run is strictly
+          // longer, so it must match at p + Lnear, and Lnear must leave room
+          const uint32_t lim = (uint32_t)E - p < kMaxLen ? (uint32_t)E - p : kMaxLen;
           const uint32_t Lnear = LO[p] & 0xFFu;
-          if (Lnear >= kMaxLen) continue;
+          if (Lnear >= lim || X[p + Lnear] != X[p + Lnear - o]) continue;
+          // run at offset o, capped at lim, eight compares per step (reads past
+          // the chunk's words stay inside the team's LDS and are masked)
           uint32_t r = 0;
-          while (r < kMaxLen && p + r < (uint32_t)E && X[p + r] == X[p + r - o]) ++r;
+          while (true) {
+            uint32_t stop = 0;
+#pragma unroll
+            for (uint32_t j = 0; j < 8u; ++j) {
+              const uint32_t idx = r + j;
+              const uint32_t a = X[p + idx], b = X[p + idx - o];
+              stop |= (uint32_t)(idx >= lim || a != b) << j;
+            }
+            if (stop) {
+              r += (uint32_t)__builtin_ctz(stop);
+              break;
+            }
+            r += 8u;
+          }
           if (r > Lnear) LO[p] = r | (o << 8);
         }
         team_sync<WPC>();
