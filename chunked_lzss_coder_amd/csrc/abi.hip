@@ -13,6 +13,9 @@ namespace {
 constexpr uint64_t kAlign = 256;
 constexpr uint64_t kStagingSlack = 256;  // realigning copies read a few bytes past a slot
 inline uint64_t round_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+// The workspace may start at any address: every layout reserves kAlign more
+// bytes and is carved from the first kAlign-aligned address inside it.
+inline uint8_t* align_up(void* p) { return (uint8_t*)(((uintptr_t)p + kAlign - 1) & ~(uintptr_t)(kAlign - 1)); }
 inline uint64_t num_chunks_of(uint64_t n, uint32_t cs) { return n / cs + ((n % cs) != 0); }
 
 struct EncLayoutHost {
@@ -25,7 +28,7 @@ EncLayoutHost enc_layout(uint64_t chunks, uint32_t cs) {
   L.ctl = 0;
   L.tiles = round_up(encode_ctl_bytes());
   L.staging = L.tiles + round_up((encode_tiles((uint32_t)chunks) + 1u) * 8u);
-  L.total = L.staging + round_up(chunks * cs + kStagingSlack);
+  L.total = L.staging + round_up(chunks * cs + kStagingSlack) + kAlign;
   return L;
 }
 
@@ -39,8 +42,13 @@ DecLayoutHost dec_layout(uint64_t chunks_cap) {
   L.params = 0;
   L.loc = round_up(decode_params_bytes());
   L.tile_sums = L.loc + round_up((chunks_cap ? chunks_cap : 1) * 4u);
-  L.tile_err = L.tile_sums + round_up(256u * 8u);
-  L.total = L.tile_err + round_up(256u * 4u);
+  // the launch uses at most this many tiles for any chunk bound up to
+  // chunks_cap: 256 while tiles grow, then one per 2^20 chunks
+  const uint32_t cap32 = chunks_cap > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)chunks_cap;
+  const uint32_t nt = decode_num_tiles(cap32);
+  const uint64_t tiles = nt > 256u ? nt : 256u;
+  L.tile_err = L.tile_sums + round_up(tiles * 8u);
+  L.total = L.tile_err + round_up(tiles * 4u) + kAlign;
   return L;
 }
 
@@ -75,7 +83,7 @@ int gpulz_encode_timed(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, 
   if (chunks > 0xFFFFFFFFull - 1024u) return GPULZ_ERR_INVALID_ARG;
   const EncLayoutHost L = enc_layout(chunks, chunk_size);
   if (workspace_bytes < L.total) return GPULZ_ERR_CAPACITY;
-  uint8_t* ws = (uint8_t*)d_workspace;
+  uint8_t* ws = align_up(d_workspace);
 
   EncodeArgs ea;
   ea.in = (const uint8_t*)d_in;
@@ -116,7 +124,7 @@ int gpulz_decode_timed(const void* d_in, uint64_t in_bytes, void* d_out, uint64_
   if (cap > 0xFFFFFFFFull) cap = 0xFFFFFFFFull;
   const DecLayoutHost L = dec_layout(dec_chunks_bound(in_bytes));
   if (workspace_bytes < L.total) return GPULZ_ERR_CAPACITY;
-  uint8_t* ws = (uint8_t*)d_workspace;
+  uint8_t* ws = align_up(d_workspace);
   DecodeArgs da;
   da.in = (const uint8_t*)d_in;
   da.in_bytes = in_bytes;

@@ -85,6 +85,58 @@ __device__ __forceinline__ T block_sum(T v, T* sh) {
   return tot;
 }
 
+// ---- wave primitives on DPP lane moves (no lane-address registers) ------------------
+// Controls of the GFX9 DPP encoding: row_shr:n, row_bcast:15, row_bcast:31,
+// wave_shl:1 (lane i takes lane i+1), wave_shr:1 (lane i takes lane i-1).  A lane whose source is out of its row, or whose row is masked
+// off, receives 0.
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143, kWaveShl1 = 0x130, kWaveShr1 = 0x138;
+
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp0(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint64_t dpp0_64(uint64_t v) {
+  return (uint64_t)dpp0<CTRL, ROWS>((uint32_t)v) | ((uint64_t)dpp0<CTRL, ROWS>((uint32_t)(v >> 32)) << 32);
+}
+
+// Inclusive prefix sum over the 64 lanes: four shifts within each 16-lane
+// row, then row 0's total into row 1 (and row 2's into row 3), then lane 31
+// into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_incl_add(uint32_t v) {
+  v += dpp0<kRowShr1>(v);
+  v += dpp0<kRowShr2>(v);
+  v += dpp0<kRowShr4>(v);
+  v += dpp0<kRowShr8>(v);
+  v += dpp0<kRowBcast15, 0xA>(v);
+  v += dpp0<kRowBcast31, 0xC>(v);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_incl_add64(uint64_t v) {
+  v += dpp0_64<kRowShr1>(v);
+  v += dpp0_64<kRowShr2>(v);
+  v += dpp0_64<kRowShr4>(v);
+  v += dpp0_64<kRowShr8>(v);
+  v += dpp0_64<kRowBcast15, 0xA>(v);
+  v += dpp0_64<kRowBcast31, 0xC>(v);
+  return v;
+}
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t wave_incl_max(uint32_t v) {
+  v = umax(v, dpp0<kRowShr1>(v));
+  v = umax(v, dpp0<kRowShr2>(v));
+  v = umax(v, dpp0<kRowShr4>(v));
+  v = umax(v, dpp0<kRowShr8>(v));
+  v = umax(v, dpp0<kRowBcast15, 0xA>(v));
+  v = umax(v, dpp0<kRowBcast31, 0xC>(v));
+  return v;
+}
+__device__ __forceinline__ uint32_t lane63(uint32_t v) { return (uint32_t)__builtin_amdgcn_readlane((int)v, 63); }
+__device__ __forceinline__ uint64_t lane63_64(uint64_t v) {
+  return (uint64_t)lane63((uint32_t)v) | ((uint64_t)lane63((uint32_t)(v >> 32)) << 32);
+}
+
 // 4 bytes starting at p (any alignment) from a buffer whose readable bytes
 // end at lim; p-3 must still be readable.  Bytes at or past lim read as 0.
 __device__ __forceinline__ uint32_t load4_unaligned(const uint8_t* p, const uint8_t* lim) {
@@ -128,13 +180,14 @@ struct DecodeArgs {
   uint32_t* status;
   void* params;         // device-resident stream parameters
   uint32_t* loc;        // chunks_cap payload offsets within their scan tile
-  uint64_t* tile_sums;  // <= 256 scan tiles
-  uint32_t* tile_err;   // <= 256 scan tiles
+  uint64_t* tile_sums;  // one per scan tile (decode_num_tiles)
+  uint32_t* tile_err;   // one per scan tile
   uint32_t chunks_cap;  // host bound on num_chunks
   hipEvent_t ev_start;  // optional, recorded around the chunk decode kernel
   hipEvent_t ev_stop;
 };
 uint32_t decode_tile_chunks(uint32_t chunks_cap);
+uint32_t decode_num_tiles(uint32_t chunks_cap);
 uint64_t decode_params_bytes();
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

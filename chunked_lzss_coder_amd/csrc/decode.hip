@@ -30,10 +30,12 @@
 namespace gpulz {
 namespace {
 
-constexpr uint32_t kTileMin = 4096;   // chunks per scan tile (at least)
-constexpr uint32_t kMaxTiles = 256;
-constexpr uint32_t kScanPer = 16;     // chunks per thread per scan round
+constexpr uint32_t kTileMin = 1024;     // chunks per scan tile: at least,
+constexpr uint32_t kTileMax = 1u << 20;  // at most (offsets within a tile < 2^32)
+constexpr uint32_t kMaxTiles = 256;      // tiles wanted for large streams
+constexpr uint32_t kScanPer = 4;         // chunks per thread per scan round
 constexpr uint32_t kScanRound = kScanPer * kBlock;
+static_assert(kTileMin % kScanRound == 0 && (uint64_t)kTileMax * 4096u <= (1ull << 32), "tile sizes");
 
 __device__ __forceinline__ uint32_t ld_u32_bytes(const uint8_t* p) {
   return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
@@ -49,60 +51,9 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// ---- wave primitives on DPP lane moves (no lane-address registers) ------------------
-// Controls of the GFX9 DPP encoding: row_shr:n, row_bcast:15, row_bcast:31,
-// wave_shr:1.  A lane whose source is out of its row, or whose row is masked
-// off, receives 0.
-constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
-constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143, kWaveShr1 = 0x138;
-
-template <int CTRL, int ROWS = 0xF>
-__device__ __forceinline__ uint32_t dpp0(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
-}
-template <int CTRL, int ROWS = 0xF>
-__device__ __forceinline__ uint64_t dpp0_64(uint64_t v) {
-  return (uint64_t)dpp0<CTRL, ROWS>((uint32_t)v) | ((uint64_t)dpp0<CTRL, ROWS>((uint32_t)(v >> 32)) << 32);
-}
-
-// Inclusive prefix sum over the 64 lanes: four shifts within each 16-lane
-// row, then row 0's total into row 1 (and row 2's into row 3), then lane 31
-// into rows 2 and 3.
-__device__ __forceinline__ uint32_t wave_incl_add(uint32_t v) {
-  v += dpp0<kRowShr1>(v);
-  v += dpp0<kRowShr2>(v);
-  v += dpp0<kRowShr4>(v);
-  v += dpp0<kRowShr8>(v);
-  v += dpp0<kRowBcast15, 0xA>(v);
-  v += dpp0<kRowBcast31, 0xC>(v);
-  return v;
-}
-__device__ __forceinline__ uint64_t wave_incl_add64(uint64_t v) {
-  v += dpp0_64<kRowShr1>(v);
-  v += dpp0_64<kRowShr2>(v);
-  v += dpp0_64<kRowShr4>(v);
-  v += dpp0_64<kRowShr8>(v);
-  v += dpp0_64<kRowBcast15, 0xA>(v);
-  v += dpp0_64<kRowBcast31, 0xC>(v);
-  return v;
-}
-__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
-__device__ __forceinline__ uint32_t wave_incl_max(uint32_t v) {
-  v = umax(v, dpp0<kRowShr1>(v));
-  v = umax(v, dpp0<kRowShr2>(v));
-  v = umax(v, dpp0<kRowShr4>(v));
-  v = umax(v, dpp0<kRowShr8>(v));
-  v = umax(v, dpp0<kRowBcast15, 0xA>(v));
-  v = umax(v, dpp0<kRowBcast31, 0xC>(v));
-  return v;
-}
-__device__ __forceinline__ uint32_t lane63(uint32_t v) { return (uint32_t)__builtin_amdgcn_readlane((int)v, 63); }
-__device__ __forceinline__ uint64_t lane63_64(uint64_t v) {
-  return (uint64_t)lane63((uint32_t)v) | ((uint64_t)lane63((uint32_t)(v >> 32)) << 32);
-}
-
 __device__ __forceinline__ uint2 read_row(const uint8_t* in, uint64_t c) {
   const uint8_t* e = in + kHeaderBytes + kEntryBytes * c;
+  if ((((uintptr_t)in) & 7u) == 0) return *(const uint2*)e;  // rows are 8-byte aligned with the stream
   return make_uint2(ld_u32_bytes(e), ld_u32_bytes(e + 4));
 }
 
@@ -612,15 +563,21 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(7))) voi
 }  // namespace
 
 uint32_t decode_tile_chunks(uint32_t chunks_cap) {
-  uint32_t T = (chunks_cap + kMaxTiles - 1u) / kMaxTiles;
+  uint64_t T = ((uint64_t)chunks_cap + kMaxTiles - 1u) / kMaxTiles;
   T = (T + kTileMin - 1u) / kTileMin * kTileMin;
-  return T < kTileMin ? kTileMin : T;
+  if (T < kTileMin) T = kTileMin;
+  if (T > kTileMax) T = kTileMax;
+  return (uint32_t)T;
+}
+uint32_t decode_num_tiles(uint32_t chunks_cap) {
+  const uint32_t T = decode_tile_chunks(chunks_cap);
+  return chunks_cap ? (uint32_t)(((uint64_t)chunks_cap + T - 1u) / T) : 1u;
 }
 uint64_t decode_params_bytes() { return sizeof(DecP); }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const uint32_t T = decode_tile_chunks(a.chunks_cap);
-  const uint32_t tiles = a.chunks_cap ? (a.chunks_cap + T - 1u) / T : 1u;
+  const uint32_t tiles = decode_num_tiles(a.chunks_cap);
   hipLaunchKernelGGL(scan_kernel, dim3(tiles), dim3(kBlock), 0, stream, a.in, a.in_bytes, a.out_capacity,
                      a.chunks_cap, T, (DecP*)a.params, a.loc, a.tile_sums, a.tile_err, a.status, a.out_bytes);
   if (a.ev_start && hipEventRecord(a.ev_start, stream) != hipSuccess) return hipErrorUnknown;

@@ -659,6 +659,16 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(const uint8_t* __restri
   }
   const uint32_t t = blockIdx.x;
   const uint64_t c0 = (uint64_t)t * kCTile;
+  // Each wave moves PW chunks.  The first 256 bytes of each of its staging
+  // slots (one dword per lane) are loaded before the sizes and offsets are
+  // known, so the loads overlap the row reads and the look-back.
+  constexpr uint32_t PW = kCTile / kWaves;
+  uint32_t pv[PW];
+#pragma unroll
+  for (uint32_t u = 0; u < PW; ++u) {
+    const uint64_t c = c0 + wave * PW + u;
+    pv[u] = c < num_chunks ? ((const uint32_t*)(staging + c * cs))[lane] : 0u;
+  }
   if (wave == 0) {
     // sizes of the tile's chunks (one per lane), their scan, and the look-back
     static_assert(kCTile == 64, "one chunk per lane of the first wave");
@@ -711,48 +721,36 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(const uint8_t* __restri
   }
   __syncthreads();
   const uint64_t pre = tile_pre;
-  // Each wave moves kCTile / kWaves chunks, kU at a time: the loads of kU
-  // chunks are issued before any of their stores, so their latencies overlap.
-  constexpr uint32_t PW = kCTile / kWaves, kU = 8;
-  for (uint32_t j0 = wave * PW; j0 < (wave + 1) * PW; j0 += kU) {
-    uint32_t lo[kU], hi[kU], head[kU], nbody[kU], size[kU];
-    uint8_t* dst[kU];
-    const uint8_t* sb[kU];
 #pragma unroll
-    for (uint32_t u = 0; u < kU; ++u) {
-      const uint32_t j = j0 + u;
-      const uint64_t c = c0 + j;
-      size[u] = c < num_chunks ? sz[j] : 0u;
-      sb[u] = staging + c * cs;
-      dst[u] = payload + pre + off[j];
-      uint32_t h = (uint32_t)((4u - ((uintptr_t)dst[u] & 3u)) & 3u);
-      head[u] = h > size[u] ? size[u] : h;
-      nbody[u] = (size[u] - head[u]) / 4u;
-      lo[u] = hi[u] = 0;
-      if (lane < nbody[u]) {
-        const uint32_t* sw = (const uint32_t*)sb[u];
-        const uint32_t s = head[u] + 4u * lane;
-        lo[u] = sw[s >> 2];
-        if (head[u]) hi[u] = sw[(s >> 2) + 1u];
-      }
+  for (uint32_t u = 0; u < PW; ++u) {
+    const uint32_t j = wave * PW + u;
+    const uint64_t c = c0 + j;
+    const uint32_t size = c < num_chunks ? sz[j] : 0u;
+    if (size == 0u) continue;
+    uint8_t* dst = payload + pre + off[j];
+    const uint8_t* sb = staging + c * cs;
+    const uint32_t* sw = (const uint32_t*)sb;
+    // head bytes up to dst's next 4-byte boundary, then aligned dwords, then
+    // the tail; payload byte b is byte b & 3 of slot dword b >> 2
+    const uint32_t a4 = (uint32_t)((4u - ((uintptr_t)dst & 3u)) & 3u);
+    const uint32_t h = a4 > size ? size : a4;
+    const uint32_t nb = (size - h) / 4u;
+    const uint32_t d0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)pv[u]);
+    if (lane < h) dst[lane] = (uint8_t)(d0 >> (8u * lane));
+    uint32_t* dw = (uint32_t*)(dst + h);
+    // body dword k takes slot dwords k and k + 1 (the next lane's)
+    const uint32_t nxt = dpp0<kWaveShl1>(pv[u]);
+    if (lane < (nb < 63u ? nb : 63u)) dw[lane] = __builtin_amdgcn_alignbyte(nxt, pv[u], h);
+    for (uint32_t k = 63u + lane; k < nb; k += 64u) {  // payloads longer than 252 bytes
+      const uint32_t s0 = h + 4u * k;
+      const uint32_t lo = sw[s0 >> 2];
+      const uint32_t hi = h ? sw[(s0 >> 2) + 1u] : 0u;
+      dw[k] = __builtin_amdgcn_alignbyte(hi, lo, h);
     }
-#pragma unroll
-    for (uint32_t u = 0; u < kU; ++u) {
-      if (size[u] == 0) continue;
-      const uint32_t h = head[u], nb = nbody[u];
-      if (lane < h) dst[u][lane] = sb[u][lane];
-      uint32_t* dw = (uint32_t*)(dst[u] + h);
-      if (lane < nb) dw[lane] = __builtin_amdgcn_alignbyte(hi[u], lo[u], h);
-      const uint32_t* sw = (const uint32_t*)sb[u];
-      for (uint32_t q = lane + 64u; q < nb; q += 64u) {  // payloads longer than 256 bytes
-        const uint32_t s = h + 4u * q;
-        const uint32_t l2 = sw[s >> 2];
-        const uint32_t h2 = h ? sw[(s >> 2) + 1u] : 0u;
-        dw[q] = __builtin_amdgcn_alignbyte(h2, l2, h);
-      }
-      const uint32_t t0 = h + 4u * nb;
-      if (t0 + lane < size[u]) dst[u][t0 + lane] = sb[u][t0 + lane];
-    }
+    const uint32_t t0 = h + 4u * nb;  // at most 3 tail bytes
+    const uint32_t tb = t0 + lane;
+    const uint32_t tv = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((tb >> 2) & 63u) << 2, (int)pv[u]);
+    if (tb < size) dst[tb] = tb < 256u ? (uint8_t)(tv >> (8u * (tb & 3u))) : sb[tb];
   }
 }
 

@@ -93,7 +93,7 @@ GPULZ_API uint64_t gpulz_decode_workspace_size(uint64_t in_bytes);
  *   d_out_bytes: device u64 that receives the stream length once the stream
  *     reaches the end of this call's work.
  *   d_workspace / workspace_bytes: at least gpulz_encode_workspace_size();
- *     its contents on entry do not matter and are clobbered.
+ *     any alignment; its contents on entry do not matter and are clobbered.
  * Output bytes do not depend on workspace contents, stream, or run. */
 GPULZ_API int gpulz_encode(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, uint32_t word_size,
                  uint32_t match_level, void* d_out, uint64_t out_capacity, uint64_t* d_out_bytes,
@@ -108,7 +108,8 @@ GPULZ_API int gpulz_encode(const void* d_in, uint64_t n_bytes, uint32_t chunk_si
  *   d_status: device u32, receives GPULZ_STATUS_OK / _CAPACITY / _CORRUPT.
  *     On _CORRUPT the output is undefined, but no access ever falls outside
  *     [d_in, d_in+in_bytes) or [d_out, d_out+out_capacity).
- *   d_workspace: at least gpulz_decode_workspace_size(in_bytes) bytes.
+ *   d_workspace: at least gpulz_decode_workspace_size(in_bytes) bytes, any
+ *     alignment.
  * The stream header is read on the device; nothing waits on the host. */
 GPULZ_API int gpulz_decode(const void* d_in, uint64_t in_bytes, void* d_out, uint64_t out_capacity,
                  uint64_t* d_out_bytes, uint32_t* d_status, void* d_workspace,

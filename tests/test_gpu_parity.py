@@ -185,7 +185,8 @@ def test_unaligned_buffers(g, oracle_mod):
             cap = g.max_compressed_size(data.size, 2048)
             obuf = torch.zeros(cap + 16, dtype=torch.uint8, device="cuda:0")
             nb = torch.zeros(1, dtype=torch.uint64, device="cuda:0")
-            wsb = torch.empty(g.encode_workspace_size(data.size, 2048), dtype=torch.uint8, device="cuda:0")
+            wsz = g.encode_workspace_size(data.size, 2048)
+            wsb = torch.empty(wsz + 8, dtype=torch.uint8, device="cuda:0")[shift_in:shift_in + wsz]  # unaligned too
             g.encode_into(xin[shift_in:shift_in + data.size], 2048, 4, 1, obuf[shift_out:shift_out + cap], nb, wsb)
             torch.cuda.synchronize()
             n = int(nb.item())
@@ -196,7 +197,8 @@ def test_unaligned_buffers(g, oracle_mod):
             dbuf = torch.zeros(data.size + 16, dtype=torch.uint8, device="cuda:0")
             db = torch.zeros(1, dtype=torch.uint64, device="cuda:0")
             st = torch.zeros(1, dtype=torch.int32, device="cuda:0")
-            dws = torch.empty(g.decode_workspace_size(n), dtype=torch.uint8, device="cuda:0")
+            dsz = g.decode_workspace_size(n)
+            dws = torch.empty(dsz + 8, dtype=torch.uint8, device="cuda:0")[shift_out + 1:shift_out + 1 + dsz]
             g.decode_into(sbuf[shift_in:shift_in + n], n, dbuf[shift_out:shift_out + data.size], db, st, dws)
             torch.cuda.synchronize()
             assert int(st.item()) == 0
