@@ -138,19 +138,17 @@ __device__ __forceinline__ uint64_t lane63_64(uint64_t v) {
 }
 
 // 4 bytes starting at p (any alignment) from a buffer whose readable bytes
-// end at lim; p-3 must still be readable.  Bytes at or past lim read as 0.
+// end at lim; bytes at or past lim read as 0.  Only aligned dwords holding at
+// least one readable byte are loaded: such a dword lies in a page the buffer
+// occupies, so nothing outside it can fault.
 __device__ __forceinline__ uint32_t load4_unaligned(const uint8_t* p, const uint8_t* lim) {
-  const uintptr_t a = (uintptr_t)p, a0 = a & ~(uintptr_t)3;
+  const uintptr_t a = (uintptr_t)p, a0 = a & ~(uintptr_t)3, e = (uintptr_t)lim;
   const uint32_t sh = (uint32_t)(a & 3u);
-  if (a0 + 8u <= (uintptr_t)lim) {
-    const uint32_t* w = (const uint32_t*)a0;
-    uint32_t lo = w[0];
-    uint32_t hi = sh ? w[1] : 0u;
-    return __builtin_amdgcn_alignbyte(hi, lo, sh);
-  }
-  uint32_t v = 0;
-  for (uint32_t b = 0; b < 4u; ++b)
-    if (p + b < lim) v |= (uint32_t)p[b] << (8u * b);
+  const uint32_t* w = (const uint32_t*)a0;
+  const uint32_t lo = a0 < e ? w[0] : 0u;
+  const uint32_t hi = (sh != 0u && a0 + 4u < e) ? w[1] : 0u;
+  uint32_t v = __builtin_amdgcn_alignbyte(hi, lo, sh);
+  if (a + 4u > e) v = a >= e ? 0u : (v & ((1u << (8u * (uint32_t)(e - a))) - 1u));
   return v;
 }
 

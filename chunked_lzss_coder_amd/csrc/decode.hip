@@ -35,6 +35,7 @@ constexpr uint32_t kTileMax = 1u << 20;  // at most (offsets within a tile < 2^3
 constexpr uint32_t kMaxTiles = 256;      // tiles wanted for large streams
 constexpr uint32_t kScanPer = 4;         // chunks per thread per scan round
 constexpr uint32_t kScanRound = kScanPer * kBlock;
+constexpr uint32_t kDecodeGrid = 8192;   // chunk-kernel workgroups at most
 static_assert(kTileMin % kScanRound == 0 && (uint64_t)kTileMax * 4096u <= (1ull << 32), "tile sizes");
 
 __device__ __forceinline__ uint32_t ld_u32_bytes(const uint8_t* p) {
@@ -251,8 +252,22 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
   // ---- load the payload; clear the start bitmap and the offsets -------------------------
   const uint32_t s0 = (4u - (F & 3u)) & 3u;  // data bytes start on a 4-byte boundary
   {
+    // four loads per lane in flight before their LDS stores
     const uint32_t nd = (s0 + F + D + 3u) / 4u;
-    for (uint32_t i = g; i < nd; i += TL) ((uint32_t*)PB)[i] = load4_unaligned(pay - s0 + 4u * i, lim);
+#pragma unroll 1
+    for (uint32_t i0 = 0; i0 < nd; i0 += 4u * TL) {
+      uint32_t v[4];
+#pragma unroll
+      for (uint32_t r = 0; r < 4u; ++r) {
+        const uint32_t i = i0 + g + r * TL;
+        v[r] = i < nd ? load4_unaligned(pay - s0 + 4u * i, lim) : 0u;
+      }
+#pragma unroll
+      for (uint32_t r = 0; r < 4u; ++r) {
+        const uint32_t i = i0 + g + r * TL;
+        if (i < nd) ((uint32_t*)PB)[i] = v[r];
+      }
+    }
 #pragma unroll
     for (uint32_t i = g; i < E / 4u; i += TL) ((uint32_t*)OB)[i] = 0u;
     if (g < NB) STB[g] = 0ull;
@@ -497,20 +512,29 @@ __device__ __forceinline__ void decode_group(const DecP& p, const uint8_t* in, c
     const uint8_t* pay = in + p.base + off;
     uint8_t* dst = out + start;
     const bool al = (((uintptr_t)dst) & 3u) == 0;
-    if (e.x == 0u && e.y == 0u) {
-      for (uint32_t i = g; i < (bc + 3u) / 4u; i += TL) {
-        if (al && 4u * i + 4u <= bc) *(uint32_t*)(dst + 4u * i) = 0u;
-        else
-          for (uint32_t b = 0; b < 4u; ++b)
-            if (4u * i + b < bc) dst[4u * i + b] = 0u;
-      }
-    } else if (e.x == 0u) {
-      for (uint32_t i = g; i < (bc + 3u) / 4u; i += TL) {
-        const uint32_t v = load4_unaligned(pay + 4u * i, lim);
-        if (al && 4u * i + 4u <= bc) *(uint32_t*)(dst + 4u * i) = v;
-        else
-          for (uint32_t b = 0; b < 4u; ++b)
-            if (4u * i + b < bc) dst[4u * i + b] = (uint8_t)(v >> (8u * b));
+    if (e.x == 0u) {
+      // zero or raw chunk: four loads per lane in flight before their stores
+      const bool zero = e.y == 0u;
+      const uint32_t nw = (bc + 3u) / 4u;
+#pragma unroll 1
+      for (uint32_t i0 = 0; i0 < nw; i0 += 4u * TL) {
+        uint32_t v[4];
+#pragma unroll
+        for (uint32_t r = 0; r < 4u; ++r) {
+          const uint32_t i = i0 + g + r * TL;
+          v[r] = (!zero && i < nw) ? load4_unaligned(pay + 4u * i, lim) : 0u;
+        }
+#pragma unroll
+        for (uint32_t r = 0; r < 4u; ++r) {
+          const uint32_t i = i0 + g + r * TL;
+          if (i >= nw) continue;
+          if (al && 4u * i + 4u <= bc) {
+            *(uint32_t*)(dst + 4u * i) = v[r];
+          } else {
+            for (uint32_t b = 0; b < 4u; ++b)
+              if (4u * i + b < bc) dst[4u * i + b] = (uint8_t)(v[r] >> (8u * b));
+          }
+        }
       }
     } else {
       if (!decode_coded<CS, WS>(pay, lim, e.x, e.y, bc, dst, arena, sh) && g == 0)
@@ -582,8 +606,11 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
                      a.chunks_cap, T, (DecP*)a.params, a.loc, a.tile_sums, a.tile_err, a.status, a.out_bytes);
   if (a.ev_start && hipEventRecord(a.ev_start, stream) != hipSuccess) return hipErrorUnknown;
   if (a.chunks_cap > 0) {
+    // workgroups loop over chunk groups: enough of them to fill every CU a few
+    // times over, not one per group (their launch would cost more than the
+    // work for zero and raw chunks)
     uint32_t grid = (a.chunks_cap + kWaves - 1u) / kWaves;
-    if (grid > kMaxGrid) grid = kMaxGrid;
+    if (grid > kDecodeGrid) grid = kDecodeGrid;
     hipLaunchKernelGGL(chunks_kernel, dim3(grid), dim3(kBlock), 0, stream, a.in, a.in_bytes, a.out,
                        (const DecP*)a.params, (const uint32_t*)a.loc, (const uint64_t*)a.tile_sums,
                        (const uint32_t*)a.tile_err, a.status, a.out_bytes);
