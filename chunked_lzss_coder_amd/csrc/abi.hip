@@ -43,7 +43,7 @@ DecLayoutHost dec_layout(uint64_t chunks_cap) {
   L.loc = round_up(decode_params_bytes());
   L.tile_sums = L.loc + round_up((chunks_cap ? chunks_cap : 1) * 4u);
   // the launch uses at most this many tiles for any chunk bound up to
-  // chunks_cap: 256 while tiles grow, then one per 2^20 chunks
+  // chunks_cap: at most 64 while tiles grow, then one per 2^20 chunks
   const uint32_t cap32 = chunks_cap > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)chunks_cap;
   const uint32_t nt = decode_num_tiles(cap32);
   const uint64_t tiles = nt > 256u ? nt : 256u;

@@ -32,7 +32,7 @@ namespace {
 
 constexpr uint32_t kTileMin = 1024;     // chunks per scan tile: at least,
 constexpr uint32_t kTileMax = 1u << 20;  // at most (offsets within a tile < 2^32)
-constexpr uint32_t kMaxTiles = 256;      // tiles wanted for large streams
+constexpr uint32_t kMaxTiles = 64;       // tiles wanted (one tile total per lane)
 constexpr uint32_t kScanPer = 4;         // chunks per thread per scan round
 constexpr uint32_t kScanRound = kScanPer * kBlock;
 constexpr uint32_t kDecodeGrid = 8192;   // chunk-kernel workgroups at most
@@ -493,21 +493,35 @@ __device__ __forceinline__ void decode_group(const DecP& p, const uint8_t* in, c
   constexpr uint32_t CPW = kWaves / G::TW;  // chunks per workgroup
   const uint32_t team = threadIdx.x / TL, g = threadIdx.x % TL;
   uint8_t* arena = arena_all + team * (G::TW * kSlot);
-  const uint32_t ngroups = (p.nc + CPW - 1u) / CPW;
-  for (uint32_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
-    const uint64_t c = (uint64_t)grp * CPW + team;
-    if (c >= p.nc) continue;  // CPW > 1 only for one-wave teams: no workgroup barrier below
-    const uint2 e = read_row(in, c);
+  // A chunk's metadata (size-table row, offset within its tile, a lane's
+  // share of the earlier tiles' totals) is fetched one chunk ahead, so those
+  // loads are in flight while the previous chunk is decoded.
+  const uint64_t stride = (uint64_t)gridDim.x * CPW;
+  uint64_t c = (uint64_t)blockIdx.x * CPW + team;
+  uint2 e_n = make_uint2(0u, 0u);
+  uint32_t loc_n = 0;
+  uint64_t tps_n = 0;
+  auto fetch = [&](uint64_t cc) {
+    e_n = read_row(in, cc);
+    loc_n = loc[cc];
+    const uint32_t t = (uint32_t)(cc / p.T);
+    tps_n = lane_id() < t ? tile_sum[lane_id()] : 0ull;
+  };
+  if (c < p.nc) fetch(c);
+  for (; c < p.nc; c += stride) {  // CPW > 1 only for one-wave teams: no workgroup barrier below
+    const uint2 e = e_n;
+    const uint32_t loc_c = loc_n;
+    uint64_t tp = tps_n;
+    if (c + stride < p.nc) fetch(c + stride);
     const uint64_t start = c * CS;
     const uint32_t bc = (uint32_t)((p.n - start) < CS ? (p.n - start) : CS);
     if (!row_ok(e, bc)) continue;  // reported by the scan kernel
     const uint32_t size = entry_payload(e.x, e.y);
     // payload offset = earlier tiles' totals + offset within the tile
     const uint32_t t = (uint32_t)(c / p.T);
-    uint64_t tp = 0;
-    for (uint32_t i = lane_id(); i < t; i += 64u) tp += tile_sum[i];
+    for (uint32_t i = lane_id() + 64u; i < t; i += 64u) tp += tile_sum[i];  // over 64 tiles: huge streams only
     tp = lane63_64(wave_incl_add64(tp));
-    const uint64_t off = tp + loc[c];
+    const uint64_t off = tp + loc_c;
     if (off + size > p.pb) continue;  // sizes inconsistent with the header: reported by wave 0 below
     const uint8_t* pay = in + p.base + off;
     uint8_t* dst = out + start;

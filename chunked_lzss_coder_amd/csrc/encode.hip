@@ -474,12 +474,23 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
         M += (uint32_t)__builtin_popcountll(isw[i] & lmw[i]);
       }
     } else {
-      if (g == 0) {
+      if (g < 64u) {
+        // the first wave hops word by word: the exits of 64 positions in one
+        // VGPR (the next word's load in flight), one readlane per hop
+        uint64_t* IS64w = (uint64_t*)ISB;
         uint32_t P = 0;
-        while (P < (uint32_t)E) {
-          const uint32_t xq = XQ[P];
-          ((uint8_t*)ISB)[P >> 3] = (uint8_t)(xq >> 16);
-          P = xq & 0xFFFFu;
+        uint32_t xq_next = XQ[lane];
+#pragma unroll 1
+        for (uint32_t i = 0; i < NR; ++i) {
+          const uint32_t xqr = xq_next;
+          if (i + 1u < NR) xq_next = XQ[64u * (i + 1u) + lane];
+          uint64_t acc = 0;
+          while (P < 64u * (i + 1u)) {
+            const uint32_t xq = __builtin_amdgcn_readlane(xqr, P & 63u);
+            acc |= (uint64_t)(xq >> 16) << (P & 56u);
+            P = xq & 0xFFFFu;
+          }
+          if (lane == 0u) IS64w[i] = acc;
         }
       }
       team_sync<WPC>();
@@ -756,8 +767,10 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(const uint8_t* __restri
 
 template <int WS, int E, int LEVEL>
 hipError_t launch_one(const EncodeArgs& a, hipStream_t stream) {
-  constexpr int WPC = E <= 1024 ? 1 : E / 1024;
-  constexpr int CPW = E <= 1024 ? 2 : 1;
+  // waves per chunk: one up to 512 elements (two chunks per workgroup), then
+  // one per 512 elements, so LDS per wave stays the same and occupancy holds
+  constexpr int WPC = E <= 512 ? 1 : E / 512;
+  constexpr int CPW = E <= 512 ? 2 : 1;
   constexpr uint32_t threads = 64u * WPC * CPW;
   const uint32_t grid = (a.num_chunks + CPW - 1) / CPW;  // one chunk per team
   hipLaunchKernelGGL((encode_kernel<WS, E, LEVEL, WPC, CPW>), dim3(grid), dim3(threads), 0, stream, a.in, a.n,
