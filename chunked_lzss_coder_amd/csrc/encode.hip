@@ -177,11 +177,14 @@ struct Lay {
   static constexpr uint32_t NW64 = E / 64;  // 64-position words
   static constexpr uint32_t NSEG = E / 8;   // 8-position parse segments
   // Word offsets inside the per-chunk region, after X[E]:
-  //   search: LV = S_1 | S_4 | S_16 | S_64 (4 x E words)
+  //   search: LV = S_1 | S_4 | S_16 | S_64, each E words followed by zero
+  //           padding that the descent may read (3, 9, 33, 129 words, rounded)
   //   level 1: LO (E) | hash table (2048)
   //   parse:   LO (E) | XQ (E) | ISB (E/32) | LMB (E/32) | FLG (E/32) | STG (CS/4 + 8)
   static constexpr uint32_t RP = 2u * E + 3u * (E / 32u) + CS / 4u + 8u;
-  static constexpr uint32_t R = (cmax(cmax(4u * E, LEVEL ? (uint32_t)E + kHashSize : 0u), RP) + 3u) & ~3u;
+  static constexpr uint32_t TOFF[4] = {0u, E + 4u, 2u * E + 16u, 3u * E + 52u};  // table offsets in LV
+  static constexpr uint32_t SEARCH = 4u * E + 184u;
+  static constexpr uint32_t R = (cmax(cmax(SEARCH, LEVEL ? (uint32_t)E + kHashSize : 0u), RP) + 3u) & ~3u;
   static constexpr uint32_t MISC = 2u * (E / 64u + 1u) + 8u;
   static constexpr uint32_t TOTAL = (E + R + MISC + 3u) & ~3u;  // words per chunk, 16-byte multiple
 };
@@ -315,12 +318,18 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
     team_sync<WPC>();
 
     // ---- 3. base-4 doubling table S_4, S_16, S_64 and a 4-round descent ------------
-    // S_k[p] = AND of omask over [p, p+k) when p + k <= E, else 0.
+    // S_k[p] = AND of omask over [p, p+k) when p + k <= E, else 0; every
+    // table is followed by zeros, so descent reads past the chunk need no
+    // bounds checks.
+    for (uint32_t i = g; i < 184u; i += TL) {  // padding word i of level lv is at (lv + 1) E + i
+      const uint32_t lv = i < 4u ? 0u : (i < 16u ? 1u : (i < 52u ? 2u : 3u));
+      LV[(lv + 1u) * (uint32_t)E + i] = 0u;
+    }
 #pragma unroll
     for (uint32_t lv = 1; lv < 4; ++lv) {
       const uint32_t k = 1u << (2 * lv), step = k >> 2;
-      const uint32_t* prev = LV + (lv - 1) * E;
-      uint32_t* cur = LV + lv * E;
+      const uint32_t* prev = LV + L::TOFF[lv - 1];
+      uint32_t* cur = LV + L::TOFF[lv];
 #pragma unroll
       for (uint32_t i = 0; i < PPL; ++i) {
         const uint32_t p = g + i * TL;
@@ -340,22 +349,13 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
 #pragma unroll
       for (int lv = 3; lv >= 0; --lv) {
         const uint32_t k = 1u << (2 * lv);
-        const uint32_t* S = LV + (uint32_t)lv * E;
-        const uint32_t q0 = p + Ln, q1 = q0 + k, q2 = q1 + k;
-        const uint32_t a = q0 < (uint32_t)E ? S[q0] : 0u;
-        const uint32_t b = q1 < (uint32_t)E ? S[q1] : 0u;
-        const uint32_t d = q2 < (uint32_t)E ? S[q2] : 0u;
-        const uint32_t t1 = surv & a, t2 = t1 & b, t3 = t2 & d;
-        if (t3) {
-          surv = t3;
-          Ln += 3u * k;
-        } else if (t2) {
-          surv = t2;
-          Ln += 2u * k;
-        } else if (t1) {
-          surv = t1;
-          Ln += k;
-        }
+        // p + Ln <= E (every surviving position is inside the chunk), so the
+        // three reads end within the table's padding
+        const uint32_t* S = LV + L::TOFF[lv] + p + Ln;
+        const uint32_t t1 = surv & S[0], t2 = t1 & S[k], t3 = t2 & S[2u * k];
+        const uint32_t n = (uint32_t)(t1 != 0u) + (uint32_t)(t2 != 0u) + (uint32_t)(t3 != 0u);
+        surv = t3 ? t3 : (t2 ? t2 : (t1 ? t1 : surv));
+        Ln += n << (2 * lv);
       }
       lo[i] = Ln ? (Ln | (((uint32_t)__builtin_ctz(surv) + 1u) << 8)) : 0u;
     }
