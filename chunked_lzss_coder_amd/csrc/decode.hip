@@ -184,43 +184,65 @@ __device__ __forceinline__ void team_sync() {
   else __syncthreads();
 }
 
-// Exclusive scan of one value per team lane; total to *tot.
+// Collectives over a chunk's team.  One wave: DPP moves and ballots only.  A
+// whole workgroup: every wave posts its partial to one of two LDS rows (they
+// alternate between calls), one barrier, then every wave reads the row.  A row
+// is written again only two calls later, after every wave has passed the
+// barrier in between, so one barrier per call suffices; that barrier also
+// orders all earlier LDS writes of the team.
 template <uint32_t TW>
-__device__ __forceinline__ uint32_t team_scan(uint32_t v, uint32_t* tot, uint32_t* sh) {
-  const uint32_t inc = wave_incl_add(v);
-  const uint32_t wt = lane63(inc);
-  if constexpr (TW == 1) {
-    *tot = wt;
-    return inc - v;
-  } else {
-    const uint32_t w = threadIdx.x >> 6;
-    if (lane_id() == 0) sh[w] = wt;
-    __syncthreads();
-    uint32_t pre = 0, t = 0;
-#pragma unroll
-    for (uint32_t i = 0; i < TW; ++i) {
-      const uint32_t x = sh[i];
-      pre += i < w ? x : 0u;
-      t += x;
-    }
-    __syncthreads();
-    *tot = t;
-    return pre + inc - v;
+struct TeamX {
+  uint32_t* rows;  // 2 x kWaves words
+  uint32_t par;
+
+  __device__ __forceinline__ uint32_t* next_row() {
+    uint32_t* r = rows + par * kWaves;
+    par ^= 1u;
+    return r;
   }
-}
-
-template <uint32_t TW>
-__device__ __forceinline__ uint32_t team_sum(uint32_t v, uint32_t* sh) {
-  uint32_t t;
-  team_scan<TW>(v, &t, sh);
-  return t;
-}
-
-template <uint32_t TW>
-__device__ __forceinline__ bool team_any(bool v) {
-  if constexpr (TW == 1) return __ballot(v) != 0ull;
-  else return __syncthreads_or(v);
-}
+  // exclusive scan of one value per team lane; total to *tot
+  __device__ __forceinline__ uint32_t scan(uint32_t v, uint32_t* tot) {
+    const uint32_t inc = wave_incl_add(v);
+    const uint32_t wt = lane63(inc);
+    if constexpr (TW == 1) {
+      *tot = wt;
+      return inc - v;
+    } else {
+      const uint32_t w = threadIdx.x >> 6;
+      uint32_t* r = next_row();
+      if (lane_id() == 0) r[w] = wt;
+      __syncthreads();
+      uint32_t pre = 0, t = 0;
+#pragma unroll
+      for (uint32_t i = 0; i < TW; ++i) {
+        const uint32_t x = r[i];
+        pre += i < w ? x : 0u;
+        t += x;
+      }
+      *tot = t;
+      return pre + inc - v;
+    }
+  }
+  __device__ __forceinline__ uint32_t sum(uint32_t v) {
+    uint32_t t;
+    scan(v, &t);
+    return t;
+  }
+  __device__ __forceinline__ bool any(bool b) {
+    const bool wb = __ballot(b) != 0ull;
+    if constexpr (TW == 1) {
+      return wb;
+    } else {
+      uint32_t* r = next_row();
+      if (lane_id() == 0) r[threadIdx.x >> 6] = wb ? 1u : 0u;
+      __syncthreads();
+      uint32_t o = 0;
+#pragma unroll
+      for (uint32_t i = 0; i < TW; ++i) o |= r[i];
+      return o != 0u;
+    }
+  }
+};
 
 // d mod o for d < 256, 1 <= o < 256: the quotient of d + 1/2 by o is computed
 // in fp32 with an approximate reciprocal; it lies at least 1/(2o) >= 1/510
@@ -239,6 +261,7 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
                              uint8_t* dst, uint8_t* arena, uint32_t* sh) {
   using G = Geo<CS, WS>;
   constexpr uint32_t E = G::E, TW = G::TW, TL = G::TL, J = G::J, NB = G::NB;
+  TeamX<TW> tx{sh, 0u};
   const uint32_t g = threadIdx.x % TL, lane = lane_id();
   uint8_t* VAL = arena;
   uint8_t* PB = arena + CS;
@@ -292,7 +315,7 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
     fb = (fb >> (k0 & 7u)) & ((1u << nit) - 1u);
   }
   uint32_t mt_total;
-  const uint32_t m0 = team_scan<TW>((uint32_t)__builtin_popcount(fb), &mt_total, sh);
+  const uint32_t m0 = tx.scan((uint32_t)__builtin_popcount(fb), &mt_total);
   const uint32_t tp0 = WS * (k0 - m0) + 2u * m0;
   // item r of this lane: flag, data offset, output length (0 if unreadable)
   auto item_len = [&](uint32_t tp, bool mt) -> uint32_t {
@@ -312,7 +335,7 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
     }
   }
   uint32_t len_total;
-  uint32_t op = team_scan<TW>(sum, &len_total, sh);
+  uint32_t op = tx.scan(sum, &len_total);
   uint32_t K = 0, MK = 0, bad = 0, ends = 0;
   {
     uint32_t tp = tp0;
@@ -353,8 +376,8 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
   // and leave no match flag set after the last of them
   {
     // K, MK <= 4103 items and bad, ends <= 256 lanes: two 16-bit fields each
-    const uint32_t r0 = team_sum<TW>(K | (MK << 16), sh);
-    const uint32_t r1 = team_sum<TW>(bad | (ends << 16), sh);
+    const uint32_t r0 = tx.sum(K | (MK << 16));
+    const uint32_t r1 = tx.sum(bad | (ends << 16));
     const uint32_t Kt = r0 & 0xFFFFu, MKt = r0 >> 16, badt = r1 & 0xFFFFu, endst = r1 >> 16;
     if (badt || endst != 1u || (Kt + 7u) / 8u != F || WS * (Kt - MKt) + 2u * MKt != D || MKt != mt_total)
       return false;
@@ -424,10 +447,10 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
       SRC[q] = (uint16_t)s;
       if (O) pend |= 1u << j;
     }
-    team_sync<TW>();
-    // pointer jumping: a source that is itself a literal ends the chain
+    // pointer jumping: a source that is itself a literal ends the chain (the
+    // exchange's barrier at the top of each round orders the writes before it)
     for (uint32_t round = 0;; ++round) {
-      if (!team_any<TW>(pend != 0u)) break;
+      if (!tx.any(pend != 0u)) break;
       if (round == 16u) return false;  // chains resolve within log2(E) + 1 rounds
 #pragma unroll
       for (uint32_t j = 0; j < J; ++j) {
@@ -441,7 +464,6 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
           }
         }
       }
-      team_sync<TW>();
     }
     // copy every match element from its literal
 #pragma unroll
@@ -481,7 +503,7 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
       }
     }
   }
-  return !team_any<TW>(padbad);
+  return !tx.any(padbad);
 }
 
 template <uint32_t CS, uint32_t WS>
@@ -575,7 +597,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(7))) voi
                                                         uint32_t* __restrict__ status,
                                                         uint64_t* __restrict__ out_bytes) {
   __shared__ __attribute__((aligned(16))) uint8_t arena[kArena];
-  __shared__ uint32_t sh[kWaves];
+  __shared__ uint32_t sh[2 * kWaves];
   const DecP p = *P;
   if (p.status != kStatusOk) return;
   if (blockIdx.x == 0 && threadIdx.x < 64u) {
