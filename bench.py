@@ -70,6 +70,36 @@ class HipEvents:
         self.events = []
 
 
+def kernel_source_hash() -> str:
+    """sha256 over the encode kernel's sources: a counter record taken from
+    other sources no longer describes the kernel."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("encode.hip", "common.h"):
+        with open(os.path.join(_ROOT, "chunked_lzss_coder_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(cs: int, ws: int, level: int, workload: str):
+    """HBM bytes per launch of the chunk encode kernel from the committed
+    rocprofv3 counter record (FETCH_SIZE and WRITE_SIZE, each scaled by the
+    same counter's reading for a plain copy of known size), or None when no
+    record matches this workload and these kernel sources."""
+    path = os.path.join(_ROOT, "profiles", "encode_traffic.json")
+    try:
+        with open(path) as fh:
+            recs = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    src = kernel_source_hash()
+    for r in recs.get("records", []):
+        if (r.get("source_sha256") == src and r.get("workload") == workload and r.get("chunk_size") == cs
+                and r.get("word_size") == ws and r.get("level") == level):
+            return r.get("traffic_bytes")
+    return None
+
+
 def cpu_baseline(w, level, gpu_stream_bytes: bytes):
     """Oracle leg: time the single-threaded CPU oracle on the same bytes and
     check the GPU stream against its stream."""
@@ -95,6 +125,22 @@ def cpu_baseline(w, level, gpu_stream_bytes: bytes):
     back = oracle.decode(ref)
     t_dec = time.perf_counter() - t0
     ok_rt = bool(np.array_equal(back, sample))
+    # all cores: the same oracle call over contiguous whole-chunk ranges, one
+    # thread each (the C call releases the interpreter lock); at most 16
+    # threads, the host share of one GPU
+    from concurrent.futures import ThreadPoolExecutor
+    threads = max(1, min(16, os.cpu_count() or 1))
+    nch = -(-take // w.chunk_size)
+    per = -(-nch // threads)
+    parts = [sample[i * per * w.chunk_size:min(take, (i + 1) * per * w.chunk_size)] for i in range(threads)]
+    parts = [q for q in parts if q.size]
+    mt_passes, t_mt = 0, 0.0
+    with ThreadPoolExecutor(max_workers=len(parts)) as ex:
+        while mt_passes == 0 or (t_mt < 5.0 and mt_passes < 200):
+            t0 = time.perf_counter()
+            list(ex.map(lambda q: oracle.encode(q, w.chunk_size, w.word_size, level), parts))
+            t_mt += time.perf_counter() - t0
+            mt_passes += 1
     identical = None
     if take == n:
         identical = bool(ref.tobytes() == gpu_stream_bytes)
@@ -110,6 +156,9 @@ def cpu_baseline(w, level, gpu_stream_bytes: bytes):
         "passes": passes,
         "decode_s": round(t_dec, 3),
         "round_trip": ok_rt,
+        "all_cores": {"value": round(take * mt_passes / t_mt / 1e9, 6), "unit": "GB/s", "cores": len(parts),
+                      "passes": mt_passes, "encode_s": round(t_mt, 3),
+                      "sample": "the same bytes split into contiguous whole-chunk ranges, one oracle call per thread"},
     }, identical
 
 
@@ -121,6 +170,10 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", type=int, default=1, help="workload index 0..4 (default 1)")
     ap.add_argument("--levels", type=str, default=None, help="comma-separated match levels (default: workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (the HBM-counter reference)")
+    ap.add_argument("--flush-reps", type=int, default=11,
+                    help="repetitions of the flushed-cache and host-latency measurements (0: skip)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -234,7 +287,55 @@ def main(argv=None) -> int:
             "algorithmic_bytes": algo,
             "round_trip": True,
         }
+    # Flushed runs: a 512 MiB write between repetitions evicts the input and
+    # the stream from the caches (the 256 MB last-level cache included); and
+    # host-observed latency: the call plus the read-back of *d_out_bytes.
+    if args.flush_reps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        s_ = torch.cuda.current_stream()
+        for lv in levels:
+            out, nb, ews, dout, dnb, st, dws = bufs[lv]
+            fe, fd, he, hd = [], [], [], []
+            for i in range(args.flush_reps):
+                flush.fill_(i & 0xFF)
+                ce = ev.pair()
+                ev.hip.hipEventRecord(ce[0], ctypes.c_void_p(s_.cuda_stream))
+                g.encode_into(x, cs, ws, lv, out, nb, ews)
+                ev.hip.hipEventRecord(ce[1], ctypes.c_void_p(s_.cuda_stream))
+                flush.fill_((i + 1) & 0xFF)
+                cd = ev.pair()
+                ev.hip.hipEventRecord(cd[0], ctypes.c_void_p(s_.cuda_stream))
+                g.decode_into(out, stream_bytes[lv], dout, dnb, st, dws)
+                ev.hip.hipEventRecord(cd[1], ctypes.c_void_p(s_.cuda_stream))
+                torch.cuda.synchronize()
+                fe.append(ev.ms(ce))
+                fd.append(ev.ms(cd))
+                th = time.perf_counter()
+                g.encode_into(x, cs, ws, lv, out, nb, ews)
+                _ = int(nb.item())
+                he.append((time.perf_counter() - th) * 1e3)
+                th = time.perf_counter()
+                g.decode_into(out, stream_bytes[lv], dout, dnb, st, dws)
+                _ = int(dnb.item())
+                hd.append((time.perf_counter() - th) * 1e3)
+            res[lv]["flushed"] = {
+                "reps": args.flush_reps,
+                "encode_ms_median": round(float(np.median(fe)), 4),
+                "decode_ms_median": round(float(np.median(fd)), 4),
+                "encode_gbps": round(n / (float(np.median(fe)) * 1e-3) / 1e9, 3),
+                "decode_gbps": round(n / (float(np.median(fd)) * 1e-3) / 1e9, 3),
+            }
+            res[lv]["host_latency_ms_median"] = {"encode": round(float(np.median(he)), 4),
+                                                 "decode": round(float(np.median(hd)), 4)}
+        del flush
     ev.close()
+    if args.calibration_copy_mib > 0:
+        a_ = torch.empty(args.calibration_copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        b_ = torch.empty_like(a_)
+        torch.cuda.synchronize()
+        b_.copy_(a_)
+        torch.cuda.synchronize()
+        del a_, b_
 
     lv0 = levels[0]
     r0 = res[lv0]
@@ -245,7 +346,7 @@ def main(argv=None) -> int:
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(r0["encode_kernel_hbm_gbps"] / HBM_PEAK_GBPS, 5),
-        "traffic": None,
+        "traffic": measured_traffic(cs, ws, lv0, w.name),
         "kernel_ms": r0["encode_kernel_ms"],
         "algorithmic_bytes_per_launch": r0["algorithmic_bytes"],
     }
