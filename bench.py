@@ -336,6 +336,23 @@ def main(argv=None) -> int:
         b_.copy_(a_)
         torch.cuda.synchronize()
         del a_, b_
+    # measured device-to-device copy rate (bytes read + written per second),
+    # reported beside the published HBM peak
+    copy_gbps = None
+    if args.flush_reps > 0:
+        a_ = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(3)
+        b_ = torch.empty_like(a_)
+        b_.copy_(a_)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(5):
+            e0.record()
+            b_.copy_(a_)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        copy_gbps = round(2 * a_.numel() / (float(np.median(ts)) * 1e-3) / 1e9, 1)
+        del a_, b_
 
     lv0 = levels[0]
     r0 = res[lv0]
@@ -347,6 +364,7 @@ def main(argv=None) -> int:
         "unit": "GB/s",
         "frac": round(r0["encode_kernel_hbm_gbps"] / HBM_PEAK_GBPS, 5),
         "traffic": measured_traffic(cs, ws, lv0, w.name),
+        "measured_copy_gbps": copy_gbps,
         "kernel_ms": r0["encode_kernel_ms"],
         "algorithmic_bytes_per_launch": r0["algorithmic_bytes"],
     }
