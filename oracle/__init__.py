@@ -72,6 +72,15 @@ def _load():
                                        ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_uint32),
                                        ctypes.POINTER(ctypes.c_uint32)]
     lib.oracle_stream_info.restype = ctypes.c_int
+    u64 = ctypes.c_uint64
+    lib.oracle_split_bounds.argtypes = [u64, ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(u64),
+                                        ctypes.POINTER(u64), ctypes.POINTER(u64)]
+    lib.oracle_split_bounds.restype = None
+    lib.oracle_encode_split.argtypes = [u8p, u64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                        u8p, u64, u8p, u8p, u64, u8p, u64, ctypes.POINTER(u64)]
+    lib.oracle_encode_split.restype = ctypes.c_int
+    lib.oracle_decode_split.argtypes = [u8p, u64, u8p, u8p, u64, u8p, u64, u8p, u64]
+    lib.oracle_decode_split.restype = ctypes.c_int64
     _lib = lib
     return lib
 
@@ -164,3 +173,50 @@ def stream_info(stream):
     if st != OK:
         return None
     return n.value, t.value, cs.value, ws.value
+
+
+# ---- split mode: literals / lengths / offsets / meta ports ----------------
+
+def split_bounds(n: int, chunk_size: int, word_size: int) -> tuple[int, int, int]:
+    """Port capacities that always suffice: (literals, lengths = offsets, meta)."""
+    a, b, c = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
+    _load().oracle_split_bounds(n, chunk_size, word_size, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    return a.value, b.value, c.value
+
+
+def encode_split(data, chunk_size: int, word_size: int, level: int):
+    """Encode into four ports; returns (literals, lengths, offsets, meta) uint8 arrays."""
+    a = _bytes(data)
+    bl, bt, bm = split_bounds(a.size, chunk_size, word_size)
+    lit = np.empty(max(bl, 1), dtype=np.uint8)
+    lens = np.empty(max(bt, 1), dtype=np.uint8)
+    offs = np.empty(max(bt, 1), dtype=np.uint8)
+    meta = np.empty(max(bm, 1), dtype=np.uint8)
+    sizes = (ctypes.c_uint64 * 4)()
+    st = _load().oracle_encode_split(_ptr(a), a.size, chunk_size, word_size, level, _ptr(lit), bl, _ptr(lens),
+                                     _ptr(offs), bt, _ptr(meta), bm, sizes)
+    if st != OK:
+        raise ValueError(f"oracle_encode_split status {st}")
+    return lit[:sizes[0]], lens[:sizes[1]], offs[:sizes[2]], meta[:sizes[3]]
+
+
+def decode_split_status(lit, lens, offs, meta, cap: int | None = None) -> tuple[int, np.ndarray]:
+    """Decode four ports; returns (status_or_size, output).  Never raises on corruption.
+    lens and offs must have the same length (one byte per match each)."""
+    lit, lens, offs, meta = (_bytes(v) for v in (lit, lens, offs, meta))
+    if lens.size != offs.size:
+        raise ValueError("lengths and offsets ports differ in length")
+    if cap is None:
+        cap = int(np.frombuffer(meta[16:24].tobytes(), dtype="<u8")[0]) if meta.size >= 32 else 0
+    out = np.zeros(max(cap, 1), dtype=np.uint8)
+    one = ctypes.c_void_p(1)
+    r = int(_load().oracle_decode_split(_ptr(lit) or one, lit.size, _ptr(lens) or one, _ptr(offs) or one,
+                                        lens.size, _ptr(meta) or one, meta.size, _ptr(out), cap))
+    return r, out[: max(r, 0)]
+
+
+def decode_split(lit, lens, offs, meta) -> np.ndarray:
+    r, out = decode_split_status(lit, lens, offs, meta)
+    if r < 0:
+        raise ValueError(f"oracle_decode_split status {r}")
+    return out

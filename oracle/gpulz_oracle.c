@@ -380,3 +380,172 @@ int64_t oracle_decode(const uint8_t* s, uint64_t in_bytes, uint8_t* out, uint64_
   if (off != pb) return OR_ECORRUPT;
   return (int64_t)n;
 }
+
+/* ---- split mode --------------------------------------------------------
+ * The same items in four ports instead of one interleaved stream (codebase
+ * notes CN-GPULZ-1, split mode; GPULZStage page, split-mode paragraphs):
+ *   literals  literal words of coded chunks in item order, and the real
+ *             bytes of raw chunks (they are all literal);
+ *   lengths   one length byte per match item;
+ *   offsets   one offset byte per match item;
+ *   meta      the 32-byte header (version byte 2), one entry per chunk, then
+ *             the flag bitmaps of the coded chunks back to back.
+ * Readings (the pages give the ports, not their byte layout): ports follow
+ * chunk order; a coded chunk's entry is {u32 items K, u32 matches M}; zero
+ * and raw chunks keep their entries (0,0) and (0, 0x80000000 | real bytes);
+ * a chunk is raw exactly when its single-stream form would be; the header's
+ * last field holds the total flag bytes. */
+#define OR_SPLIT_VERSION 2u
+
+/* Port capacities that always suffice. */
+void oracle_split_bounds(uint64_t n, uint32_t cs, uint32_t ws, uint64_t* lit, uint64_t* tok, uint64_t* meta) {
+  uint64_t chunks = (n + cs - 1) / cs;
+  *lit = n;           /* a coded chunk's literals are fewer than its bytes */
+  *tok = n / 2 + 1;   /* two data bytes per match, and fewer than the chunk */
+  *meta = OR_HEADER_BYTES + OR_ENTRY_BYTES * chunks + chunks * ((cs / ws + 7u) / 8u);
+}
+
+/* Encode into the four ports.  sizes[0..3] = bytes written to literals,
+ * lengths, offsets, meta.  Returns OR_OK or a negative status. */
+int oracle_encode_split(const uint8_t* in, uint64_t n, uint32_t cs, uint32_t ws, uint32_t level,
+                        uint8_t* lit, uint64_t lit_cap, uint8_t* lens, uint8_t* offs, uint64_t tok_cap,
+                        uint8_t* meta, uint64_t meta_cap, uint64_t* sizes) {
+  if (!cs_ok(cs) || !ws_ok(ws) || level > 1u) return OR_EINVAL;
+  if (n > 0 && in == NULL) return OR_EINVAL;
+  uint64_t chunks = (n + cs - 1) / cs;
+  if (chunks > 0xFFFFFFFFull) return OR_EINVAL;
+  uint64_t blit, btok, bmeta;
+  oracle_split_bounds(n, cs, ws, &blit, &btok, &bmeta);
+  if (meta == NULL || lit_cap < blit || tok_cap < btok || meta_cap < bmeta) return OR_ECAP;
+  if (n > 0 && (lit == NULL || lens == NULL || offs == NULL)) return OR_ECAP;
+
+  uint8_t* table = meta + OR_HEADER_BYTES;
+  uint8_t* flags_out = table + OR_ENTRY_BYTES * chunks;
+  uint8_t* payload = (uint8_t*)malloc(cs + 8);
+  uint64_t nl = 0, nt = 0, nf = 0;
+  for (uint64_t c = 0; c < chunks; ++c) {
+    uint64_t start = c * cs;
+    uint32_t bc = (uint32_t)((n - start) < cs ? (n - start) : cs);
+    uint32_t f, d, pb;
+    int st = oracle_encode_chunk(in + start, bc, cs, ws, level, &f, &d, payload, &pb);
+    if (st != OR_OK) { free(payload); return st; }
+    if (f == 0) { /* zero or raw: the entry as in one stream; raw bytes to literals */
+      put_u32(table + OR_ENTRY_BYTES * c, 0);
+      put_u32(table + OR_ENTRY_BYTES * c + 4, d);
+      memcpy(lit + nl, payload, pb);
+      nl += pb;
+      continue;
+    }
+    /* coded: walk the single-stream items in order and deal them out */
+    const uint8_t* fl = payload;
+    const uint8_t* dp = payload + f;
+    uint32_t used = 0, K = 0, M = 0;
+    while (used < d) {
+      if ((fl[K >> 3] >> (K & 7u)) & 1u) {
+        lens[nt + M] = dp[used];
+        offs[nt + M] = dp[used + 1];
+        used += 2;
+        ++M;
+      } else {
+        memcpy(lit + nl, dp + used, ws);
+        nl += ws;
+        used += ws;
+      }
+      ++K;
+    }
+    put_u32(table + OR_ENTRY_BYTES * c, K);
+    put_u32(table + OR_ENTRY_BYTES * c + 4, M);
+    memcpy(flags_out + nf, fl, f); /* f = ceil(K / 8), unused bits 0 */
+    nf += f;
+    nt += M;
+  }
+  free(payload);
+  put_u32(meta + 0, OR_MAGIC);
+  meta[4] = (uint8_t)OR_SPLIT_VERSION;
+  meta[5] = (uint8_t)ws;
+  meta[6] = 0;
+  meta[7] = 0;
+  put_u32(meta + 8, cs);
+  put_u32(meta + 12, (uint32_t)chunks);
+  put_u64(meta + 16, n);
+  put_u64(meta + 24, nf);
+  sizes[0] = nl;
+  sizes[1] = nt;
+  sizes[2] = nt;
+  sizes[3] = OR_HEADER_BYTES + OR_ENTRY_BYTES * chunks + nf;
+  return OR_OK;
+}
+
+/* Decode from the four ports (each at least as long as the table implies;
+ * extra bytes are ignored).  Returns original_size or a negative status;
+ * never reads past a port's given length or writes past cap. */
+int64_t oracle_decode_split(const uint8_t* lit, uint64_t lit_n, const uint8_t* lens, const uint8_t* offs,
+                            uint64_t tok_n, const uint8_t* meta, uint64_t meta_n, uint8_t* out, uint64_t cap) {
+  if (meta == NULL) return OR_EINVAL;
+  if (meta_n < OR_HEADER_BYTES) return OR_ECORRUPT;
+  if (get_u32(meta) != OR_MAGIC || meta[4] != OR_SPLIT_VERSION || meta[6] != 0 || meta[7] != 0) return OR_ECORRUPT;
+  uint32_t ws = meta[5], cs = get_u32(meta + 8), chunks = get_u32(meta + 12);
+  uint64_t n = get_u64(meta + 16), nf_total = get_u64(meta + 24);
+  if (!ws_ok(ws) || !cs_ok(cs) || (n + cs - 1) / cs != chunks) return OR_ECORRUPT;
+  if ((uint64_t)OR_HEADER_BYTES + (uint64_t)OR_ENTRY_BYTES * chunks > meta_n) return OR_ECORRUPT;
+  if (nf_total > meta_n - OR_HEADER_BYTES - (uint64_t)OR_ENTRY_BYTES * chunks) return OR_ECORRUPT;
+  if (cap < n || (n > 0 && out == NULL)) return OR_ECAP;
+  const uint8_t* table = meta + OR_HEADER_BYTES;
+  const uint8_t* flags = table + OR_ENTRY_BYTES * chunks;
+  uint32_t E = cs / ws;
+  uint32_t* x = (uint32_t*)malloc(sizeof(uint32_t) * E);
+  uint64_t nl = 0, nt = 0, nf = 0;
+  int st = OR_OK;
+  for (uint64_t c = 0; c < chunks && st == OR_OK; ++c) {
+    uint64_t start = c * cs;
+    uint32_t bc = (uint32_t)((n - start) < cs ? (n - start) : cs);
+    uint32_t K = get_u32(table + OR_ENTRY_BYTES * c), M = get_u32(table + OR_ENTRY_BYTES * c + 4);
+    if (K == 0 && M == 0) { memset(out + start, 0, bc); continue; }
+    if (K == 0 && (M & OR_RAW_BIT)) {
+      if ((M & ~OR_RAW_BIT) != bc || nl + bc > lit_n) { st = OR_ECORRUPT; break; }
+      memcpy(out + start, lit + nl, bc);
+      nl += bc;
+      continue;
+    }
+    /* coded: K items, M of them matches; its single-stream form must have
+     * been smaller than the chunk (else it would be raw) */
+    uint32_t F = (uint32_t)(((uint64_t)K + 7u) / 8u);
+    if (K == 0 || M > K || K > E) { st = OR_ECORRUPT; break; }
+    if ((uint64_t)F + (uint64_t)ws * (K - M) + 2ull * M >= bc) { st = OR_ECORRUPT; break; }
+    if (nf + F > nf_total || nl + (uint64_t)ws * (K - M) > lit_n || nt + M > tok_n) { st = OR_ECORRUPT; break; }
+    const uint8_t* fl = flags + nf;
+    uint32_t q = 0, m = 0;
+    for (uint32_t k = 0; k < K && st == OR_OK; ++k) {
+      if (q >= E) { st = OR_ECORRUPT; break; } /* more items than elements */
+      if ((fl[k >> 3] >> (k & 7u)) & 1u) {
+        if (m >= M) { st = OR_ECORRUPT; break; }
+        uint32_t L = lens[nt + m], O = offs[nt + m];
+        ++m;
+        if (L == 0 || O == 0 || O > q || q + L > E) { st = OR_ECORRUPT; break; }
+        for (uint32_t j = 0; j < L; ++j) { x[q] = x[q - O]; ++q; }
+      } else {
+        if ((uint64_t)(k - m) >= (uint64_t)(K - M)) { st = OR_ECORRUPT; break; }
+        x[q++] = load_word(lit + nl + (uint64_t)ws * (k - m), ws);
+      }
+    }
+    if (st != OR_OK) break;
+    if (q != E || m != M) { st = OR_ECORRUPT; break; }
+    for (uint32_t b = K; b < 8u * F; ++b)
+      if ((fl[b >> 3] >> (b & 7u)) & 1u) { st = OR_ECORRUPT; break; } /* unused flag bits are 0 */
+    if (st != OR_OK) break;
+    for (uint32_t i = 0; i < E && st == OR_OK; ++i)
+      for (uint32_t b = 0; b < ws; ++b) {
+        uint64_t pos = (uint64_t)i * ws + b;
+        uint8_t v = (uint8_t)(x[i] >> (8 * b));
+        if (pos < bc) out[start + pos] = v;
+        else if (v != 0) { st = OR_ECORRUPT; break; } /* padding decodes to zeros */
+      }
+    nl += (uint64_t)ws * (K - M);
+    nt += M;
+    nf += F;
+  }
+  free(x);
+  if (st != OR_OK) return st;
+  if (nf != nf_total) return OR_ECORRUPT;
+  return (int64_t)n;
+}

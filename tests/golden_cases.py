@@ -65,3 +65,45 @@ def load():
                 cases.append(cur)
                 cur = None
     return cases
+
+
+SPLIT_GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "split_examples.txt")
+
+
+def _port(tokens: list[str], data: bytes) -> bytes:
+    out = b""
+    for p in tokens:
+        if p == "-":
+            continue
+        if p == "+INPUT":
+            out += data
+        elif p == "+INPUT64W":
+            out += data[: 64 * 4]
+        else:
+            out += bytes.fromhex(p)
+    return out
+
+
+def load_split():
+    """Cases of tests/golden/split_examples.txt: dicts with cs, ws, level,
+    input and the four ports lit / lens / offs / meta (bytes)."""
+    cases, cur = [], None
+    with open(SPLIT_GOLDEN) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, _, val = line.partition(" ")
+            if key == "case":
+                if cur is not None:
+                    cases.append(cur)
+                cur = {"name": val}
+            elif key in ("cs", "ws", "level"):
+                cur[key] = int(val)
+            elif key == "input":
+                cur["input"] = _input(val.split())
+            elif key in ("lit", "lens", "offs", "meta"):
+                cur[key] = _port(val.split(), cur["input"])
+    if cur is not None:
+        cases.append(cur)
+    return cases
