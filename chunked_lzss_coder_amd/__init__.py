@@ -16,7 +16,9 @@ LIB_PATH = os.path.join(_HERE, "libgpulz.so")
 OK, ERR_INVALID_ARG, ERR_CAPACITY, ERR_CORRUPT, ERR_HIP = 0, -1, -2, -3, -4
 STATUS_OK, STATUS_CAPACITY, STATUS_CORRUPT = 0, 2, 3
 SYMBOLS = ("gpulz_max_compressed_size", "gpulz_encode_workspace_size", "gpulz_decode_workspace_size",
-           "gpulz_encode", "gpulz_decode", "gpulz_stream_info", "gpulz_encode_timed", "gpulz_decode_timed")
+           "gpulz_encode", "gpulz_decode", "gpulz_stream_info", "gpulz_encode_timed", "gpulz_decode_timed",
+           "gpulz_split_bounds", "gpulz_encode_split_workspace_size", "gpulz_encode_split",
+           "gpulz_decode_split_workspace_size", "gpulz_decode_split")
 
 _lib = None
 
@@ -55,6 +57,16 @@ def lib() -> ctypes.CDLL:
     L.gpulz_encode_timed.restype = ctypes.c_int
     L.gpulz_decode_timed.argtypes = L.gpulz_decode.argtypes + [vp, vp]
     L.gpulz_decode_timed.restype = ctypes.c_int
+    L.gpulz_split_bounds.argtypes = [u64, u32, u32, ctypes.POINTER(u64), ctypes.POINTER(u64), ctypes.POINTER(u64)]
+    L.gpulz_split_bounds.restype = ctypes.c_int
+    L.gpulz_encode_split_workspace_size.argtypes = [u64, u32]
+    L.gpulz_encode_split_workspace_size.restype = u64
+    L.gpulz_encode_split.argtypes = [vp, u64, u32, u32, u32, vp, u64, vp, vp, u64, vp, u64, vp, vp, u64, vp]
+    L.gpulz_encode_split.restype = ctypes.c_int
+    L.gpulz_decode_split_workspace_size.argtypes = [u64]
+    L.gpulz_decode_split_workspace_size.restype = u64
+    L.gpulz_decode_split.argtypes = [vp, u64, vp, vp, u64, vp, u64, vp, u64, vp, vp, vp, u64, vp]
+    L.gpulz_decode_split.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -175,3 +187,88 @@ def stream_info(prefix: bytes):
     if rc != OK:
         return None
     return n.value, t.value, cs.value, ws.value
+
+
+# ---- split mode: literals / lengths / offsets / meta ports ----------------
+
+def split_bounds(n_bytes: int, chunk_size: int, word_size: int) -> tuple[int, int, int]:
+    """Port capacities that always suffice: (literals, lengths = offsets, meta)."""
+    a, b, c = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
+    _check(lib().gpulz_split_bounds(n_bytes, chunk_size, word_size, ctypes.byref(a), ctypes.byref(b),
+                                    ctypes.byref(c)), "gpulz_split_bounds")
+    return a.value, b.value, c.value
+
+
+def encode_split_workspace_size(n_bytes: int, chunk_size: int) -> int:
+    return int(lib().gpulz_encode_split_workspace_size(n_bytes, chunk_size))
+
+
+def decode_split_workspace_size(meta_bytes: int) -> int:
+    return int(lib().gpulz_decode_split_workspace_size(meta_bytes))
+
+
+def encode_split_into(d_in, chunk_size: int, word_size: int, match_level: int, lit, lens, offs, meta, port_bytes,
+                      workspace, stream=None) -> None:
+    """Enqueue gpulz_encode_split with caller-provided buffers (no allocation).
+    lens and offs must have the same size; port_bytes is a device uint64[4]."""
+    src = _u8_view(d_in)
+    if lens.numel() != offs.numel():
+        raise GpulzError("lengths and offsets buffers differ in size")
+    _check(lib().gpulz_encode_split(_ptr(src), src.numel(), chunk_size, word_size, match_level, _ptr(lit),
+                                    lit.numel(), _ptr(lens), _ptr(offs), lens.numel(), _ptr(meta), meta.numel(),
+                                    _ptr(port_bytes), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "gpulz_encode_split")
+
+
+def encode_split(d_in, chunk_size: int = 2048, word_size: int = 4, match_level: int = 0, stream=None):
+    """Encode into four ports.  Returns (literals, lengths, offsets, meta)
+    uint8 tensors of the worst-case sizes and port_bytes, a device uint64[4]
+    with the bytes used in each."""
+    import torch
+    src = _u8_view(d_in)
+    bl, bt, bm = split_bounds(src.numel(), chunk_size, word_size)
+    dev = src.device
+    lit = torch.empty(max(bl, 1), dtype=torch.uint8, device=dev)
+    lens = torch.empty(max(bt, 1), dtype=torch.uint8, device=dev)
+    offs = torch.empty(max(bt, 1), dtype=torch.uint8, device=dev)
+    meta = torch.empty(max(bm, 1), dtype=torch.uint8, device=dev)
+    pbytes = torch.zeros(4, dtype=torch.uint64, device=dev)
+    ws = torch.empty(max(encode_split_workspace_size(src.numel(), chunk_size), 1), dtype=torch.uint8, device=dev)
+    encode_split_into(src, chunk_size, word_size, match_level, lit, lens, offs, meta, pbytes, ws, stream)
+    return lit, lens, offs, meta, pbytes
+
+
+def decode_split_into(lit, lit_bytes: int, lens, offs, tok_bytes: int, meta, meta_bytes: int, out, out_bytes,
+                      status, workspace, stream=None) -> None:
+    """Enqueue gpulz_decode_split with caller-provided buffers (no allocation)."""
+    if lit_bytes > lit.numel() or tok_bytes > min(lens.numel(), offs.numel()) or meta_bytes > meta.numel():
+        raise GpulzError("port byte counts exceed the port buffers")
+    _check(lib().gpulz_decode_split(_ptr(lit), lit_bytes, _ptr(lens), _ptr(offs), tok_bytes, _ptr(meta), meta_bytes,
+                                    _ptr(out), out.numel(), _ptr(out_bytes), _ptr(status), _ptr(workspace),
+                                    workspace.numel(), _stream(stream)), "gpulz_decode_split")
+
+
+def decode_split(lit, lens, offs, meta, port_bytes=None, out_capacity: int | None = None, stream=None):
+    """Decode four ports held in CUDA uint8 tensors.  port_bytes: the
+    (literals, tokens, meta) byte counts, or a uint64[4] tensor from
+    encode_split, or None for the whole tensors.  out_capacity: if None the
+    header is copied to the host once to size the output.  Returns (out,
+    out_bytes, status) like decode."""
+    import torch
+    if port_bytes is None:
+        nl, nt, nm = lit.numel(), lens.numel(), meta.numel()
+    elif hasattr(port_bytes, "cpu"):
+        v = [int(x) for x in port_bytes.cpu().tolist()]
+        nl, nt, nm = v[0], v[1], v[3]
+    else:
+        nl, nt, nm = port_bytes
+    if out_capacity is None:
+        head = meta[:32].cpu().numpy().tobytes()
+        out_capacity = int.from_bytes(head[16:24], "little") if len(head) == 32 else 0
+    dev = meta.device
+    out = torch.empty(max(out_capacity, 1), dtype=torch.uint8, device=dev)[:out_capacity]
+    out_bytes = torch.zeros(1, dtype=torch.uint64, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(decode_split_workspace_size(nm), 1), dtype=torch.uint8, device=dev)
+    decode_split_into(lit, nl, lens, offs, nt, meta, nm, out, out_bytes, status, ws, stream)
+    return out, out_bytes, status

@@ -3,6 +3,7 @@
 // workspace carving and kernel launches on the caller's stream.
 #include "gpulz.h"
 #include "gpulz_timing.h"
+#include "gpulz_split.h"
 
 #include "common.h"
 
@@ -49,6 +50,36 @@ DecLayoutHost dec_layout(uint64_t chunks_cap) {
   const uint64_t tiles = nt > 256u ? nt : 256u;
   L.tile_err = L.tile_sums + round_up(tiles * 8u);
   L.total = L.tile_err + round_up(tiles * 4u) + kAlign;
+  return L;
+}
+
+// split encode: control block | three sets of tile flags | {items, matches}
+// per chunk | one cs-byte payload slot per chunk
+struct EncSplitLayoutHost {
+  uint64_t ctl, tiles, km, staging, total;
+};
+EncSplitLayoutHost enc_split_layout(uint64_t chunks, uint32_t cs) {
+  EncSplitLayoutHost L;
+  L.ctl = 0;
+  L.tiles = round_up(encode_ctl_bytes());
+  L.km = L.tiles + round_up((3u * encode_tiles((uint32_t)chunks) + 1u) * 8u);
+  L.staging = L.km + round_up((chunks ? chunks : 1) * 8u);
+  L.total = L.staging + round_up(chunks * cs + kStagingSlack) + kAlign;
+  return L;
+}
+
+// split decode: parameters | 3 x chunk offsets in tiles | 3 x 4096 tile totals | tile errors
+constexpr uint64_t kSplitTiles = 4096;
+struct DecSplitLayoutHost {
+  uint64_t params, loc, tile_sums, tile_err, total;
+};
+DecSplitLayoutHost dec_split_layout(uint64_t chunks_cap) {
+  DecSplitLayoutHost L;
+  L.params = 0;
+  L.loc = round_up(decode_params_bytes());
+  L.tile_sums = L.loc + round_up(3u * (chunks_cap ? chunks_cap : 1) * 4u);
+  L.tile_err = L.tile_sums + round_up(3u * kSplitTiles * 8u);
+  L.total = L.tile_err + round_up(kSplitTiles * 4u) + kAlign;
   return L;
 }
 
@@ -147,6 +178,102 @@ int gpulz_decode(const void* d_in, uint64_t in_bytes, void* d_out, uint64_t out_
                  uint32_t* d_status, void* d_workspace, uint64_t workspace_bytes, hipStream_t stream) {
   return gpulz_decode_timed(d_in, in_bytes, d_out, out_capacity, d_out_bytes, d_status, d_workspace,
                             workspace_bytes, stream, nullptr, nullptr);
+}
+
+int gpulz_split_bounds(uint64_t n_bytes, uint32_t chunk_size, uint32_t word_size, uint64_t* lit_cap,
+                       uint64_t* tok_cap, uint64_t* meta_cap) {
+  if (!chunk_size_ok(chunk_size) || !word_size_ok(word_size) || !lit_cap || !tok_cap || !meta_cap)
+    return GPULZ_ERR_INVALID_ARG;
+  const uint64_t chunks = num_chunks_of(n_bytes, chunk_size);
+  *lit_cap = n_bytes;
+  *tok_cap = n_bytes / 2u + 1u;
+  *meta_cap = (uint64_t)kHeaderBytes + (uint64_t)kEntryBytes * chunks + chunks * ((chunk_size / word_size + 7u) / 8u);
+  return GPULZ_OK;
+}
+
+uint64_t gpulz_encode_split_workspace_size(uint64_t n_bytes, uint32_t chunk_size) {
+  if (!chunk_size_ok(chunk_size)) return 0;
+  return enc_split_layout(num_chunks_of(n_bytes, chunk_size), chunk_size).total;
+}
+
+int gpulz_encode_split(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, uint32_t word_size,
+                       uint32_t match_level, void* d_lit, uint64_t lit_cap, void* d_lens, void* d_offs,
+                       uint64_t tok_cap, void* d_meta, uint64_t meta_cap, uint64_t* d_port_bytes, void* d_workspace,
+                       uint64_t workspace_bytes, hipStream_t stream) {
+  if (!chunk_size_ok(chunk_size) || !word_size_ok(word_size) || match_level > 1u) return GPULZ_ERR_INVALID_ARG;
+  if ((n_bytes > 0 && (d_in == nullptr || d_lit == nullptr || d_lens == nullptr || d_offs == nullptr)) ||
+      d_meta == nullptr || d_port_bytes == nullptr || d_workspace == nullptr)
+    return GPULZ_ERR_INVALID_ARG;
+  const uint64_t chunks = num_chunks_of(n_bytes, chunk_size);
+  if (chunks > 0xFFFFFFFFull - 1024u) return GPULZ_ERR_INVALID_ARG;
+  uint64_t bl, bt, bm;
+  gpulz_split_bounds(n_bytes, chunk_size, word_size, &bl, &bt, &bm);
+  if (lit_cap < bl || tok_cap < bt || meta_cap < bm) return GPULZ_ERR_CAPACITY;
+  const EncSplitLayoutHost L = enc_split_layout(chunks, chunk_size);
+  if (workspace_bytes < L.total) return GPULZ_ERR_CAPACITY;
+  uint8_t* ws = align_up(d_workspace);
+  EncodeArgs ea;
+  ea.in = (const uint8_t*)d_in;
+  ea.n = n_bytes;
+  ea.cs = chunk_size;
+  ea.ws = word_size;
+  ea.level = match_level;
+  ea.num_chunks = (uint32_t)chunks;
+  ea.out = (uint8_t*)d_meta;
+  ea.out_bytes = nullptr;
+  ea.staging = ws + L.staging;
+  ea.tile_flags = (uint64_t*)(ws + L.tiles);
+  ea.ctl = ws + L.ctl;
+  ea.km = (uint2*)(ws + L.km);
+  ea.lit = (uint8_t*)d_lit;
+  ea.lens = (uint8_t*)d_lens;
+  ea.offs = (uint8_t*)d_offs;
+  ea.port_bytes = d_port_bytes;
+  if (launch_encode_chunks(ea, stream) != hipSuccess) return GPULZ_ERR_HIP;
+  if (launch_split_compact(ea, stream) != hipSuccess) return GPULZ_ERR_HIP;
+  return GPULZ_OK;
+}
+
+uint64_t gpulz_decode_split_workspace_size(uint64_t meta_bytes) {
+  return dec_split_layout(dec_chunks_bound(meta_bytes)).total;
+}
+
+int gpulz_decode_split(const void* d_lit, uint64_t lit_bytes, const void* d_lens, const void* d_offs,
+                       uint64_t tok_bytes, const void* d_meta, uint64_t meta_bytes, void* d_out, uint64_t out_capacity,
+                       uint64_t* d_out_bytes, uint32_t* d_status, void* d_workspace, uint64_t workspace_bytes,
+                       hipStream_t stream) {
+  if (d_meta == nullptr || d_out_bytes == nullptr || d_status == nullptr || d_workspace == nullptr)
+    return GPULZ_ERR_INVALID_ARG;
+  if ((lit_bytes > 0 && d_lit == nullptr) || (tok_bytes > 0 && (d_lens == nullptr || d_offs == nullptr)) ||
+      (out_capacity > 0 && d_out == nullptr))
+    return GPULZ_ERR_INVALID_ARG;
+  if (meta_bytes < kHeaderBytes) return GPULZ_ERR_CORRUPT;
+  uint64_t cap = dec_chunks_bound(meta_bytes);
+  const uint64_t by_out = num_chunks_of(out_capacity, 1024u);
+  if (by_out < cap) cap = by_out;
+  if (cap > 0xFFFFFFFFull) cap = 0xFFFFFFFFull;
+  const DecSplitLayoutHost L = dec_split_layout(dec_chunks_bound(meta_bytes));
+  if (workspace_bytes < L.total) return GPULZ_ERR_CAPACITY;
+  uint8_t* ws = align_up(d_workspace);
+  SplitDecodeArgs da;
+  da.meta = (const uint8_t*)d_meta;
+  da.meta_bytes = meta_bytes;
+  da.lit = (const uint8_t*)d_lit;
+  da.lit_bytes = lit_bytes;
+  da.lens = (const uint8_t*)d_lens;
+  da.offs = (const uint8_t*)d_offs;
+  da.tok_bytes = tok_bytes;
+  da.out = (uint8_t*)d_out;
+  da.out_capacity = out_capacity;
+  da.out_bytes = d_out_bytes;
+  da.status = d_status;
+  da.params = ws + L.params;
+  da.loc = (uint32_t*)(ws + L.loc);
+  da.tile_sums = (uint64_t*)(ws + L.tile_sums);
+  da.tile_err = (uint32_t*)(ws + L.tile_err);
+  da.chunks_cap = (uint32_t)cap;
+  if (launch_decode_split(da, stream) != hipSuccess) return GPULZ_ERR_HIP;
+  return GPULZ_OK;
 }
 
 int gpulz_stream_info(const void* h_prefix, uint64_t bytes, uint64_t* original_size, uint64_t* stream_bytes,

@@ -10,6 +10,7 @@ namespace gpulz {
 // ---- stream format ------------------------------------------------------
 constexpr uint32_t kMagic = 0x315A4C47u;  // "GLZ1"
 constexpr uint32_t kVersion = 1u;
+constexpr uint32_t kSplitVersion = 2u;  // split mode: four ports, meta carries the header
 constexpr uint32_t kHeaderBytes = 32u;
 constexpr uint32_t kEntryBytes = 8u;
 constexpr uint32_t kRawBit = 0x80000000u;
@@ -161,13 +162,21 @@ struct EncodeArgs {
   uint8_t* out;          // the stream
   uint64_t* out_bytes;
   uint8_t* staging;      // num_chunks * cs bytes (+ slack): one payload slot per chunk
-  uint64_t* tile_flags;  // one look-back word per compaction tile
+  uint64_t* tile_flags;  // one look-back word per compaction tile (three sets in split mode)
   void* ctl;             // error flag
+  // split mode only (km == nullptr otherwise): per-chunk {items, matches}
+  // and the ports; out is then the meta port
+  uint2* km = nullptr;
+  uint8_t* lit = nullptr;
+  uint8_t* lens = nullptr;
+  uint8_t* offs = nullptr;
+  uint64_t* port_bytes = nullptr;  // [4]: literals, lengths, offsets, meta
 };
 uint64_t encode_ctl_bytes();
 uint64_t encode_tiles(uint32_t num_chunks);
 hipError_t launch_encode_chunks(const EncodeArgs& a, hipStream_t stream);
 hipError_t launch_compact(const EncodeArgs& a, hipStream_t stream);
+hipError_t launch_split_compact(const EncodeArgs& a, hipStream_t stream);
 
 struct DecodeArgs {
   const uint8_t* in;
@@ -188,5 +197,27 @@ uint32_t decode_tile_chunks(uint32_t chunks_cap);
 uint32_t decode_num_tiles(uint32_t chunks_cap);
 uint64_t decode_params_bytes();
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Split mode: the meta port plays the stream's part (header, size table, flag
+// bitmaps); the item bytes come from the other three ports.
+struct SplitDecodeArgs {
+  const uint8_t* meta;
+  uint64_t meta_bytes;
+  const uint8_t* lit;
+  uint64_t lit_bytes;
+  const uint8_t* lens;
+  const uint8_t* offs;
+  uint64_t tok_bytes;   // bytes of each of lengths and offsets
+  uint8_t* out;
+  uint64_t out_capacity;
+  uint64_t* out_bytes;
+  uint32_t* status;
+  void* params;
+  uint32_t* loc;        // 3 x chunks_cap offsets within the scan tile: flags, literals, matches
+  uint64_t* tile_sums;  // 3 x tiles
+  uint32_t* tile_err;   // tiles
+  uint32_t chunks_cap;
+};
+hipError_t launch_decode_split(const SplitDecodeArgs& a, hipStream_t stream);
 
 }  // namespace gpulz

@@ -36,6 +36,7 @@ constexpr uint32_t kMaxTiles = 64;       // tiles wanted (one tile total per lan
 constexpr uint32_t kScanPer = 4;         // chunks per thread per scan round
 constexpr uint32_t kScanRound = kScanPer * kBlock;
 constexpr uint32_t kDecodeGrid = 8192;   // chunk-kernel workgroups at most
+constexpr uint32_t kMaxTilesAlloc = 4096; // split mode: stride of the three tile-total arrays
 static_assert(kTileMin % kScanRound == 0 && (uint64_t)kTileMax * 4096u <= (1ull << 32), "tile sizes");
 
 __device__ __forceinline__ uint32_t ld_u32_bytes(const uint8_t* p) {
@@ -253,12 +254,28 @@ __device__ __forceinline__ uint32_t small_mod(uint32_t d, uint32_t o) {
   return d - q * o;
 }
 
-// Decode one coded chunk.  pay: its payload (F flag bytes, D data bytes) in
-// the stream; lim: end of the readable input; bc: the chunk's real bytes.
-// Writes them to dst; returns false on a rule violation.
-template <uint32_t CS, uint32_t WS>
+// Split mode: where a coded chunk's items are (the GPULZStage page's
+// split-mode decode paragraph: items are read straight out of the ports, no
+// re-packing into one stream).
+struct SplitSrc {
+  const uint8_t* flags;  // its (K + 7) / 8 flag bytes, in the meta port
+  const uint8_t* lit;    // its K - M literal words
+  const uint8_t* lens;   // its M match lengths
+  const uint8_t* offs;   // its M match offsets
+  const uint8_t* meta_lim;
+  const uint8_t* lit_lim;
+  const uint8_t* lens_lim;
+  const uint8_t* offs_lim;
+  uint32_t K, M;
+};
+
+// Decode one coded chunk.  One stream: pay is its payload (F flag bytes, D
+// data bytes), lim the end of the readable input.  Split mode: sp locates
+// its items in the ports (pay, lim, F, D unused).  bc: the chunk's real
+// bytes, written to dst.  Returns false on a rule violation.
+template <uint32_t CS, uint32_t WS, bool SPLIT = false>
 __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* lim, uint32_t F, uint32_t D, uint32_t bc,
-                             uint8_t* dst, uint8_t* arena, uint32_t* sh) {
+                             uint8_t* dst, uint8_t* arena, uint32_t* sh, const SplitSrc& sp) {
   using G = Geo<CS, WS>;
   constexpr uint32_t E = G::E, TW = G::TW, TL = G::TL, J = G::J, NB = G::NB;
   TeamX<TW> tx{sh, 0u};
@@ -269,40 +286,65 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
   uint8_t* OB = PB + G::PBB;
   uint64_t* STB = (uint64_t*)(OB + E);
 
+  if constexpr (SPLIT) F = (sp.K + 7u) / 8u;
   // every live item covers at least one element: at most E items, so at most
   // (E + 7) / 8 flag bytes
   if (F > (E + 7u) / 8u) return false;
-  // ---- load the payload; clear the start bitmap and the offsets -------------------------
-  const uint32_t s0 = (4u - (F & 3u)) & 3u;  // data bytes start on a 4-byte boundary
-  {
-    // four loads per lane in flight before their LDS stores
-    const uint32_t nd = (s0 + F + D + 3u) / 4u;
+  // stage len bytes from src into PB at byte offset at (4-byte aligned), four
+  // loads per lane in flight before their LDS stores
+  auto stage = [&](uint32_t at, const uint8_t* src, uint32_t len, const uint8_t* srclim) {
+    const uint32_t nd = (len + 3u) / 4u;
 #pragma unroll 1
     for (uint32_t i0 = 0; i0 < nd; i0 += 4u * TL) {
       uint32_t v[4];
 #pragma unroll
       for (uint32_t r = 0; r < 4u; ++r) {
         const uint32_t i = i0 + g + r * TL;
-        v[r] = i < nd ? load4_unaligned(pay - s0 + 4u * i, lim) : 0u;
+        v[r] = i < nd ? load4_unaligned(src + 4u * i, srclim) : 0u;
       }
 #pragma unroll
       for (uint32_t r = 0; r < 4u; ++r) {
         const uint32_t i = i0 + g + r * TL;
-        if (i < nd) ((uint32_t*)PB)[i] = v[r];
+        if (i < nd) ((uint32_t*)(PB + at))[i] = v[r];
       }
     }
+  };
+  // ---- load the items; clear the start bitmap and the offsets -----------------------------
+  // One stream: the payload, data bytes from a 4-byte boundary.  Split mode:
+  // flags | literals | lengths | offsets, each from a 4-byte boundary (they
+  // total F + D + 9 bytes at most, with F + D < bc).
+  const uint8_t *FL, *PD, *LITB, *LENB, *OFFB;
+  const uint32_t NL = SPLIT ? sp.K - sp.M : 0u;  // split: literal words
+  if constexpr (SPLIT) {
+    const uint32_t lo = (F + 3u) & ~3u, mo = (lo + WS * NL + 3u) & ~3u, oo = (mo + sp.M + 3u) & ~3u;
+    stage(0u, sp.flags, F, sp.meta_lim);
+    stage(lo, sp.lit, WS * NL, sp.lit_lim);
+    stage(mo, sp.lens, sp.M, sp.lens_lim);
+    stage(oo, sp.offs, sp.M, sp.offs_lim);
+    FL = PB;
+    LITB = PB + lo;
+    LENB = PB + mo;
+    OFFB = PB + oo;
+    PD = PB;
+  } else {
+    const uint32_t s0 = (4u - (F & 3u)) & 3u;
+    stage(0u, pay - s0, s0 + F + D, lim);
+    FL = PB + s0;
+    PD = PB + s0 + F;
+    LITB = LENB = OFFB = PD;
+  }
+  {
 #pragma unroll
     for (uint32_t i = g; i < E / 4u; i += TL) ((uint32_t*)OB)[i] = 0u;
     if (g < NB) STB[g] = 0ull;
   }
-  const uint8_t* FL = PB + s0;      // flag bytes
-  const uint8_t* PD = PB + s0 + F;  // data bytes, 4-byte aligned
   team_sync<TW>();
 
   // ---- a. items: lane g reads items [g*R, g*R + nit) one after another --------------------
-  // An item's data offset follows from the matches before it; two team scans
+  // An item's data (one stream: its data offset; split mode: its literal or
+  // match index) follows from the matches before it; two team scans
   // (matches, then output lengths) place every item.
-  const uint32_t NI = 8u * F;
+  const uint32_t NI = SPLIT ? sp.K : 8u * F;
   const uint32_t R = (NI + TL - 1u) / TL;  // <= RMAX
   const uint32_t k0 = g * R;
   const uint32_t nit = k0 < NI ? (NI - k0 < R ? NI - k0 : R) : 0u;
@@ -316,21 +358,37 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
   }
   uint32_t mt_total;
   const uint32_t m0 = tx.scan((uint32_t)__builtin_popcount(fb), &mt_total);
-  const uint32_t tp0 = WS * (k0 - m0) + 2u * m0;
-  // item r of this lane: flag, data offset, output length (0 if unreadable)
-  auto item_len = [&](uint32_t tp, bool mt) -> uint32_t {
-    if (mt) return tp + 2u <= D ? (uint32_t)PD[tp] : 0u;
-    return tp + WS <= D ? 1u : 0u;
+  // cursor of item k: one stream, its data offset; split mode, its literal
+  // index (matches: the match index m)
+  const uint32_t c0 = SPLIT ? k0 - m0 : WS * (k0 - m0) + 2u * m0;
+  // output length of an item (0 if unreadable)
+  auto item_len = [&](uint32_t cur, uint32_t m, bool mt) -> uint32_t {
+    if constexpr (SPLIT) {
+      if (mt) return m < sp.M ? (uint32_t)LENB[m] : 0u;
+      return cur < NL ? 1u : 0u;
+    } else {
+      if (mt) return cur + 2u <= D ? (uint32_t)PD[cur] : 0u;
+      return cur + WS <= D ? 1u : 0u;
+    }
+  };
+  auto advance = [&](uint32_t& cur, uint32_t& m, bool mt) {
+    if constexpr (SPLIT) {
+      if (mt) ++m;
+      else ++cur;
+    } else {
+      cur += mt ? 2u : WS;
+      m += mt ? 1u : 0u;
+    }
   };
   uint32_t sum = 0;
   {
-    uint32_t tp = tp0;
+    uint32_t cur = c0, m = m0;
 #pragma unroll 4
     for (uint32_t r = 0; r < G::RMAX; ++r) {
       if (r < nit) {
         const bool mt = (fb >> r) & 1u;
-        sum += item_len(tp, mt);
-        tp += mt ? 2u : WS;
+        sum += item_len(cur, m, mt);
+        advance(cur, m, mt);
       }
     }
   }
@@ -338,49 +396,56 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
   uint32_t op = tx.scan(sum, &len_total);
   uint32_t K = 0, MK = 0, bad = 0, ends = 0;
   {
-    uint32_t tp = tp0;
+    uint32_t cur = c0, m = m0;
 #pragma unroll 4
     for (uint32_t r = 0; r < G::RMAX; ++r) {
       if (r < nit) {
         const bool mt = (fb >> r) & 1u;
-        const uint32_t len = item_len(tp, mt);
+        const uint32_t len = item_len(cur, m, mt);
         if (op < E) {  // live: starts before the chunk's end
           ++K;
           if (len == 0u) {
             bad = 1u;  // unreadable, or a zero-length match
           } else if (mt) {
             ++MK;
-            const uint32_t O = PD[tp + 1u];
+            const uint32_t O = SPLIT ? OFFB[m] : PD[cur + 1u];
             if (O == 0u || O > op || op + len > E) bad = 1u;
             else OB[op] = (uint8_t)O;
           } else {
-            uint32_t v;
+            const uint8_t* w = SPLIT ? LITB + WS * cur : PD + cur;  // 2-byte aligned for WS >= 2
             if constexpr (WS == 4) {
-              v = (uint32_t)*(const uint16_t*)(PD + tp) | ((uint32_t)*(const uint16_t*)(PD + tp + 2u) << 16);
-              *(uint32_t*)(VAL + 4u * op) = v;
+              *(uint32_t*)(VAL + 4u * op) =
+                  (uint32_t)*(const uint16_t*)w | ((uint32_t)*(const uint16_t*)(w + 2u) << 16);
             } else if constexpr (WS == 2) {
-              *(uint16_t*)(VAL + 2u * op) = *(const uint16_t*)(PD + tp);
+              *(uint16_t*)(VAL + 2u * op) = *(const uint16_t*)w;
             } else {
-              VAL[op] = PD[tp];
+              VAL[op] = *w;
             }
           }
           if (len != 0u) atomicOr((unsigned long long*)&STB[op >> 6], 1ull << (op & 63u));
           if (op + len == E) ends = 1u;
         }
         op += len;
-        tp += mt ? 2u : WS;
+        advance(cur, m, mt);
       }
     }
   }
-  // the live items must cover exactly E elements, use exactly D data bytes
-  // and leave no match flag set after the last of them
   {
     // K, MK <= 4103 items and bad, ends <= 256 lanes: two 16-bit fields each
     const uint32_t r0 = tx.sum(K | (MK << 16));
     const uint32_t r1 = tx.sum(bad | (ends << 16));
     const uint32_t Kt = r0 & 0xFFFFu, MKt = r0 >> 16, badt = r1 & 0xFFFFu, endst = r1 >> 16;
-    if (badt || endst != 1u || (Kt + 7u) / 8u != F || WS * (Kt - MKt) + 2u * MKt != D || MKt != mt_total)
-      return false;
+    if constexpr (SPLIT) {
+      // all K items are live and cover exactly E elements, M of them are
+      // matches, and the flag bits past the last item are 0
+      const bool pad = (sp.K & 7u) != 0u && (FL[F - 1u] >> (sp.K & 7u)) != 0u;
+      if (badt || endst != 1u || Kt != sp.K || MKt != sp.M || mt_total != sp.M || pad) return false;
+    } else {
+      // the live items cover exactly E elements, use exactly D data bytes and
+      // leave no match flag set after the last of them
+      if (badt || endst != 1u || (Kt + 7u) / 8u != F || WS * (Kt - MKt) + 2u * MKt != D || MKt != mt_total)
+        return false;
+    }
   }
   team_sync<TW>();
 
@@ -573,7 +638,7 @@ __device__ __forceinline__ void decode_group(const DecP& p, const uint8_t* in, c
         }
       }
     } else {
-      if (!decode_coded<CS, WS>(pay, lim, e.x, e.y, bc, dst, arena, sh) && g == 0)
+      if (!decode_coded<CS, WS>(pay, lim, e.x, e.y, bc, dst, arena, sh, SplitSrc{}) && g == 0)
         raise_status(status, out_bytes, kStatusCorrupt);
     }
     team_sync<G::TW>();
@@ -620,6 +685,204 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(7))) voi
   else decode_by_ws<4096>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh);
 }
 
+// ---- split mode ------------------------------------------------------------------
+// The three per-chunk sizes of a split-mode entry {items K, matches M}: flag
+// bytes, literal bytes (a raw chunk's bytes too) and matches.  False if the
+// entry breaks a rule (zero: (0,0); raw: (0, bit 31 | real bytes); coded:
+// 1 <= K <= E, M <= K, and its one-stream form smaller than the chunk).
+__device__ __forceinline__ bool split_sizes(uint2 e, uint32_t bc, uint32_t cs, uint32_t ws, uint32_t* f,
+                                            uint32_t* l, uint32_t* m) {
+  *f = *l = *m = 0;
+  if (e.x == 0u) {
+    if (e.y == 0u) return true;
+    if ((e.y & kRawBit) && (e.y & ~kRawBit) == bc) {
+      *l = bc;
+      return true;
+    }
+    return false;
+  }
+  const uint32_t K = e.x, M = e.y, E = cs / ws;
+  if (K > E || M > K) return false;
+  const uint32_t F = (K + 7u) / 8u;
+  if ((uint64_t)F + (uint64_t)ws * (K - M) + 2ull * M >= bc) return false;
+  *f = F;
+  *l = ws * (K - M);
+  *m = M;
+  return true;
+}
+
+// Header and entry checks of a split stream, per tile of T chunks: each
+// chunk's three offsets within its tile, the tile's three totals.
+__global__ __launch_bounds__(kBlock) void split_scan_kernel(const uint8_t* __restrict__ meta, uint64_t meta_bytes,
+                                                            uint64_t out_capacity, uint32_t chunks_cap, uint32_t T,
+                                                            DecP* __restrict__ P, uint32_t* __restrict__ loc,
+                                                            uint64_t* __restrict__ tile_sum,
+                                                            uint32_t* __restrict__ tile_err,
+                                                            uint32_t* __restrict__ status,
+                                                            uint64_t* __restrict__ out_bytes) {
+  __shared__ uint64_t sh[kWaves];
+  const uint32_t magic = ld_u32_bytes(meta);
+  const uint32_t ver = meta[4], ws = meta[5], res = meta[6] | ((uint32_t)meta[7] << 8);
+  const uint32_t cs = ld_u32_bytes(meta + 8), nc = ld_u32_bytes(meta + 12);
+  const uint64_t n = ld_u64_bytes(meta + 16), nflag = ld_u64_bytes(meta + 24);
+  uint32_t st = kStatusOk;
+  if (magic != kMagic || ver != kSplitVersion || res != 0 || !word_size_ok(ws) || !chunk_size_ok(cs)) {
+    st = kStatusCorrupt;
+  } else {
+    const uint64_t want = n / cs + ((n % cs) != 0);
+    const uint64_t table_end = (uint64_t)kHeaderBytes + (uint64_t)kEntryBytes * nc;
+    if (want != nc || table_end > meta_bytes || nflag > meta_bytes - table_end) st = kStatusCorrupt;
+    else if (n > out_capacity) st = kStatusCapacity;
+    else if (nc > chunks_cap) st = kStatusCorrupt;
+  }
+  const uint32_t ntiles = (nc + T - 1u) / T;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    P->n = n;
+    P->pb = nflag;
+    P->base = (uint64_t)kHeaderBytes + (uint64_t)kEntryBytes * nc;
+    P->cs = cs;
+    P->ws = ws;
+    P->nc = nc;
+    P->status = st;
+    P->T = T;
+    P->ntiles = ntiles;
+    *status = st;
+    *out_bytes = st == kStatusOk ? n : 0u;
+  }
+  if (st != kStatusOk || blockIdx.x >= ntiles) return;
+  const uint64_t t0 = (uint64_t)blockIdx.x * T;
+  const uint64_t t1 = (t0 + T) < nc ? (t0 + T) : nc;
+  uint64_t carry[3] = {0, 0, 0};
+  bool bad = false;
+  for (uint64_t r0 = t0; r0 < t1; r0 += kScanRound) {
+    const uint64_t c0 = r0 + (uint64_t)threadIdx.x * kScanPer;
+    uint32_t sz[3][kScanPer];
+    uint64_t local[3] = {0, 0, 0};
+#pragma unroll
+    for (uint32_t j = 0; j < kScanPer; ++j) {
+      const uint64_t c = c0 + j;
+      sz[0][j] = sz[1][j] = sz[2][j] = 0;
+      if (c < t1) {
+        const uint2 e = read_row(meta, c);
+        const uint64_t start = c * cs;
+        const uint32_t bc = (uint32_t)((n - start) < cs ? (n - start) : cs);
+        if (!split_sizes(e, bc, cs, ws, &sz[0][j], &sz[1][j], &sz[2][j])) bad = true;
+      }
+#pragma unroll
+      for (uint32_t q = 0; q < 3u; ++q) local[q] += sz[q][j];
+    }
+#pragma unroll
+    for (uint32_t q = 0; q < 3u; ++q) {
+      uint64_t tot;
+      uint64_t off = carry[q] + block_exclusive_scan(local[q], &tot, sh);
+#pragma unroll
+      for (uint32_t j = 0; j < kScanPer; ++j) {
+        const uint64_t c = c0 + j;
+        if (c < t1) loc[(uint64_t)q * chunks_cap + c] = (uint32_t)off;  // < 2^32 by the tile sizing
+        off += sz[q][j];
+      }
+      carry[q] += tot;
+    }
+  }
+  const bool anybad = __syncthreads_or(bad);
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (uint32_t q = 0; q < 3u; ++q) tile_sum[(uint64_t)q * kMaxTilesAlloc + blockIdx.x] = carry[q];
+    tile_err[blockIdx.x] = anybad ? 1u : 0u;
+  }
+}
+
+template <uint32_t CS, uint32_t WS>
+__device__ __forceinline__ void decode_group_split(const DecP& p, const SplitDecodeArgs& a, const uint32_t* loc,
+                                                   const uint64_t* tile_sum, uint8_t* arena_all, uint32_t* sh) {
+  using G = Geo<CS, WS>;
+  constexpr uint32_t TL = G::TL;
+  constexpr uint32_t CPW = kWaves / G::TW;  // chunks per workgroup
+  const uint32_t team = threadIdx.x / TL, g = threadIdx.x % TL, lane = lane_id();
+  uint8_t* arena = arena_all + team * (G::TW * kSlot);
+  const uint8_t* flags = a.meta + p.base;
+  const uint8_t* meta_lim = a.meta + a.meta_bytes;
+  const uint64_t stride = (uint64_t)gridDim.x * CPW;
+  for (uint64_t c = (uint64_t)blockIdx.x * CPW + team; c < p.nc; c += stride) {
+    const uint2 e = read_row(a.meta, c);
+    const uint64_t start = c * CS;
+    const uint32_t bc = (uint32_t)((p.n - start) < CS ? (p.n - start) : CS);
+    uint32_t fz, lz, mz;
+    if (!split_sizes(e, bc, CS, WS, &fz, &lz, &mz)) continue;  // reported by the scan kernel
+    // offsets: earlier tiles' totals + offsets within the tile, for each port
+    const uint32_t t = (uint32_t)(c / p.T);
+    uint64_t pre[3];
+#pragma unroll
+    for (uint32_t q = 0; q < 3u; ++q) {
+      uint64_t s = 0;
+      for (uint32_t i = lane; i < t; i += 64u) s += tile_sum[(uint64_t)q * kMaxTilesAlloc + i];
+      pre[q] = lane63_64(wave_incl_add64(s)) + loc[(uint64_t)q * a.chunks_cap + c];
+    }
+    // sizes inconsistent with the ports: reported by workgroup 0 below
+    if (pre[0] + fz > p.pb || pre[1] + lz > a.lit_bytes || pre[2] + mz > a.tok_bytes) continue;
+    uint8_t* dst = a.out + start;
+    if (e.x == 0u) {
+      const bool zero = e.y == 0u;
+      const bool al = (((uintptr_t)dst) & 3u) == 0;
+      const uint8_t* src = a.lit + pre[1];
+      const uint8_t* lim = a.lit + a.lit_bytes;
+      const uint32_t nw = (bc + 3u) / 4u;
+      for (uint32_t i = g; i < nw; i += TL) {
+        const uint32_t v = zero ? 0u : load4_unaligned(src + 4u * i, lim);
+        if (al && 4u * i + 4u <= bc) {
+          *(uint32_t*)(dst + 4u * i) = v;
+        } else {
+          for (uint32_t b = 0; b < 4u; ++b)
+            if (4u * i + b < bc) dst[4u * i + b] = (uint8_t)(v >> (8u * b));
+        }
+      }
+    } else {
+      const SplitSrc sp{flags + pre[0], a.lit + pre[1], a.lens + pre[2], a.offs + pre[2], meta_lim,
+                        a.lit + a.lit_bytes, a.lens + a.tok_bytes, a.offs + a.tok_bytes, e.x, e.y};
+      if (!decode_coded<CS, WS, true>(nullptr, nullptr, 0u, 0u, bc, dst, arena, sh, sp) && g == 0)
+        raise_status(a.status, a.out_bytes, kStatusCorrupt);
+    }
+    team_sync<G::TW>();
+  }
+}
+
+template <uint32_t CS>
+__device__ __forceinline__ void decode_split_by_ws(const DecP& p, const SplitDecodeArgs& a, const uint32_t* loc,
+                                                   const uint64_t* tile_sum, uint8_t* arena, uint32_t* sh) {
+  if (p.ws == 4u) decode_group_split<CS, 4>(p, a, loc, tile_sum, arena, sh);
+  else if (p.ws == 2u) decode_group_split<CS, 2>(p, a, loc, tile_sum, arena, sh);
+  else decode_group_split<CS, 1>(p, a, loc, tile_sum, arena, sh);
+}
+
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(7))) void split_chunks_kernel(
+    SplitDecodeArgs a, const DecP* __restrict__ P) {
+  __shared__ __attribute__((aligned(16))) uint8_t arena[kArena];
+  __shared__ uint32_t sh[2 * kWaves];
+  const DecP p = *P;
+  if (p.status != kStatusOk) return;
+  if (blockIdx.x == 0 && threadIdx.x < 64u) {
+    // port-wide checks: the flag totals must add up to the header's, the
+    // other ports must hold what the entries say, no entry may be invalid
+    uint64_t s0 = 0, s1 = 0, s2 = 0;
+    uint32_t err = 0;
+    for (uint32_t i = lane_id(); i < p.ntiles; i += 64u) {
+      s0 += a.tile_sums[i];
+      s1 += a.tile_sums[kMaxTilesAlloc + i];
+      s2 += a.tile_sums[2u * kMaxTilesAlloc + i];
+      err |= a.tile_err[i];
+    }
+    s0 = lane63_64(wave_incl_add64(s0));
+    s1 = lane63_64(wave_incl_add64(s1));
+    s2 = lane63_64(wave_incl_add64(s2));
+    err = lane63(wave_incl_add(err));
+    if (lane_id() == 0 && (s0 != p.pb || s1 > a.lit_bytes || s2 > a.tok_bytes || err))
+      raise_status(a.status, a.out_bytes, kStatusCorrupt);
+  }
+  if (p.cs == 1024u) decode_split_by_ws<1024>(p, a, a.loc, a.tile_sums, arena, sh);
+  else if (p.cs == 2048u) decode_split_by_ws<2048>(p, a, a.loc, a.tile_sums, arena, sh);
+  else decode_split_by_ws<4096>(p, a, a.loc, a.tile_sums, arena, sh);
+}
+
 }  // namespace
 
 uint32_t decode_tile_chunks(uint32_t chunks_cap) {
@@ -634,6 +897,20 @@ uint32_t decode_num_tiles(uint32_t chunks_cap) {
   return chunks_cap ? (uint32_t)(((uint64_t)chunks_cap + T - 1u) / T) : 1u;
 }
 uint64_t decode_params_bytes() { return sizeof(DecP); }
+
+hipError_t launch_decode_split(const SplitDecodeArgs& a, hipStream_t stream) {
+  const uint32_t T = decode_tile_chunks(a.chunks_cap);
+  const uint32_t tiles = decode_num_tiles(a.chunks_cap);
+  if (tiles > kMaxTilesAlloc) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(split_scan_kernel, dim3(tiles), dim3(kBlock), 0, stream, a.meta, a.meta_bytes, a.out_capacity,
+                     a.chunks_cap, T, (DecP*)a.params, a.loc, a.tile_sums, a.tile_err, a.status, a.out_bytes);
+  if (a.chunks_cap > 0) {
+    uint32_t grid = (a.chunks_cap + kWaves - 1u) / kWaves;
+    if (grid > kDecodeGrid) grid = kDecodeGrid;
+    hipLaunchKernelGGL(split_chunks_kernel, dim3(grid), dim3(kBlock), 0, stream, a, (const DecP*)a.params);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const uint32_t T = decode_tile_chunks(a.chunks_cap);

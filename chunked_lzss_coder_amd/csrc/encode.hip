@@ -194,7 +194,8 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
                                                                  uint32_t num_chunks, uint8_t* __restrict__ out,
                                                                  uint8_t* __restrict__ staging,
                                                                  uint64_t* __restrict__ tile_flags,
-                                                                 uint32_t num_tiles, EncCtl* __restrict__ ctl) {
+                                                                 uint32_t num_tiles, uint32_t flag_sets,
+                                                                 uint2* __restrict__ km, EncCtl* __restrict__ ctl) {
   using L = Lay<WS, E, LEVEL>;
   constexpr uint32_t CS = L::CS;
   constexpr uint32_t TL = 64u * WPC;  // lanes per team
@@ -629,9 +630,14 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
       put_le(row, ent.x, 4);
       put_le(row + 4, ent.y, 4);
     }
-    // the first team of workgroup b clears the compaction kernel's tile flag b
-    // (there are never more tiles than workgroups), workgroup 0 the error flag
-    if (team == 0 && blockIdx.x < num_tiles) tile_flags[blockIdx.x] = 0ull;
+    // items and matches of the chunk, for the split-mode assembly (coded
+    // chunks; zero and raw chunks report none)
+    if (km) km[c] = (nonzero && !raw) ? make_uint2(K, M) : make_uint2(0u, 0u);
+    // the first team of workgroup b clears tile flag b of every flag set of
+    // the assembly kernel (there are never more tiles than workgroups),
+    // workgroup 0 the error flag
+    if (team == 0 && blockIdx.x < num_tiles)
+      for (uint32_t k = 0; k < flag_sets; ++k) tile_flags[(uint64_t)k * num_tiles + blockIdx.x] = 0ull;
     if (team == 0 && blockIdx.x == 0) ctl->error = 0u;
   }
 }
@@ -765,6 +771,174 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(const uint8_t* __restri
   }
 }
 
+// Copy n bytes from a 4-byte-aligned source to any destination with one
+// wave: single bytes up to dst's next 4-byte boundary, then aligned dwords
+// realigned from two source dwords, then single bytes.  Reads may run up to
+// 3 bytes past src + n (inside the staging area and its slack).
+__device__ __forceinline__ void wave_copy_to(uint8_t* dst, const uint8_t* src, uint32_t n) {
+  const uint32_t lane = lane_id();
+  const uint32_t a4 = (uint32_t)((4u - ((uintptr_t)dst & 3u)) & 3u);
+  const uint32_t h = a4 > n ? n : a4;
+  if (lane < h) dst[lane] = src[lane];
+  const uint32_t nb = (n - h) / 4u;
+  const uint32_t* sw = (const uint32_t*)src;
+  uint32_t* dw = (uint32_t*)(dst + h);
+  for (uint32_t k = lane; k < nb; k += 64u) {
+    const uint32_t lo = sw[k];
+    const uint32_t hi = h ? sw[k + 1u] : 0u;
+    dw[k] = __builtin_amdgcn_alignbyte(hi, lo, h);
+  }
+  const uint32_t t0 = h + 4u * nb;
+  if (t0 + lane < n) dst[t0 + lane] = src[t0 + lane];
+}
+
+// Split-mode assembly (codebase notes CN-GPULZ-1, split mode; GPULZStage page,
+// split-mode paragraphs): one workgroup per tile of kCTile chunks.  A chunk
+// contributes flag bytes to the meta port, literal bytes (its literal words,
+// or all its bytes when raw) to the literals port and one byte per match to
+// each of the lengths and offsets ports; three scans with decoupled look-back
+// (one flag set each) place them.  Coded chunks' rows become {items,
+// matches}; then every wave deals its chunks' items from the staging slots
+// into the ports.  The last tile writes the header and the port lengths.
+__global__ __launch_bounds__(kBlock) void split_compact_kernel(
+    const uint8_t* __restrict__ staging, const uint2* __restrict__ km, uint32_t cs, uint32_t ws, uint64_t n,
+    uint32_t num_chunks, uint32_t num_tiles, uint8_t* __restrict__ meta, uint8_t* __restrict__ lit,
+    uint8_t* __restrict__ lens, uint8_t* __restrict__ offs, uint64_t* __restrict__ port_bytes,
+    uint64_t* __restrict__ tile_flags, EncCtl* __restrict__ ctl) {
+  __shared__ uint32_t s_kind[kCTile], s_f[kCTile], s_k[kCTile], s_m[kCTile], s_lb[kCTile];
+  __shared__ uint32_t s_fo[kCTile], s_lo[kCTile], s_mo[kCTile];
+  __shared__ uint64_t s_pre[3];
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  uint8_t* table = meta + kHeaderBytes;
+  uint8_t* mflags = table + (uint64_t)kEntryBytes * num_chunks;
+  auto header = [&](uint64_t nflag) {
+    put_le(meta + 0, kMagic, 4);
+    meta[4] = (uint8_t)kSplitVersion;
+    meta[5] = (uint8_t)ws;
+    meta[6] = 0;
+    meta[7] = 0;
+    put_le(meta + 8, cs, 4);
+    put_le(meta + 12, num_chunks, 4);
+    put_le(meta + 16, n, 8);
+    put_le(meta + 24, nflag, 8);
+  };
+  if (num_chunks == 0) {
+    if (tid == 0) {
+      header(0);
+      port_bytes[0] = port_bytes[1] = port_bytes[2] = 0;
+      port_bytes[3] = kHeaderBytes;
+    }
+    return;
+  }
+  const uint32_t t = blockIdx.x;
+  const uint64_t c0 = (uint64_t)t * kCTile;
+  const uint32_t E = cs / ws;
+  if (wave == 0) {
+    static_assert(kCTile == 64, "one chunk per lane of the first wave");
+    const uint64_t c = c0 + lane;
+    uint32_t kind = 0, f = 0, K = 0, M = 0, lb = 0;  // kind: 0 zero / none, 1 raw, 2 coded
+    uint8_t* row = table + kEntryBytes * c;
+    const bool al = (((uintptr_t)table) & 7u) == 0;
+    if (c < num_chunks) {
+      uint2 e;
+      if (al) {
+        e = *(const uint2*)row;
+      } else {
+        e.x = (uint32_t)row[0] | ((uint32_t)row[1] << 8) | ((uint32_t)row[2] << 16) | ((uint32_t)row[3] << 24);
+        e.y = (uint32_t)row[4] | ((uint32_t)row[5] << 8) | ((uint32_t)row[6] << 16) | ((uint32_t)row[7] << 24);
+      }
+      const uint64_t start = c * cs;
+      const uint32_t bc = (uint32_t)((n - start) < cs ? (n - start) : cs);
+      // sizes never exceed the chunk's, so every write stays inside the ports
+      // even if a row were wrong
+      if (e.x != 0u) {
+        const uint2 q = km[c];
+        kind = 2;
+        K = q.x < E ? q.x : E;
+        M = q.y < K ? q.y : K;
+        f = (K + 7u) / 8u;
+        lb = ws * (K - M);
+      } else if (e.y & kRawBit) {
+        kind = 1;
+        lb = bc;
+      }
+    }
+    const uint32_t incf = wave_incl_add(f), incl = wave_incl_add(lb), incm = wave_incl_add(M);
+    s_kind[lane] = kind;
+    s_f[lane] = f;
+    s_k[lane] = K;
+    s_m[lane] = M;
+    s_lb[lane] = lb;
+    s_fo[lane] = incf - f;
+    s_lo[lane] = incl - lb;
+    s_mo[lane] = incm - M;
+    const uint64_t tf = lane63(incf), tl = lane63(incl), tm = lane63(incm);
+    const uint64_t pf = look_back(tile_flags, t, tf, &ctl->error);
+    const uint64_t pl = look_back(tile_flags + num_tiles, t, tl, &ctl->error);
+    const uint64_t pm = look_back(tile_flags + 2u * (uint64_t)num_tiles, t, tm, &ctl->error);
+    if (kind == 2) {  // the row of a coded chunk becomes {items, matches}
+      if (al) {
+        *(uint2*)row = make_uint2(K, M);
+      } else {
+        put_le(row, K, 4);
+        put_le(row + 4, M, 4);
+      }
+    }
+    if (lane == 0) {
+      s_pre[0] = pf;
+      s_pre[1] = pl;
+      s_pre[2] = pm;
+      if (t == num_tiles - 1u) {
+        const uint64_t nf = pf + tf;
+        header(nf);
+        const bool err = __hip_atomic_load(&ctl->error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+        port_bytes[0] = err ? 0ull : pl + tl;
+        port_bytes[1] = err ? 0ull : pm + tm;
+        port_bytes[2] = err ? 0ull : pm + tm;
+        port_bytes[3] = err ? 0ull : (uint64_t)kHeaderBytes + (uint64_t)kEntryBytes * num_chunks + nf;
+      }
+    }
+  }
+  __syncthreads();
+  const uint64_t pf = s_pre[0], pl = s_pre[1], pm = s_pre[2];
+  constexpr uint32_t PW = kCTile / kWaves;
+  for (uint32_t u = 0; u < PW; ++u) {
+    const uint32_t j = wave * PW + u;
+    const uint64_t c = c0 + j;
+    if (c >= num_chunks) break;
+    const uint32_t kind = s_kind[j];
+    const uint8_t* src = staging + c * cs;
+    if (kind == 1u) {
+      wave_copy_to(lit + pl + s_lo[j], src, s_lb[j]);
+    } else if (kind == 2u) {
+      const uint32_t F = s_f[j], K = s_k[j];
+      wave_copy_to(mflags + pf + s_fo[j], src, F);
+      const uint8_t* data = src + F;
+      uint8_t* L = lit + pl + s_lo[j];
+      uint8_t* LN = lens + pm + s_mo[j];
+      uint8_t* OF = offs + pm + s_mo[j];
+      uint32_t mg = 0;  // matches before this group of 64 items
+      for (uint32_t k0 = 0; k0 < K; k0 += 64u) {
+        const uint32_t k = k0 + lane;
+        const bool live = k < K;
+        const bool mt = live && ((src[k >> 3] >> (k & 7u)) & 1u);
+        const uint64_t mw = __ballot(mt);
+        const uint32_t mb = mg + mbcnt64(mw);  // matches before item k
+        if (live) {
+          const uint32_t tp = ws * (k - mb) + 2u * mb;  // item k's data offset
+          if (mt) {
+            LN[mb] = data[tp];
+            OF[mb] = data[tp + 1u];
+          } else {
+            for (uint32_t b = 0; b < ws; ++b) L[ws * (k - mb) + b] = data[tp + b];
+          }
+        }
+        mg += (uint32_t)__builtin_popcountll(mw);
+      }
+    }
+  }
+}
+
 template <int WS, int E, int LEVEL>
 hipError_t launch_one(const EncodeArgs& a, hipStream_t stream) {
   // waves per chunk: one up to 512 elements (two chunks per workgroup), then
@@ -774,7 +948,8 @@ hipError_t launch_one(const EncodeArgs& a, hipStream_t stream) {
   constexpr uint32_t threads = 64u * WPC * CPW;
   const uint32_t grid = (a.num_chunks + CPW - 1) / CPW;  // one chunk per team
   hipLaunchKernelGGL((encode_kernel<WS, E, LEVEL, WPC, CPW>), dim3(grid), dim3(threads), 0, stream, a.in, a.n,
-                     a.num_chunks, a.out, a.staging, a.tile_flags, num_tiles_of(a.num_chunks), (EncCtl*)a.ctl);
+                     a.num_chunks, a.out, a.staging, a.tile_flags, num_tiles_of(a.num_chunks),
+                     a.km ? 3u : 1u, a.km, (EncCtl*)a.ctl);
   return hipGetLastError();
 }
 
@@ -792,6 +967,14 @@ hipError_t launch_compact(const EncodeArgs& a, hipStream_t stream) {
   const uint32_t tiles = num_tiles_of(a.num_chunks);
   hipLaunchKernelGGL(compact_kernel, dim3(tiles ? tiles : 1u), dim3(kBlock), 0, stream, a.staging, a.cs, a.ws, a.n,
                      a.num_chunks, tiles, a.out, a.out_bytes, a.tile_flags, (EncCtl*)a.ctl);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_compact(const EncodeArgs& a, hipStream_t stream) {
+  const uint32_t tiles = num_tiles_of(a.num_chunks);
+  hipLaunchKernelGGL(split_compact_kernel, dim3(tiles ? tiles : 1u), dim3(kBlock), 0, stream, a.staging,
+                     (const uint2*)a.km, a.cs, a.ws, a.n, a.num_chunks, tiles, a.out, a.lit, a.lens, a.offs,
+                     a.port_bytes, a.tile_flags, (EncCtl*)a.ctl);
   return hipGetLastError();
 }
 

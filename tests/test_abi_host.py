@@ -32,7 +32,10 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted(["gpulz_decode", "gpulz_decode_workspace_size", "gpulz_encode",
                                          "gpulz_encode_workspace_size", "gpulz_max_compressed_size",
-                                         "gpulz_stream_info", "gpulz_encode_timed", "gpulz_decode_timed"])
+                                         "gpulz_stream_info", "gpulz_encode_timed", "gpulz_decode_timed",
+                                         "gpulz_split_bounds", "gpulz_encode_split_workspace_size",
+                                         "gpulz_encode_split", "gpulz_decode_split_workspace_size",
+                                         "gpulz_decode_split"])
 
 
 def test_library_exports_every_declared_symbol(g):
@@ -117,3 +120,39 @@ def test_product_package_does_not_import_the_oracle():
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in txt and "from oracle" not in txt, f
                 assert "gpulz_oracle" not in txt and "liboracle" not in txt, f
+
+
+@pytest.mark.parametrize("cs,ws", [(1024, 1), (2048, 4), (4096, 2)])
+def test_split_bounds_match_the_oracle(g, oracle_mod, cs, ws):
+    for n in [0, 1, cs, 3 * cs + 5, 26_214_400]:
+        assert g.split_bounds(n, cs, ws) == oracle_mod.split_bounds(n, cs, ws)
+    with pytest.raises(g.GpulzError):
+        g.split_bounds(10, 3000, 4)
+
+
+def test_split_rejects_bad_arguments_before_launch(g):
+    p = ctypes.c_void_p(0x1000)
+    big = 1 << 40
+    enc = g.lib().gpulz_encode_split
+    bl, bt, bm = g.split_bounds(100, 2048, 4)
+    wsn = g.encode_split_workspace_size(100, 2048)
+    args = [p, 100, 2048, 4, 0, p, bl, p, p, bt, p, bm, p, p, wsn, None]
+    for i, bad in [(2, 3000), (3, 3), (4, 2), (0, None), (5, None), (7, None), (8, None), (10, None), (12, None),
+                   (13, None)]:
+        a = list(args); a[i] = bad
+        assert enc(*a) == g.ERR_INVALID_ARG, i
+    for i in (6, 9, 11, 14):
+        a = list(args); a[i] = args[i] - 1
+        assert enc(*a) == g.ERR_CAPACITY, i
+    dec = g.lib().gpulz_decode_split
+    need = g.decode_split_workspace_size(1000)
+    dargs = [p, 10, p, p, 10, p, 1000, p, big, p, p, p, need, None]
+    for i in (5, 9, 10, 11):
+        a = list(dargs); a[i] = None
+        assert dec(*a) == g.ERR_INVALID_ARG, i
+    a = list(dargs); a[0] = None
+    assert dec(*a) == g.ERR_INVALID_ARG
+    a = list(dargs); a[6] = 31
+    assert dec(*a) == g.ERR_CORRUPT
+    a = list(dargs); a[12] = need - 1
+    assert dec(*a) == g.ERR_CAPACITY
