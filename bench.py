@@ -172,6 +172,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (the HBM-counter reference)")
+    ap.add_argument("--no-split", action="store_true", help="skip the split-mode (four ports) measurement")
     ap.add_argument("--flush-reps", type=int, default=11,
                     help="repetitions of the flushed-cache and host-latency measurements (0: skip)")
     args = ap.parse_args(argv)
@@ -328,6 +329,50 @@ def main(argv=None) -> int:
             res[lv]["host_latency_ms_median"] = {"encode": round(float(np.median(he)), 4),
                                                  "decode": round(float(np.median(hd)), 4)}
         del flush
+    # Split mode (four ports) at the first level: whole-call encode and decode
+    # times with the same inputs, and the port sizes.
+    split = None
+    if not args.no_split:
+        lv = levels[0]
+        bl, bt, bm = g.split_bounds(n, cs, ws)
+        p_lit = torch.empty(max(bl, 1), dtype=torch.uint8, device=dev)
+        p_len = torch.empty(max(bt, 1), dtype=torch.uint8, device=dev)
+        p_off = torch.empty(max(bt, 1), dtype=torch.uint8, device=dev)
+        p_meta = torch.empty(max(bm, 1), dtype=torch.uint8, device=dev)
+        p_bytes = torch.zeros(4, dtype=torch.uint64, device=dev)
+        s_ews = torch.empty(g.encode_split_workspace_size(n, cs), dtype=torch.uint8, device=dev)
+        g.encode_split_into(x, cs, ws, lv, p_lit, p_len, p_off, p_meta, p_bytes, s_ews)
+        torch.cuda.synchronize()
+        pbv = [int(v) for v in p_bytes.cpu().tolist()]
+        s_dws = torch.empty(g.decode_split_workspace_size(pbv[3]), dtype=torch.uint8, device=dev)
+        dout, dnb, st = bufs[lv][3], bufs[lv][4], bufs[lv][5]
+        g.decode_split_into(p_lit, pbv[0], p_len, p_off, pbv[1], p_meta, pbv[3], dout, dnb, st, s_dws)
+        torch.cuda.synchronize()
+        if int(st.item()) != 0 or not torch.equal(dout[:n], x):
+            print("bench.py: split-mode round trip failed", file=sys.stderr)
+            return 1
+        s_ = torch.cuda.current_stream()
+        se, sd = [], []
+        for i in range(args.warmup + args.steps):
+            ce, cd = ev.pair(), ev.pair()
+            ev.hip.hipEventRecord(ce[0], ctypes.c_void_p(s_.cuda_stream))
+            g.encode_split_into(x, cs, ws, lv, p_lit, p_len, p_off, p_meta, p_bytes, s_ews)
+            ev.hip.hipEventRecord(ce[1], ctypes.c_void_p(s_.cuda_stream))
+            ev.hip.hipEventRecord(cd[0], ctypes.c_void_p(s_.cuda_stream))
+            g.decode_split_into(p_lit, pbv[0], p_len, p_off, pbv[1], p_meta, pbv[3], dout, dnb, st, s_dws)
+            ev.hip.hipEventRecord(cd[1], ctypes.c_void_p(s_.cuda_stream))
+            if i >= args.warmup:
+                se.append(ce)
+                sd.append(cd)
+        torch.cuda.synchronize()
+        me = float(np.mean([ev.ms(p) for p in se]))
+        md = float(np.mean([ev.ms(p) for p in sd]))
+        split = {"level": lv, "encode_gbps": round(n / (me * 1e-3) / 1e9, 3),
+                 "decode_gbps": round(n / (md * 1e-3) / 1e9, 3), "encode_ms": round(me, 4),
+                 "decode_ms": round(md, 4),
+                 "port_bytes": {"literals": pbv[0], "lengths": pbv[1], "offsets": pbv[2], "meta": pbv[3]},
+                 "ratio_before_entropy_coding": round(n / max(1, sum(pbv)), 4)}
+        del p_lit, p_len, p_off, p_meta, s_ews, s_dws
     ev.close()
     if args.calibration_copy_mib > 0:
         a_ = torch.empty(args.calibration_copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -397,6 +442,7 @@ def main(argv=None) -> int:
         "decode_gbps": r0["decode_gbps"],
         "ratio": r0["ratio"],
         "levels": {str(k): v for k, v in res.items()},
+        "split": split,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
