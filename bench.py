@@ -373,6 +373,28 @@ def main(argv=None) -> int:
                  "port_bytes": {"literals": pbv[0], "lengths": pbv[1], "offsets": pbv[2], "meta": pbv[3]},
                  "ratio_before_entropy_coding": round(n / max(1, sum(pbv)), 4)}
         del p_lit, p_len, p_off, p_meta, s_ews, s_dws
+    # Baseline: the one-thread-per-chunk decode of the same stream (the shape
+    # the pages attribute to upstream), kernel time against the block decoder.
+    baseline = None
+    if not args.no_split:
+        lv = levels[0]
+        out, nb, ews, dout, dnb, st, dws = bufs[lv]
+        s_ = torch.cuda.current_stream()
+        kb, ks = [], []
+        for i in range(args.warmup + args.steps):
+            k1, k2 = ev.pair(), ev.pair()
+            g.decode_into(out, stream_bytes[lv], dout, dnb, st, dws, events=k1)
+            g.decode_one_thread_per_chunk_into(out, stream_bytes[lv], dout, dnb, st, dws, events=k2)
+            if i >= args.warmup:
+                kb.append(k1)
+                ks.append(k2)
+        torch.cuda.synchronize()
+        if int(st.item()) != 0 or not torch.equal(dout[:n], x):
+            print("bench.py: one-thread-per-chunk decode mismatch", file=sys.stderr)
+            return 1
+        mb_, ms_ = float(np.mean([ev.ms(p) for p in kb])), float(np.mean([ev.ms(p) for p in ks]))
+        baseline = {"level": lv, "block_decode_kernel_ms": round(mb_, 4),
+                    "one_thread_per_chunk_decode_kernel_ms": round(ms_, 4), "speedup": round(ms_ / mb_, 2)}
     ev.close()
     if args.calibration_copy_mib > 0:
         a_ = torch.empty(args.calibration_copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -443,6 +465,7 @@ def main(argv=None) -> int:
         "ratio": r0["ratio"],
         "levels": {str(k): v for k, v in res.items()},
         "split": split,
+        "decode_baseline": baseline,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -18,7 +18,7 @@ STATUS_OK, STATUS_CAPACITY, STATUS_CORRUPT = 0, 2, 3
 SYMBOLS = ("gpulz_max_compressed_size", "gpulz_encode_workspace_size", "gpulz_decode_workspace_size",
            "gpulz_encode", "gpulz_decode", "gpulz_stream_info", "gpulz_encode_timed", "gpulz_decode_timed",
            "gpulz_split_bounds", "gpulz_encode_split_workspace_size", "gpulz_encode_split",
-           "gpulz_decode_split_workspace_size", "gpulz_decode_split")
+           "gpulz_decode_split_workspace_size", "gpulz_decode_split", "gpulz_decode_one_thread_per_chunk")
 
 _lib = None
 
@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
     L.gpulz_decode_split_workspace_size.restype = u64
     L.gpulz_decode_split.argtypes = [vp, u64, vp, vp, u64, vp, u64, vp, u64, vp, vp, vp, u64, vp]
     L.gpulz_decode_split.restype = ctypes.c_int
+    L.gpulz_decode_one_thread_per_chunk.argtypes = L.gpulz_decode.argtypes + [vp, vp]
+    L.gpulz_decode_one_thread_per_chunk.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -151,6 +153,20 @@ def decode_into(d_stream, in_bytes: int, out, out_bytes, status, workspace, stre
         _check(lib().gpulz_decode(*args), "gpulz_decode")
     else:
         _check(lib().gpulz_decode_timed(*args, events[0], events[1]), "gpulz_decode_timed")
+
+
+def decode_one_thread_per_chunk_into(d_stream, in_bytes: int, out, out_bytes, status, workspace, stream=None,
+                                     events=None) -> None:
+    """The one-thread-per-chunk baseline decoder (gpulz_baseline.h), same
+    buffers as decode_into."""
+    s = _u8_view(d_stream)
+    if in_bytes > s.numel():
+        raise GpulzError("in_bytes exceeds the stream buffer")
+    ev = events if events is not None else (None, None)
+    _check(lib().gpulz_decode_one_thread_per_chunk(_ptr(s), in_bytes, _ptr(out), out.numel(), _ptr(out_bytes),
+                                                   _ptr(status), _ptr(workspace), workspace.numel(),
+                                                   _stream(stream), ev[0], ev[1]),
+           "gpulz_decode_one_thread_per_chunk")
 
 
 def decode(d_stream, in_bytes: int | None = None, out_capacity: int | None = None, stream=None):

@@ -4,6 +4,7 @@
 #include "gpulz.h"
 #include "gpulz_timing.h"
 #include "gpulz_split.h"
+#include "gpulz_baseline.h"
 
 #include "common.h"
 
@@ -142,9 +143,33 @@ int gpulz_encode(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, uint32
                             d_workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
+namespace {
+int decode_common(const void* d_in, uint64_t in_bytes, void* d_out, uint64_t out_capacity, uint64_t* d_out_bytes,
+                  uint32_t* d_status, void* d_workspace, uint64_t workspace_bytes, hipStream_t stream,
+                  hipEvent_t ev_start, hipEvent_t ev_stop, bool serial);
+}  // namespace
+
 int gpulz_decode_timed(const void* d_in, uint64_t in_bytes, void* d_out, uint64_t out_capacity,
                        uint64_t* d_out_bytes, uint32_t* d_status, void* d_workspace, uint64_t workspace_bytes,
                        hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  return decode_common(d_in, in_bytes, d_out, out_capacity, d_out_bytes, d_status, d_workspace, workspace_bytes,
+                       stream, ev_start, ev_stop, false);
+}
+
+int gpulz_decode_one_thread_per_chunk(const void* d_in, uint64_t in_bytes, void* d_out, uint64_t out_capacity,
+                                      uint64_t* d_out_bytes, uint32_t* d_status, void* d_workspace,
+                                      uint64_t workspace_bytes, hipStream_t stream, hipEvent_t ev_start,
+                                      hipEvent_t ev_stop) {
+  return decode_common(d_in, in_bytes, d_out, out_capacity, d_out_bytes, d_status, d_workspace, workspace_bytes,
+                       stream, ev_start, ev_stop, true);
+}
+
+}  // extern "C"
+
+namespace {
+int decode_common(const void* d_in, uint64_t in_bytes, void* d_out, uint64_t out_capacity, uint64_t* d_out_bytes,
+                  uint32_t* d_status, void* d_workspace, uint64_t workspace_bytes, hipStream_t stream,
+                  hipEvent_t ev_start, hipEvent_t ev_stop, bool serial) {
   if (d_in == nullptr || d_out_bytes == nullptr || d_status == nullptr || d_workspace == nullptr)
     return GPULZ_ERR_INVALID_ARG;
   if (out_capacity > 0 && d_out == nullptr) return GPULZ_ERR_INVALID_ARG;
@@ -170,9 +195,12 @@ int gpulz_decode_timed(const void* d_in, uint64_t in_bytes, void* d_out, uint64_
   da.chunks_cap = (uint32_t)cap;
   da.ev_start = ev_start;
   da.ev_stop = ev_stop;
-  if (launch_decode(da, stream) != hipSuccess) return GPULZ_ERR_HIP;
+  if ((serial ? launch_decode_serial(da, stream) : launch_decode(da, stream)) != hipSuccess) return GPULZ_ERR_HIP;
   return GPULZ_OK;
 }
+}  // namespace
+
+extern "C" {
 
 int gpulz_decode(const void* d_in, uint64_t in_bytes, void* d_out, uint64_t out_capacity, uint64_t* d_out_bytes,
                  uint32_t* d_status, void* d_workspace, uint64_t workspace_bytes, hipStream_t stream) {

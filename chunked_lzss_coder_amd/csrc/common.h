@@ -197,6 +197,7 @@ uint32_t decode_tile_chunks(uint32_t chunks_cap);
 uint32_t decode_num_tiles(uint32_t chunks_cap);
 uint64_t decode_params_bytes();
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_serial(const DecodeArgs& a, hipStream_t stream);
 
 // Split mode: the meta port plays the stream's part (header, size table, flag
 // bitmaps); the item bytes come from the other three ports.

@@ -883,6 +883,122 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(7))) voi
   else decode_split_by_ws<4096>(p, a, a.loc, a.tile_sums, arena, sh);
 }
 
+// ---- one thread per chunk ----------------------------------------------------------
+// The decode shape the GPULZStage page attributes to upstream (its
+// block-parallel decode paragraph): a whole chunk on one thread, replaying
+// its items in order.  Kept as a measured baseline; same stream rules and
+// results as chunks_kernel.  Bytes past the chunk's real end are never
+// stored: they must decode to zero, so a match source there reads as zero.
+__global__ __launch_bounds__(kBlock) void serial_chunks_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes,
+                                                               uint8_t* __restrict__ out, const DecP* __restrict__ P,
+                                                               const uint32_t* __restrict__ loc,
+                                                               const uint64_t* __restrict__ tile_sum,
+                                                               const uint32_t* __restrict__ tile_err,
+                                                               uint32_t* __restrict__ status,
+                                                               uint64_t* __restrict__ out_bytes) {
+  const DecP p = *P;
+  if (p.status != kStatusOk) return;
+  if (blockIdx.x == 0 && threadIdx.x < 64u) {
+    uint64_t s = 0;
+    uint32_t err = 0;
+    for (uint32_t i = lane_id(); i < p.ntiles; i += 64u) {
+      s += tile_sum[i];
+      err |= tile_err[i];
+    }
+    s = lane63_64(wave_incl_add64(s));
+    err = lane63(wave_incl_add(err));
+    if (lane_id() == 0 && (s != p.pb || err)) raise_status(status, out_bytes, kStatusCorrupt);
+  }
+  const uint32_t cs = p.cs, ws = p.ws, E = cs / ws;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; c < p.nc; c += stride) {
+    const uint2 e = read_row(in, c);
+    const uint64_t start = c * cs;
+    const uint32_t bc = (uint32_t)((p.n - start) < cs ? (p.n - start) : cs);
+    if (!row_ok(e, bc)) continue;  // reported by the scan kernel
+    const uint32_t size = entry_payload(e.x, e.y);
+    const uint32_t t = (uint32_t)(c / p.T);
+    uint64_t off = loc[c];
+    for (uint32_t i = 0; i < t; ++i) off += tile_sum[i];
+    if (off + size > p.pb) continue;  // reported by the tile-total check
+    const uint8_t* pay = in + p.base + off;
+    uint8_t* dst = out + start;
+    if (e.x == 0u) {
+      const bool zero = e.y == 0u;
+      for (uint32_t y = 0; y < bc; ++y) dst[y] = zero ? 0u : pay[y];
+      continue;
+    }
+    const uint32_t F = e.x, D = e.y;
+    const uint8_t* fl = pay;
+    const uint8_t* dt = pay + F;
+    uint32_t q = 0, d = 0, k = 0;
+    bool ok = true;
+    // whole-element loads and stores when the element is real and aligned
+    const bool wal = (((uintptr_t)dst) & (ws - 1u)) == 0;
+    auto get_el = [&](uint32_t i) -> uint32_t {  // element i of the output (0 past the real bytes)
+      if (wal && (i + 1u) * ws <= bc) {
+        if (ws == 4u) return *(const uint32_t*)(dst + 4u * i);
+        if (ws == 2u) return *(const uint16_t*)(dst + 2u * i);
+        return dst[i];
+      }
+      uint32_t v = 0;
+      for (uint32_t b = 0; b < ws; ++b)
+        if (i * ws + b < bc) v |= (uint32_t)dst[i * ws + b] << (8u * b);
+      return v;
+    };
+    auto put_el = [&](uint32_t i, uint32_t v) {  // padding elements must decode to zero
+      if (wal && (i + 1u) * ws <= bc) {
+        if (ws == 4u) *(uint32_t*)(dst + 4u * i) = v;
+        else if (ws == 2u) *(uint16_t*)(dst + 2u * i) = (uint16_t)v;
+        else dst[i] = (uint8_t)v;
+        return;
+      }
+      for (uint32_t b = 0; b < ws; ++b) {
+        const uint8_t x = (uint8_t)(v >> (8u * b));
+        if (i * ws + b < bc) dst[i * ws + b] = x;
+        else if (x != 0u) ok = false;
+      }
+    };
+    while (ok && q < E) {
+      if (k >= 8u * F) {
+        ok = false;
+        break;
+      }
+      if ((fl[k >> 3] >> (k & 7u)) & 1u) {
+        if (d + 2u > D) {
+          ok = false;
+          break;
+        }
+        const uint32_t L = dt[d], O = dt[d + 1u];
+        d += 2u;
+        if (L == 0u || O == 0u || O > q || q + L > E) {
+          ok = false;
+          break;
+        }
+        for (uint32_t j = 0; j < L; ++j) put_el(q + j, get_el(q + j - O));  // overlapping copies run forward
+        q += L;
+      } else {
+        if (d + ws > D) {
+          ok = false;
+          break;
+        }
+        uint32_t v = 0;
+        for (uint32_t b = 0; b < ws; ++b) v |= (uint32_t)dt[d + b] << (8u * b);
+        put_el(q, v);
+        d += ws;
+        ++q;
+      }
+      ++k;
+    }
+    if (ok) {
+      if (d != D || (k + 7u) / 8u != F) ok = false;
+      for (uint32_t b = k; ok && b < 8u * F; ++b)
+        if ((fl[b >> 3] >> (b & 7u)) & 1u) ok = false;
+    }
+    if (!ok) raise_status(status, out_bytes, kStatusCorrupt);
+  }
+}
+
 }  // namespace
 
 uint32_t decode_tile_chunks(uint32_t chunks_cap) {
@@ -909,6 +1025,23 @@ hipError_t launch_decode_split(const SplitDecodeArgs& a, hipStream_t stream) {
     if (grid > kDecodeGrid) grid = kDecodeGrid;
     hipLaunchKernelGGL(split_chunks_kernel, dim3(grid), dim3(kBlock), 0, stream, a, (const DecP*)a.params);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_serial(const DecodeArgs& a, hipStream_t stream) {
+  const uint32_t T = decode_tile_chunks(a.chunks_cap);
+  const uint32_t tiles = decode_num_tiles(a.chunks_cap);
+  hipLaunchKernelGGL(scan_kernel, dim3(tiles), dim3(kBlock), 0, stream, a.in, a.in_bytes, a.out_capacity,
+                     a.chunks_cap, T, (DecP*)a.params, a.loc, a.tile_sums, a.tile_err, a.status, a.out_bytes);
+  if (a.ev_start && hipEventRecord(a.ev_start, stream) != hipSuccess) return hipErrorUnknown;
+  if (a.chunks_cap > 0) {
+    uint32_t grid = (a.chunks_cap + kBlock - 1u) / kBlock;
+    if (grid > kDecodeGrid) grid = kDecodeGrid;
+    hipLaunchKernelGGL(serial_chunks_kernel, dim3(grid), dim3(kBlock), 0, stream, a.in, a.in_bytes, a.out,
+                       (const DecP*)a.params, (const uint32_t*)a.loc, (const uint64_t*)a.tile_sums,
+                       (const uint32_t*)a.tile_err, a.status, a.out_bytes);
+  }
+  if (a.ev_stop && hipEventRecord(a.ev_stop, stream) != hipSuccess) return hipErrorUnknown;
   return hipGetLastError();
 }
 

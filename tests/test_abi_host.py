@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
                                          "gpulz_stream_info", "gpulz_encode_timed", "gpulz_decode_timed",
                                          "gpulz_split_bounds", "gpulz_encode_split_workspace_size",
                                          "gpulz_encode_split", "gpulz_decode_split_workspace_size",
-                                         "gpulz_decode_split"])
+                                         "gpulz_decode_split", "gpulz_decode_one_thread_per_chunk"])
 
 
 def test_library_exports_every_declared_symbol(g):
