@@ -153,6 +153,73 @@ __device__ __forceinline__ uint32_t load4_unaligned(const uint8_t* p, const uint
   return v;
 }
 
+// ---- 16-byte copies ---------------------------------------------------------
+// Bytes 4q + r .. 4q + r + 15 of the 32 bytes a | b (q < 4, r < 4, the same
+// in every lane).  Plain variables, no array: a select between two array
+// elements would keep the array in memory.
+__device__ __forceinline__ uint4 funnel16(uint4 a, uint4 b, uint32_t q, uint32_t r) {
+  const bool q2 = (q & 2u) != 0u, q1 = (q & 1u) != 0u;
+  // shift by two dwords, then by one
+  const uint32_t v0 = q2 ? a.z : a.x, v1 = q2 ? a.w : a.y, v2 = q2 ? b.x : a.z, v3 = q2 ? b.y : a.w,
+                 v4 = q2 ? b.z : b.x, v5 = q2 ? b.w : b.y;
+  const uint32_t u0 = q1 ? v1 : v0, u1 = q1 ? v2 : v1, u2 = q1 ? v3 : v2, u3 = q1 ? v4 : v3, u4 = q1 ? v5 : v4;
+  return make_uint4(__builtin_amdgcn_alignbyte(u1, u0, r), __builtin_amdgcn_alignbyte(u2, u1, r),
+                    __builtin_amdgcn_alignbyte(u3, u2, r), __builtin_amdgcn_alignbyte(u4, u3, r));
+}
+
+// Copy n bytes from src to dst (any alignments) with one wave (this is lane
+// l): single bytes before dst's first 16-byte boundary and after its last,
+// 16-byte stores in between.  The source is read as aligned 16-byte blocks
+// that each hold at least one of the n bytes, so no read leaves the pages the
+// source bytes lie in.  Each lane loads four blocks before it stores; the
+// block after a lane's comes from the next lane by a wave shift (lane 63
+// takes lane 0's next block, or loads the block after the round).  Named
+// registers rather than an array keep the blocks out of memory.
+__device__ __forceinline__ void copy_bytes16(uint8_t* dst, const uint8_t* src, uint32_t n, uint32_t l) {
+  const uint32_t h0 = (uint32_t)((16u - ((uintptr_t)dst & 15u)) & 15u);
+  const uint32_t h = h0 < n ? h0 : n;
+  if (l < h) dst[l] = src[l];
+  const uint32_t nb = (n - h) >> 4;         // 16-byte stores
+  const uintptr_t s = (uintptr_t)(src + h);
+  const uint32_t sh = (uint32_t)(s & 15u);
+  const uint32_t ns = nb + (sh ? 1u : 0u);  // source blocks holding the stored bytes
+  const uint4* sb = (const uint4*)(s - sh);
+  uint4* db = (uint4*)(dst + h);
+  const uint32_t q = sh >> 2, r = sh & 3u;
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  auto next_of = [&](uint4 a, uint4 nx) {  // the block after this lane's
+    uint4 b;
+    b.x = dpp0<kWaveShl1>(a.x);
+    b.y = dpp0<kWaveShl1>(a.y);
+    b.z = dpp0<kWaveShl1>(a.z);
+    b.w = dpp0<kWaveShl1>(a.w);
+    return l == 63u ? nx : b;
+  };
+  auto lane0 = [&](uint4 a) {
+    return make_uint4((uint32_t)__builtin_amdgcn_readlane((int)a.x, 0), (uint32_t)__builtin_amdgcn_readlane((int)a.y, 0),
+                      (uint32_t)__builtin_amdgcn_readlane((int)a.z, 0), (uint32_t)__builtin_amdgcn_readlane((int)a.w, 0));
+  };
+  auto put = [&](uint32_t k, uint4 a, uint4 b) {
+    if (k < nb) db[k] = sh ? funnel16(a, b, q, r) : a;
+  };
+#pragma unroll 1
+  for (uint32_t k0 = 0; k0 < nb; k0 += 256u) {
+    const uint32_t k = k0 + l;
+    const uint4 a0 = k < ns ? sb[k] : z;
+    const uint4 a1 = k + 64u < ns ? sb[k + 64u] : z;
+    const uint4 a2 = k + 128u < ns ? sb[k + 128u] : z;
+    const uint4 a3 = k + 192u < ns ? sb[k + 192u] : z;
+    const uint32_t kx = k0 + 256u;  // first block of the next round
+    const uint4 x = (l == 63u && sh && kx < ns) ? sb[kx] : z;
+    put(k, a0, next_of(a0, lane0(a1)));
+    put(k + 64u, a1, next_of(a1, lane0(a2)));
+    put(k + 128u, a2, next_of(a2, lane0(a3)));
+    put(k + 192u, a3, next_of(a3, x));
+  }
+  const uint32_t t = h + 16u * nb + l;  // fewer than 16 tail bytes
+  if (t < n) dst[t] = src[t];
+}
+
 // ---- launchers (host side, one per kernel family) -------------------------
 struct EncodeArgs {
   const uint8_t* in;

@@ -1,19 +1,16 @@
-// encode.hip -- chunked LZSS encode for gfx950, one fused pass.
+// encode.hip -- chunked LZSS encode for gfx950: a chunk kernel and an
+// assembly kernel.
 //
-// A "team" of WPC wave64s owns one chunk (WPC = 1 for chunks of up to 1024
-// elements, so most of the work needs no workgroup barrier; a workgroup holds
-// CPW teams).  Teams assemble the stream themselves: once a chunk's payload
-// size is known it is published and the chunk's output offset is found by a
-// decoupled look-back over its predecessors' published sizes, so flags and
-// data go straight from LDS to their final place in the stream (no staging
-// area, no second pass).
-//
-// Per chunk (GPULZStage page paragraphs in brackets):
+// encode_kernel: a "team" of WPC wave64s owns one chunk (WPC = 1 for chunks
+// of up to 512 elements, so most of the work needs no workgroup barrier; a
+// workgroup holds CPW teams).  Per chunk (GPULZStage page paragraphs in
+// brackets):
 //   1. load the chunk (zero padded past its real bytes) into LDS as E words;
 //      all zero -> entry (0,0), no payload [zero-chunk paragraph];
 //   2. omask[p], bit o-1 = (x[p] == x[p-o]), o = 1..32 [exact-search
 //      paragraph]: each lane holds 8 consecutive positions and the 32 words
 //      before them in registers, so the 256 comparisons per lane read LDS once;
+//      no bit set anywhere -> at level 0 the chunk is raw, steps 3-6 skipped;
 //   3. a base-4 doubling table S_k[p] = AND of omask over [p, p+k) for
 //      k = 1, 4, 16, 64, and a 4-round descent per position (up to three
 //      steps of k per round, so L <= 255) giving the exact longest run of any
@@ -27,9 +24,15 @@
 //      segments then fixes the real entry of each segment;
 //   6. item counts from popcounts (two item sizes only) -> flag bytes F and
 //      data bytes D; raw when F + D >= real bytes [raw-fallback paragraph];
-//   7. the size is published first, the payload is built in LDS, and only
-//      then does the look-back wait for the output offset; then the size-table
-//      row and the payload bytes are written.
+//   7. the size-table row goes straight into the stream; a coded payload
+//      (flag bitmap, then data bytes) is built in LDS and written to the
+//      chunk's fixed-stride staging slot.  A raw chunk's payload is its input
+//      bytes: it is staged only when the assembly cannot read it from the
+//      input (input not 16-byte aligned, or split mode).
+// compact_kernel: one workgroup per tile of 64 chunks scans the tile's sizes,
+//   finds the tile's offset by decoupled look-back over the tiles before it
+//   and moves every payload to its place in the stream with 16-byte stores;
+//   the last tile writes the header.
 #include "common.h"
 
 namespace gpulz {
@@ -278,6 +281,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
   uint32_t kb[WPC == 1 ? NR : 1], mb[WPC == 1 ? NR : 1];
   if (nonzero) {
     // ---- 2. omask: 8 consecutive positions per lane, window in registers -------------
+    uint32_t any_om = 0;  // OR of this lane's masks
     {
       constexpr uint32_t PPASS = (E == 256 ? 4u : 8u);  // positions per lane per pass
       constexpr uint32_t NPASS = E / (PPASS * TL);
@@ -310,223 +314,242 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
           match_bits16(m, &w[q + 16], w[32 + q]);
           const uint32_t p = p0 + q;
           om[q] = p >= 32u ? m : (m & ((1u << p) - 1u));
+          any_om |= om[q];
         }
 #pragma unroll
         for (uint32_t i = 0; i < PPASS / 4; ++i)
           *(uint4*)(LV + p0 + 4 * i) = make_uint4(om[4 * i], om[4 * i + 1], om[4 * i + 2], om[4 * i + 3]);
       }
     }
-    team_sync<WPC>();
-
-    // ---- 3. base-4 doubling table S_4, S_16, S_64 and a 4-round descent ------------
-    // S_k[p] = AND of omask over [p, p+k) when p + k <= E, else 0; every
-    // table is followed by zeros, so descent reads past the chunk need no
-    // bounds checks.
-    for (uint32_t i = g; i < 184u; i += TL) {  // padding word i of level lv is at (lv + 1) E + i
-      const uint32_t lv = i < 4u ? 0u : (i < 16u ? 1u : (i < 52u ? 2u : 3u));
-      LV[(lv + 1u) * (uint32_t)E + i] = 0u;
+    // No near match anywhere in the chunk: every length is 0.  At level 0 the
+    // parse is then E literals, F + D = E / 8 + CS > bc, so the chunk is raw
+    // and the search and parse are skipped; level 1 still runs its table.
+    bool near;
+    if (WPC == 1) {
+      near = __ballot(any_om != 0u) != 0ull;
+      wave_sync();
+    } else {
+      near = __syncthreads_or(any_om != 0u);
     }
+    if (LEVEL == 0 && !near) {
+      K = (uint32_t)E;
+    } else {
+      if (near) {
+        // ---- 3. base-4 doubling table S_4, S_16, S_64 and a 4-round descent ------------
+        // S_k[p] = AND of omask over [p, p+k) when p + k <= E, else 0; every
+        // table is followed by zeros, so descent reads past the chunk need no
+        // bounds checks.
+        for (uint32_t i = g; i < 184u; i += TL) {  // padding word i of level lv is at (lv + 1) E + i
+          const uint32_t lv = i < 4u ? 0u : (i < 16u ? 1u : (i < 52u ? 2u : 3u));
+          LV[(lv + 1u) * (uint32_t)E + i] = 0u;
+        }
 #pragma unroll
-    for (uint32_t lv = 1; lv < 4; ++lv) {
-      const uint32_t k = 1u << (2 * lv), step = k >> 2;
-      const uint32_t* prev = LV + L::TOFF[lv - 1];
-      uint32_t* cur = LV + L::TOFF[lv];
+        for (uint32_t lv = 1; lv < 4; ++lv) {
+          const uint32_t k = 1u << (2 * lv), step = k >> 2;
+          const uint32_t* prev = LV + L::TOFF[lv - 1];
+          uint32_t* cur = LV + L::TOFF[lv];
 #pragma unroll
-      for (uint32_t i = 0; i < PPL; ++i) {
-        const uint32_t p = g + i * TL;
-        uint32_t v = 0;
-        if (p + k <= (uint32_t)E) v = prev[p] & prev[p + step] & prev[p + 2 * step] & prev[p + 3 * step];
-        cur[p] = v;
+          for (uint32_t i = 0; i < PPL; ++i) {
+            const uint32_t p = g + i * TL;
+            uint32_t v = 0;
+            if (p + k <= (uint32_t)E) v = prev[p] & prev[p + step] & prev[p + 2 * step] & prev[p + 3 * step];
+            cur[p] = v;
+          }
+          team_sync<WPC>();
+        }
+        uint32_t lo[PPL];
+#pragma unroll
+        for (uint32_t i = 0; i < PPL; ++i) {
+          const uint32_t p = g + i * TL;
+          uint32_t surv = ~0u, Ln = 0;
+          // digits of L in base 4, most significant first: at most 3 steps of k per
+          // round, so L <= 3 * (64 + 16 + 4 + 1) = 255, the length cap
+#pragma unroll
+          for (int lv = 3; lv >= 0; --lv) {
+            const uint32_t k = 1u << (2 * lv);
+            // p + Ln <= E (every surviving position is inside the chunk), so the
+            // three reads end within the table's padding
+            const uint32_t* S = LV + L::TOFF[lv] + p + Ln;
+            const uint32_t t1 = surv & S[0], t2 = t1 & S[k], t3 = t2 & S[2u * k];
+            const uint32_t n = (uint32_t)(t1 != 0u) + (uint32_t)(t2 != 0u) + (uint32_t)(t3 != 0u);
+            surv = t3 ? t3 : (t2 ? t2 : (t1 ? t1 : surv));
+            Ln += n << (2 * lv);
+          }
+          lo[i] = Ln ? (Ln | (((uint32_t)__builtin_ctz(surv) + 1u) << 8)) : 0u;
+        }
+        team_sync<WPC>();
+#pragma unroll
+        for (uint32_t i = 0; i < PPL; ++i) LO[g + i * TL] = lo[i];
+        team_sync<WPC>();
+      } else {
+#pragma unroll
+        for (uint32_t i = 0; i < PPL; ++i) LO[g + i * TL] = 0u;
+        team_sync<WPC>();
+      }
+
+      // ---- 4. level 1 ----------------------------------------------------------------------
+      if (LEVEL == 1) {
+        for (uint32_t i = g; i < kHashSize; i += TL) T[i] = 0u;
+        team_sync<WPC>();  // T overlays dead table levels
+        constexpr uint32_t SB = E / kSubBlocks;
+#pragma unroll 1
+        for (uint32_t s = 0; s < kSubBlocks; ++s) {
+          for (uint32_t p = s * SB + g; p < (s + 1) * SB; p += TL) {
+            if (p + 1 >= (uint32_t)E) continue;
+            const uint32_t v = T[bucket_of(X[p], X[p + 1])];
+            if (v == 0) continue;
+            const uint32_t o = p - (v - 1u);  // entries come from earlier sub-blocks: o >= 1
+            if (o > kMaxFar) continue;
+            // the candidate replaces the near match only if its run is strictly
+            // longer, so it must match at p + Lnear, and Lnear must leave room
+            const uint32_t lim = (uint32_t)E - p < kMaxLen ? (uint32_t)E - p : kMaxLen;
+            const uint32_t Lnear = LO[p] & 0xFFu;
+            if (Lnear >= lim || X[p + Lnear] != X[p + Lnear - o]) continue;
+            // run at offset o, capped at lim, eight compares per step (reads past
+            // the chunk's words stay inside the team's LDS and are masked)
+            uint32_t r = 0;
+            while (true) {
+              uint32_t stop = 0;
+#pragma unroll
+              for (uint32_t j = 0; j < 8u; ++j) {
+                const uint32_t idx = r + j;
+                const uint32_t a = X[p + idx], b = X[p + idx - o];
+                stop |= (uint32_t)(idx >= lim || a != b) << j;
+              }
+              if (stop) {
+                r += (uint32_t)__builtin_ctz(stop);
+                break;
+              }
+              r += 8u;
+            }
+            if (r > Lnear) LO[p] = r | (o << 8);
+          }
+          team_sync<WPC>();
+          for (uint32_t p = s * SB + g; p < (s + 1) * SB; p += TL)
+            if (p + 1 < (uint32_t)E) atomicMax(&T[bucket_of(X[p], X[p + 1])], p + 1u);
+          team_sync<WPC>();
+        }
+      }
+
+      // ---- 5. parallel greedy parse --------------------------------------------------------
+      // (a) per segment of 8 positions: for every entry q, the exit position and
+      //     the item-start mask of the parse walked from q.
+      for (uint32_t sg = g; sg < L::NSEG; sg += TL) {
+        const uint32_t p0 = sg * 8u;
+        const uint4 a = *(const uint4*)(LO + p0);
+        const uint4 b = *(const uint4*)(LO + p0 + 4);
+        const uint32_t l8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        uint32_t ex[8], im[8], lmb = 0;
+#pragma unroll
+        for (int q = 7; q >= 0; --q) {
+          const uint32_t len = l8[q] & 0xFFu;
+          const bool mt = len >= MM;
+          lmb |= (mt ? 1u : 0u) << q;
+          const uint32_t nq = (uint32_t)q + (mt ? len : 1u);
+          uint32_t e = p0 + nq, m = 1u << q;
+#pragma unroll
+          for (int r = q + 1; r < 8; ++r)
+            if (nq == (uint32_t)r) {
+              e = ex[r];
+              m = (1u << q) | im[r];
+            }
+          ex[q] = e;
+          im[q] = m;
+        }
+        *(uint4*)(XQ + p0) = make_uint4(ex[0] | (im[0] << 16), ex[1] | (im[1] << 16), ex[2] | (im[2] << 16),
+                                        ex[3] | (im[3] << 16));
+        *(uint4*)(XQ + p0 + 4) = make_uint4(ex[4] | (im[4] << 16), ex[5] | (im[5] << 16),
+                                            ex[6] | (im[6] << 16), ex[7] | (im[7] << 16));
+        if (WPC > 1) {
+          ((uint8_t*)LMB)[sg] = (uint8_t)lmb;
+          ((uint8_t*)ISB)[sg] = 0;
+        }
       }
       team_sync<WPC>();
-    }
-    uint32_t lo[PPL];
+      // (b) hops: the parse's real entry into every segment it passes through
+      if constexpr (WPC == 1) {
+        // exits held in registers (lane j of word i = position 64i + j); the hop
+        // position P is uniform, so each hop is one readlane
+        uint32_t xqr[NR];
 #pragma unroll
-    for (uint32_t i = 0; i < PPL; ++i) {
-      const uint32_t p = g + i * TL;
-      uint32_t surv = ~0u, Ln = 0;
-      // digits of L in base 4, most significant first: at most 3 steps of k per
-      // round, so L <= 3 * (64 + 16 + 4 + 1) = 255, the length cap
-#pragma unroll
-      for (int lv = 3; lv >= 0; --lv) {
-        const uint32_t k = 1u << (2 * lv);
-        // p + Ln <= E (every surviving position is inside the chunk), so the
-        // three reads end within the table's padding
-        const uint32_t* S = LV + L::TOFF[lv] + p + Ln;
-        const uint32_t t1 = surv & S[0], t2 = t1 & S[k], t3 = t2 & S[2u * k];
-        const uint32_t n = (uint32_t)(t1 != 0u) + (uint32_t)(t2 != 0u) + (uint32_t)(t3 != 0u);
-        surv = t3 ? t3 : (t2 ? t2 : (t1 ? t1 : surv));
-        Ln += n << (2 * lv);
-      }
-      lo[i] = Ln ? (Ln | (((uint32_t)__builtin_ctz(surv) + 1u) << 8)) : 0u;
-    }
-    team_sync<WPC>();
-#pragma unroll
-    for (uint32_t i = 0; i < PPL; ++i) LO[g + i * TL] = lo[i];
-    team_sync<WPC>();
-
-    // ---- 4. level 1 ----------------------------------------------------------------------
-    if (LEVEL == 1) {
-      for (uint32_t i = g; i < kHashSize; i += TL) T[i] = 0u;
-      team_sync<WPC>();  // T overlays dead table levels
-      constexpr uint32_t SB = E / kSubBlocks;
-#pragma unroll 1
-      for (uint32_t s = 0; s < kSubBlocks; ++s) {
-        for (uint32_t p = s * SB + g; p < (s + 1) * SB; p += TL) {
-          if (p + 1 >= (uint32_t)E) continue;
-          const uint32_t v = T[bucket_of(X[p], X[p + 1])];
-          if (v == 0) continue;
-          const uint32_t o = p - (v - 1u);  // entries come from earlier sub-blocks: o >= 1
-          if (o > kMaxFar) continue;
-          // the candidate replaces the near match only if its run is strictly
-          // longer, so it must match at p + Lnear, and Lnear must leave room
-          const uint32_t lim = (uint32_t)E - p < kMaxLen ? (uint32_t)E - p : kMaxLen;
-          const uint32_t Lnear = LO[p] & 0xFFu;
-          if (Lnear >= lim || X[p + Lnear] != X[p + Lnear - o]) continue;
-          // run at offset o, capped at lim, eight compares per step (reads past
-          // the chunk's words stay inside the team's LDS and are masked)
-          uint32_t r = 0;
-          while (true) {
-            uint32_t stop = 0;
-#pragma unroll
-            for (uint32_t j = 0; j < 8u; ++j) {
-              const uint32_t idx = r + j;
-              const uint32_t a = X[p + idx], b = X[p + idx - o];
-              stop |= (uint32_t)(idx >= lim || a != b) << j;
-            }
-            if (stop) {
-              r += (uint32_t)__builtin_ctz(stop);
-              break;
-            }
-            r += 8u;
-          }
-          if (r > Lnear) LO[p] = r | (o << 8);
-        }
-        team_sync<WPC>();
-        for (uint32_t p = s * SB + g; p < (s + 1) * SB; p += TL)
-          if (p + 1 < (uint32_t)E) atomicMax(&T[bucket_of(X[p], X[p + 1])], p + 1u);
-        team_sync<WPC>();
-      }
-    }
-
-    // ---- 5. parallel greedy parse --------------------------------------------------------
-    // (a) per segment of 8 positions: for every entry q, the exit position and
-    //     the item-start mask of the parse walked from q.
-    for (uint32_t sg = g; sg < L::NSEG; sg += TL) {
-      const uint32_t p0 = sg * 8u;
-      const uint4 a = *(const uint4*)(LO + p0);
-      const uint4 b = *(const uint4*)(LO + p0 + 4);
-      const uint32_t l8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      uint32_t ex[8], im[8], lmb = 0;
-#pragma unroll
-      for (int q = 7; q >= 0; --q) {
-        const uint32_t len = l8[q] & 0xFFu;
-        const bool mt = len >= MM;
-        lmb |= (mt ? 1u : 0u) << q;
-        const uint32_t nq = (uint32_t)q + (mt ? len : 1u);
-        uint32_t e = p0 + nq, m = 1u << q;
-#pragma unroll
-        for (int r = q + 1; r < 8; ++r)
-          if (nq == (uint32_t)r) {
-            e = ex[r];
-            m = (1u << q) | im[r];
-          }
-        ex[q] = e;
-        im[q] = m;
-      }
-      *(uint4*)(XQ + p0) = make_uint4(ex[0] | (im[0] << 16), ex[1] | (im[1] << 16), ex[2] | (im[2] << 16),
-                                      ex[3] | (im[3] << 16));
-      *(uint4*)(XQ + p0 + 4) = make_uint4(ex[4] | (im[4] << 16), ex[5] | (im[5] << 16),
-                                          ex[6] | (im[6] << 16), ex[7] | (im[7] << 16));
-      if (WPC > 1) {
-        ((uint8_t*)LMB)[sg] = (uint8_t)lmb;
-        ((uint8_t*)ISB)[sg] = 0;
-      }
-    }
-    team_sync<WPC>();
-    // (b) hops: the parse's real entry into every segment it passes through
-    if constexpr (WPC == 1) {
-      // exits held in registers (lane j of word i = position 64i + j); the hop
-      // position P is uniform, so each hop is one readlane
-      uint32_t xqr[NR];
-#pragma unroll
-      for (uint32_t i = 0; i < NR; ++i) {
-        const uint32_t p = 64u * i + lane;
-        xqr[i] = XQ[p];
-        lmw[i] = __ballot((LO[p] & 0xFFu) >= MM);
-      }
-      uint32_t P = 0;
-#pragma unroll
-      for (uint32_t i = 0; i < NR; ++i) {
-        uint64_t acc = 0;
-        while (P < 64u * (i + 1u)) {
-          const uint32_t xq = __builtin_amdgcn_readlane(xqr[i], P & 63u);
-          acc |= (uint64_t)(xq >> 16) << (P & 56u);
-          P = xq & 0xFFFFu;
-        }
-        isw[i] = acc;
-      }
-      // ---- 6. counts -------------------------------------------------------------------
-#pragma unroll
-      for (uint32_t i = 0; i < NR; ++i) {
-        kb[i] = K;
-        mb[i] = M;
-        K += (uint32_t)__builtin_popcountll(isw[i]);
-        M += (uint32_t)__builtin_popcountll(isw[i] & lmw[i]);
-      }
-    } else {
-      if (g < 64u) {
-        // the first wave hops word by word: the exits of 64 positions in one
-        // VGPR (the next word's load in flight), one readlane per hop
-        uint64_t* IS64w = (uint64_t*)ISB;
-        uint32_t P = 0;
-        uint32_t xq_next = XQ[lane];
-#pragma unroll 1
         for (uint32_t i = 0; i < NR; ++i) {
-          const uint32_t xqr = xq_next;
-          if (i + 1u < NR) xq_next = XQ[64u * (i + 1u) + lane];
+          const uint32_t p = 64u * i + lane;
+          xqr[i] = XQ[p];
+          lmw[i] = __ballot((LO[p] & 0xFFu) >= MM);
+        }
+        uint32_t P = 0;
+#pragma unroll
+        for (uint32_t i = 0; i < NR; ++i) {
           uint64_t acc = 0;
           while (P < 64u * (i + 1u)) {
-            const uint32_t xq = __builtin_amdgcn_readlane(xqr, P & 63u);
+            const uint32_t xq = __builtin_amdgcn_readlane(xqr[i], P & 63u);
             acc |= (uint64_t)(xq >> 16) << (P & 56u);
             P = xq & 0xFFFFu;
           }
-          if (lane == 0u) IS64w[i] = acc;
+          isw[i] = acc;
         }
-      }
-      team_sync<WPC>();
-      // ---- 6. counts (first wave) --------------------------------------------------------
-      const uint64_t* IS64 = (const uint64_t*)ISB;
-      const uint64_t* LM64 = (const uint64_t*)LMB;
-      if (g < 64u) {
-        uint32_t kc = 0, mc = 0;
-        if (g < NR) {
-          const uint64_t is = IS64[g];
-          kc = __builtin_popcountll(is);
-          mc = __builtin_popcountll(is & LM64[g]);
-        }
-        uint32_t ki = kc, mi = mc;
+        // ---- 6. counts -------------------------------------------------------------------
 #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const uint32_t a = __shfl_up(ki, d, 64), b = __shfl_up(mi, d, 64);
-          if (lane >= (uint32_t)d) {
-            ki += a;
-            mi += b;
+        for (uint32_t i = 0; i < NR; ++i) {
+          kb[i] = K;
+          mb[i] = M;
+          K += (uint32_t)__builtin_popcountll(isw[i]);
+          M += (uint32_t)__builtin_popcountll(isw[i] & lmw[i]);
+        }
+      } else {
+        if (g < 64u) {
+          // the first wave hops word by word: the exits of 64 positions in one
+          // VGPR (the next word's load in flight), one readlane per hop
+          uint64_t* IS64w = (uint64_t*)ISB;
+          uint32_t P = 0;
+          uint32_t xq_next = XQ[lane];
+#pragma unroll 1
+          for (uint32_t i = 0; i < NR; ++i) {
+            const uint32_t xqr = xq_next;
+            if (i + 1u < NR) xq_next = XQ[64u * (i + 1u) + lane];
+            uint64_t acc = 0;
+            while (P < 64u * (i + 1u)) {
+              const uint32_t xq = __builtin_amdgcn_readlane(xqr, P & 63u);
+              acc |= (uint64_t)(xq >> 16) << (P & 56u);
+              P = xq & 0xFFFFu;
+            }
+            if (lane == 0u) IS64w[i] = acc;
           }
         }
-        if (g < NR) {
-          KB[g] = ki - kc;
-          MB[g] = mi - mc;
+        team_sync<WPC>();
+        // ---- 6. counts (first wave) --------------------------------------------------------
+        const uint64_t* IS64 = (const uint64_t*)ISB;
+        const uint64_t* LM64 = (const uint64_t*)LMB;
+        if (g < 64u) {
+          uint32_t kc = 0, mc = 0;
+          if (g < NR) {
+            const uint64_t is = IS64[g];
+            kc = __builtin_popcountll(is);
+            mc = __builtin_popcountll(is & LM64[g]);
+          }
+          uint32_t ki = kc, mi = mc;
+#pragma unroll
+          for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t a = __shfl_up(ki, d, 64), b = __shfl_up(mi, d, 64);
+            if (lane >= (uint32_t)d) {
+              ki += a;
+              mi += b;
+            }
+          }
+          if (g < NR) {
+            KB[g] = ki - kc;
+            MB[g] = mi - mc;
+          }
+          if (g == NR - 1u) {
+            SC[1] = ki;
+            SC[2] = mi;
+          }
         }
-        if (g == NR - 1u) {
-          SC[1] = ki;
-          SC[2] = mi;
-        }
+        team_sync<WPC>();
+        K = SC[1];
+        M = SC[2];
       }
-      team_sync<WPC>();
-      K = SC[1];
-      M = SC[2];
-    }
+    }  // near match, or level 1
   }  // nonzero
   const uint32_t F = (K + 7u) / 8u;
   const uint32_t D = (uint32_t)WS * (K - M) + 2u * M;
@@ -609,7 +632,9 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
     }
     team_sync<WPC>();
     for (uint32_t i = g; i < (F + D + 3u) / 4u; i += TL) slot[i] = STG32[i];
-  } else if (raw) {
+  } else if (raw && km) {
+    // split mode stages raw bytes for the literals port; the one-stream
+    // assembly copies a raw chunk straight from the input
     if (WS == 4) {
       for (uint32_t i = g; i < CS / 4u; i += TL) slot[i] = X[i];
     } else {
@@ -645,16 +670,16 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
 // Compaction: one workgroup per tile of kCTile chunks.  Reads the tile's
 // size-table rows, scans the payload sizes, finds the tile's output offset
 // by decoupled look-back over the tiles before it, then moves every payload
-// from its staging slot to its place in the stream.  The last tile writes
-// the header and the stream length.
-__global__ __launch_bounds__(kBlock) void compact_kernel(const uint8_t* __restrict__ staging, uint32_t cs,
+// to its place in the stream: a coded chunk's from its staging slot, a raw
+// chunk's straight from the input.  The last tile writes the header and the
+// stream length.
+__global__ __launch_bounds__(kBlock) void compact_kernel(const uint8_t* __restrict__ in,
+                                                         const uint8_t* __restrict__ staging, uint32_t cs,
                                                          uint32_t ws, uint64_t n, uint32_t num_chunks,
                                                          uint32_t num_tiles, uint8_t* __restrict__ out,
                                                          uint64_t* __restrict__ out_bytes,
                                                          uint64_t* __restrict__ tile_flags,
                                                          EncCtl* __restrict__ ctl) {
-  __shared__ uint32_t sz[kCTile];
-  __shared__ uint32_t off[kCTile];
   __shared__ uint64_t tile_pre;
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const uint8_t* table = out + kHeaderBytes;
@@ -676,21 +701,24 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(const uint8_t* __restri
   }
   const uint32_t t = blockIdx.x;
   const uint64_t c0 = (uint64_t)t * kCTile;
-  // Each wave moves PW chunks.  The first 256 bytes of each of its staging
-  // slots (one dword per lane) are loaded before the sizes and offsets are
-  // known, so the loads overlap the row reads and the look-back.
+  // Wave w moves chunks 16w .. 16w + 15 of the tile.  The first 256 bytes of
+  // each of their staging slots (one dword per lane) are loaded before any
+  // size or offset is known, so the loads overlap the row reads and the
+  // look-back (a raw chunk's slot is never read past this).
   constexpr uint32_t PW = kCTile / kWaves;
-  uint32_t pv[PW];
+  typedef uint32_t pv_t __attribute__((ext_vector_type(PW)));  // a value, never memory
+  pv_t pv;
 #pragma unroll
   for (uint32_t u = 0; u < PW; ++u) {
     const uint64_t c = c0 + wave * PW + u;
     pv[u] = c < num_chunks ? ((const uint32_t*)(staging + c * cs))[lane] : 0u;
   }
-  if (wave == 0) {
-    // sizes of the tile's chunks (one per lane), their scan, and the look-back
-    static_assert(kCTile == 64, "one chunk per lane of the first wave");
+  // Every wave reads the tile's rows (one chunk per lane) and scans the sizes
+  // itself, so only the tile's offset has to be shared.
+  static_assert(kCTile == 64, "one chunk per lane");
+  uint32_t size = 0, raw = 0;
+  {
     const uint64_t c = c0 + lane;
-    uint32_t size = 0;
     if (c < num_chunks) {
       const uint8_t* row = table + kEntryBytes * c;
       uint2 e;
@@ -706,16 +734,13 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(const uint8_t* __restri
       const uint32_t bc = (uint32_t)((n - start) < cs ? (n - start) : cs);
       const uint32_t s0 = entry_payload(e.x, e.y);
       size = s0 < bc ? s0 : bc;
+      raw = (e.x == 0u && (e.y & kRawBit)) ? 1u : 0u;
     }
-    uint32_t inc = size;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t v = __shfl_up(inc, d, 64);
-      if (lane >= (uint32_t)d) inc += v;
-    }
-    sz[lane] = size;
-    off[lane] = inc - size;
-    const uint64_t tot = (uint64_t)__shfl(inc, 63, 64);
+  }
+  const uint32_t inc = wave_incl_add(size);
+  const uint32_t excl = inc - size;
+  if (wave == 0) {
+    const uint64_t tot = (uint64_t)lane63(inc);
     const uint64_t pre = look_back(tile_flags, t, tot, &ctl->error);
     if (lane == 0) {
       tile_pre = pre;
@@ -737,37 +762,50 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(const uint8_t* __restri
     }
   }
   __syncthreads();
-  const uint64_t pre = tile_pre;
+  uint8_t* const dst0 = payload + tile_pre;
+  // the first bytes of every coded payload, from the loaded dwords
 #pragma unroll
   for (uint32_t u = 0; u < PW; ++u) {
     const uint32_t j = wave * PW + u;
-    const uint64_t c = c0 + j;
-    const uint32_t size = c < num_chunks ? sz[j] : 0u;
-    if (size == 0u) continue;
-    uint8_t* dst = payload + pre + off[j];
-    const uint8_t* sb = staging + c * cs;
-    const uint32_t* sw = (const uint32_t*)sb;
+    const uint32_t sz = (uint32_t)__builtin_amdgcn_readlane((int)size, (int)j);
+    if (sz == 0u || __builtin_amdgcn_readlane((int)raw, (int)j)) continue;
+    uint8_t* dst = dst0 + (uint32_t)__builtin_amdgcn_readlane((int)excl, (int)j);
     // head bytes up to dst's next 4-byte boundary, then aligned dwords, then
     // the tail; payload byte b is byte b & 3 of slot dword b >> 2
     const uint32_t a4 = (uint32_t)((4u - ((uintptr_t)dst & 3u)) & 3u);
-    const uint32_t h = a4 > size ? size : a4;
-    const uint32_t nb = (size - h) / 4u;
+    const uint32_t h = a4 > sz ? sz : a4;
+    const uint32_t nb = (sz - h) / 4u;
     const uint32_t d0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)pv[u]);
     if (lane < h) dst[lane] = (uint8_t)(d0 >> (8u * lane));
     uint32_t* dw = (uint32_t*)(dst + h);
     // body dword k takes slot dwords k and k + 1 (the next lane's)
     const uint32_t nxt = dpp0<kWaveShl1>(pv[u]);
     if (lane < (nb < 63u ? nb : 63u)) dw[lane] = __builtin_amdgcn_alignbyte(nxt, pv[u], h);
-    for (uint32_t k = 63u + lane; k < nb; k += 64u) {  // payloads longer than 252 bytes
-      const uint32_t s0 = h + 4u * k;
-      const uint32_t lo = sw[s0 >> 2];
-      const uint32_t hi = h ? sw[(s0 >> 2) + 1u] : 0u;
-      dw[k] = __builtin_amdgcn_alignbyte(hi, lo, h);
+    if (nb < 63u) {
+      const uint32_t tb = h + 4u * nb + lane;  // at most 3 tail bytes, below h + 251
+      const uint32_t tv = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((tb >> 2) & 63u) << 2, (int)pv[u]);
+      if (tb < sz) dst[tb] = (uint8_t)(tv >> (8u * (tb & 3u)));
     }
-    const uint32_t t0 = h + 4u * nb;  // at most 3 tail bytes
-    const uint32_t tb = t0 + lane;
-    const uint32_t tv = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((tb >> 2) & 63u) << 2, (int)pv[u]);
-    if (tb < size) dst[tb] = tb < 256u ? (uint8_t)(tv >> (8u * (tb & 3u))) : sb[tb];
+  }
+  // the rest of coded payloads longer than that, and raw chunks, whose
+  // payload is their input bytes
+#pragma unroll 1
+  for (uint32_t u = 0; u < PW; ++u) {
+    const uint32_t j = wave * PW + u;
+    const uint32_t sz = (uint32_t)__builtin_amdgcn_readlane((int)size, (int)j);
+    if (sz == 0u) continue;
+    uint8_t* dst = dst0 + (uint32_t)__builtin_amdgcn_readlane((int)excl, (int)j);
+    const uint64_t c = c0 + j;
+    if (__builtin_amdgcn_readlane((int)raw, (int)j)) {
+      copy_bytes16(dst, in + c * cs, sz, lane);
+      continue;
+    }
+    const uint32_t a4 = (uint32_t)((4u - ((uintptr_t)dst & 3u)) & 3u);
+    const uint32_t h = a4 > sz ? sz : a4;
+    if ((sz - h) / 4u >= 63u) {
+      const uint32_t done = h + 4u * 63u;
+      copy_bytes16(dst + done, staging + c * cs + done, sz - done, lane);
+    }
   }
 }
 
@@ -965,8 +1003,8 @@ uint64_t encode_tiles(uint32_t num_chunks) { return num_tiles_of(num_chunks); }
 
 hipError_t launch_compact(const EncodeArgs& a, hipStream_t stream) {
   const uint32_t tiles = num_tiles_of(a.num_chunks);
-  hipLaunchKernelGGL(compact_kernel, dim3(tiles ? tiles : 1u), dim3(kBlock), 0, stream, a.staging, a.cs, a.ws, a.n,
-                     a.num_chunks, tiles, a.out, a.out_bytes, a.tile_flags, (EncCtl*)a.ctl);
+  hipLaunchKernelGGL(compact_kernel, dim3(tiles ? tiles : 1u), dim3(kBlock), 0, stream, a.in, a.staging, a.cs,
+                     a.ws, a.n, a.num_chunks, tiles, a.out, a.out_bytes, a.tile_flags, (EncCtl*)a.ctl);
   return hipGetLastError();
 }
 
