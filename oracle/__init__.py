@@ -31,7 +31,7 @@ RAW_BIT = 0x80000000
 def build(verbose: bool = False) -> str:
     """Compile liboracle.so with gcc (always recompiles)."""
     tmp = _LIB_PATH + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-shared", "-fPIC", _SRC, "-o", tmp]
+    cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
@@ -81,6 +81,8 @@ def _load():
     lib.oracle_encode_split.restype = ctypes.c_int
     lib.oracle_decode_split.argtypes = [u8p, u64, u8p, u8p, u64, u8p, u64, u8p, u64]
     lib.oracle_decode_split.restype = ctypes.c_int64
+    lib.oracle_lorenzo_quant.argtypes = [u8p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_double, u8p]
+    lib.oracle_lorenzo_quant.restype = ctypes.c_uint64
     _lib = lib
     return lib
 
@@ -220,3 +222,16 @@ def decode_split(lit, lens, offs, meta) -> np.ndarray:
     if r < 0:
         raise ValueError(f"oracle_decode_split status {r}")
     return out
+
+
+def lorenzo_quant(field, eb: float) -> tuple[np.ndarray, int]:
+    """Lorenzo-quantizer front end: a float32 field of shape (nx,), (ny, nx)
+    or (nz, ny, nx), x fastest, and an absolute error bound -> (u32 codes of
+    the same shape, number of clamped cells)."""
+    f = np.ascontiguousarray(field, dtype=np.float32)
+    if f.ndim not in (1, 2, 3) or f.size == 0:
+        raise ValueError("field must be a non-empty 1-D, 2-D or 3-D array")
+    dims = (1,) * (3 - f.ndim) + f.shape  # (nz, ny, nx)
+    codes = np.empty(f.shape, dtype=np.uint32)
+    clamped = _load().oracle_lorenzo_quant(_ptr(f), dims[2], dims[1], dims[0], float(eb), _ptr(codes))
+    return codes, int(clamped)

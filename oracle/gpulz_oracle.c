@@ -23,6 +23,7 @@
  * omask-AND search, round trips, an independent Python stream walker, an
  * independent level-1 table simulation, corrupted-stream rejection).
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -548,4 +549,41 @@ int64_t oracle_decode_split(const uint8_t* lit, uint64_t lit_n, const uint8_t* l
   if (st != OR_OK) return st;
   if (nf != nf_total) return OR_ECORRUPT;
   return (int64_t)n;
+}
+
+/* ---- Lorenzo-quantizer front end ------------------------------------------
+ * The coder's measured input is Lorenzo-quantized residuals of a float field
+ * (GPULZStage page, results paragraph); LorenzoQuant turns float32 values
+ * into integer codes (its alignment paragraph).  The pages give no formula;
+ * this is the plainest reading, written out cell by cell:
+ *   q(z,y,x) = round-half-even(f(z,y,x) / (2 eb)), in double precision;
+ *   delta    = sum over the corners (dz,dy,dx) in {0,1}^3 of
+ *              (-1)^(dz+dy+dx) q(z-dz, y-dy, x-dx), cells outside the grid 0;
+ *   code     = delta + 32768, clamped to [0, 65535].
+ * Field and codes are x fastest, then y, then z.  Returns the number of
+ * clamped cells.  Parity pins: closed forms (constant and ramp fields), the
+ * inverse (prefix sums of code - 32768 give back q), the error bound
+ * |f - 2 eb q| <= eb, round-half-even ties, clamping. */
+uint64_t oracle_lorenzo_quant(const float* f, uint32_t nx, uint32_t ny, uint32_t nz, double eb, uint32_t* codes) {
+  uint64_t clamped = 0;
+  for (uint32_t z = 0; z < nz; ++z)
+    for (uint32_t y = 0; y < ny; ++y)
+      for (uint32_t x = 0; x < nx; ++x) {
+        int64_t delta = 0;
+        for (uint32_t dz = 0; dz < 2; ++dz)
+          for (uint32_t dy = 0; dy < 2; ++dy)
+            for (uint32_t dx = 0; dx < 2; ++dx) {
+              if (z < dz || y < dy || x < dx) continue; /* outside the grid: 0 */
+              uint64_t at = ((uint64_t)(z - dz) * ny + (y - dy)) * nx + (x - dx);
+              int64_t q = (int64_t)rint((double)f[at] / (2.0 * eb));
+              delta += ((dz + dy + dx) & 1u) ? -q : q;
+            }
+        int64_t code = delta + 32768;
+        if (code < 0 || code > 65535) {
+          ++clamped;
+          code = code < 0 ? 0 : 65535;
+        }
+        codes[((uint64_t)z * ny + y) * nx + x] = (uint32_t)code;
+      }
+  return clamped;
 }
