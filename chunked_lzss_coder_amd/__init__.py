@@ -18,7 +18,8 @@ STATUS_OK, STATUS_CAPACITY, STATUS_CORRUPT = 0, 2, 3
 SYMBOLS = ("gpulz_max_compressed_size", "gpulz_encode_workspace_size", "gpulz_decode_workspace_size",
            "gpulz_encode", "gpulz_decode", "gpulz_stream_info", "gpulz_encode_timed", "gpulz_decode_timed",
            "gpulz_split_bounds", "gpulz_encode_split_workspace_size", "gpulz_encode_split",
-           "gpulz_decode_split_workspace_size", "gpulz_decode_split", "gpulz_decode_one_thread_per_chunk")
+           "gpulz_decode_split_workspace_size", "gpulz_decode_split", "gpulz_decode_one_thread_per_chunk",
+           "gpulz_lorenzo_quant")
 
 _lib = None
 
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
     L.gpulz_decode_split.restype = ctypes.c_int
     L.gpulz_decode_one_thread_per_chunk.argtypes = L.gpulz_decode.argtypes + [vp, vp]
     L.gpulz_decode_one_thread_per_chunk.restype = ctypes.c_int
+    L.gpulz_lorenzo_quant.argtypes = [vp, u32, u32, u32, ctypes.c_double, vp, vp, vp]
+    L.gpulz_lorenzo_quant.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -288,3 +291,30 @@ def decode_split(lit, lens, offs, meta, port_bytes=None, out_capacity: int | Non
     ws = torch.empty(max(decode_split_workspace_size(nm), 1), dtype=torch.uint8, device=dev)
     decode_split_into(lit, nl, lens, offs, nt, meta, nm, out, out_bytes, status, ws, stream)
     return out, out_bytes, status
+
+
+def lorenzo_quant_into(d_field, eb: float, codes, clamped, stream=None) -> None:
+    """Enqueue gpulz_lorenzo_quant (gpulz_lorenzo.h): a float32 CUDA tensor of
+    1, 2 or 3 dimensions (last one fastest) and an absolute error bound ->
+    u32 codes in `codes` (int32 or uint32 tensor, same number of cells) and
+    the clamped-cell count in `clamped` (one 64-bit integer)."""
+    import torch
+    if not d_field.is_cuda or d_field.dtype != torch.float32 or d_field.dim() not in (1, 2, 3):
+        raise GpulzError("field must be a 1-D, 2-D or 3-D float32 CUDA tensor")
+    f = d_field.contiguous()
+    dims = (1,) * (3 - f.dim()) + tuple(f.shape)  # (nz, ny, nx)
+    if codes.numel() != f.numel() or codes.element_size() != 4 or clamped.element_size() != 8:
+        raise GpulzError("codes must hold one 4-byte code per cell, clamped one 8-byte count")
+    _check(lib().gpulz_lorenzo_quant(_ptr(f), dims[2], dims[1], dims[0], float(eb), _ptr(codes), _ptr(clamped),
+                                     _stream(stream)), "gpulz_lorenzo_quant")
+
+
+def lorenzo_quant(d_field, eb: float, stream=None):
+    """Lorenzo-quantize a float32 CUDA tensor; returns (codes as a uint32
+    tensor of the field's shape, clamped count as a one-element int64
+    tensor), both on the device."""
+    import torch
+    codes = torch.empty(d_field.shape, dtype=torch.uint32, device=d_field.device)
+    clamped = torch.zeros(1, dtype=torch.int64, device=d_field.device)
+    lorenzo_quant_into(d_field, eb, codes, clamped, stream)
+    return codes, clamped

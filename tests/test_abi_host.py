@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
                                          "gpulz_stream_info", "gpulz_encode_timed", "gpulz_decode_timed",
                                          "gpulz_split_bounds", "gpulz_encode_split_workspace_size",
                                          "gpulz_encode_split", "gpulz_decode_split_workspace_size",
-                                         "gpulz_decode_split", "gpulz_decode_one_thread_per_chunk"])
+                                         "gpulz_decode_split", "gpulz_decode_one_thread_per_chunk",
+                                         "gpulz_lorenzo_quant"])
 
 
 def test_library_exports_every_declared_symbol(g):
@@ -156,3 +157,21 @@ def test_split_rejects_bad_arguments_before_launch(g):
     assert dec(*a) == g.ERR_CORRUPT
     a = list(dargs); a[12] = need - 1
     assert dec(*a) == g.ERR_CAPACITY
+
+
+def test_lorenzo_quant_rejects_bad_arguments(g):
+    # every call below fails a host check, so nothing is enqueued (the
+    # pointers are never dereferenced)
+    lib = g.lib()
+    p = ctypes.c_void_p(0x1000)
+    q = lambda f, nx, ny, nz, eb, c, k: lib.gpulz_lorenzo_quant(f, nx, ny, nz, eb, c, k, None)
+    assert q(None, 4, 4, 1, 0.1, p, p) == g.ERR_INVALID_ARG
+    assert q(p, 4, 4, 1, 0.1, None, p) == g.ERR_INVALID_ARG
+    assert q(p, 4, 4, 1, 0.1, p, None) == g.ERR_INVALID_ARG
+    for dims in [(0, 4, 1), (4, 0, 1), (4, 4, 0), (1 << 16, 1 << 16, 1), (1 << 11, 1 << 11, 1 << 10)]:
+        assert q(p, *dims, 0.1, p, p) == g.ERR_INVALID_ARG
+    for eb in [0.0, -1.0, float("nan"), float("inf"), 1e308]:
+        assert q(p, 4, 4, 1, eb, p, p) == g.ERR_INVALID_ARG
+    assert q(ctypes.c_void_p(0x1002), 4, 4, 1, 0.1, p, p) == g.ERR_INVALID_ARG
+    assert q(p, 4, 4, 1, 0.1, ctypes.c_void_p(0x1001), p) == g.ERR_INVALID_ARG
+    assert q(p, 4, 4, 1, 0.1, p, ctypes.c_void_p(0x1004)) == g.ERR_INVALID_ARG
