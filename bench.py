@@ -395,6 +395,40 @@ def main(argv=None) -> int:
         mb_, ms_ = float(np.mean([ev.ms(p) for p in kb])), float(np.mean([ev.ms(p) for p in ks]))
         baseline = {"level": lv, "block_decode_kernel_ms": round(mb_, 4),
                     "one_thread_per_chunk_decode_kernel_ms": round(ms_, 4), "speedup": round(ms_ / mb_, 2)}
+    # The Lorenzo-quantizer front end on the device: the workload's float
+    # field -> its u32 codes (they must equal the coder's input), kernel time
+    # and the front end's roofline (4 bytes read + 4 written per cell).
+    front = None
+    fld = synth.field_of(args.workload)
+    if fld is not None and not args.no_split:
+        f32, rel = fld
+        eb = synth.abs_error_bound(f32, rel)
+        d_f = torch.from_numpy(f32).to(dev)
+        codes = torch.empty(f32.shape, dtype=torch.uint32, device=dev)
+        clamped = torch.zeros(1, dtype=torch.int64, device=dev)
+        s_ = torch.cuda.current_stream()
+        ts_ = []
+        for i in range(args.warmup + args.steps):
+            e_ = ev.pair()
+            ev.hip.hipEventRecord(e_[0], ctypes.c_void_p(s_.cuda_stream))
+            g.lorenzo_quant_into(d_f, eb, codes, clamped)
+            ev.hip.hipEventRecord(e_[1], ctypes.c_void_p(s_.cuda_stream))
+            if i >= args.warmup:
+                ts_.append(e_)
+        torch.cuda.synchronize()
+        match = bool(torch.equal(codes.reshape(-1).view(torch.uint8), x))
+        mq = float(np.mean([ev.ms(p_) for p_ in ts_]))
+        cells = f32.size
+        hbm = 8.0 * cells / (mq * 1e-3) / 1e9
+        front = {"field": "x".join(str(d_) for d_ in f32.shape) + " float32", "abs_error_bound": eb,
+                 "ms": round(mq, 4), "field_gbps": round(4.0 * cells / (mq * 1e-3) / 1e9, 3),
+                 "codes_equal_coder_input": match, "clamped": int(clamped.item()),
+                 "roofline": {"bound": "hbm", "achieved": round(hbm, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                              "frac": round(hbm / HBM_PEAK_GBPS, 5)}}
+        if not match:
+            print("bench.py: device Lorenzo codes differ from the coder input", file=sys.stderr)
+            return 1
+        del d_f, codes, clamped
     ev.close()
     if args.calibration_copy_mib > 0:
         a_ = torch.empty(args.calibration_copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -466,6 +500,7 @@ def main(argv=None) -> int:
         "levels": {str(k): v for k, v in res.items()},
         "split": split,
         "decode_baseline": baseline,
+        "lorenzo_front_end": front,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -70,8 +70,7 @@ def _lorenzo_codes(field32: np.ndarray, rel_eb: float) -> tuple[np.ndarray, int]
     """Pre-quantize a float32 field and return uint32 Lorenzo residual codes
     (radius-offset, clamped) plus the number of clamped cells."""
     f = field32.astype(np.float64)
-    rng_ = float(f.max() - f.min())
-    eb = rel_eb * (rng_ if rng_ > 0 else 1.0)
+    eb = abs_error_bound(field32, rel_eb)
     q = np.rint(f / (2.0 * eb)).astype(np.int64)
     # integer Lorenzo predictor: inclusion-exclusion over the lower corner
     # neighbours, cells outside the grid read as 0
@@ -87,23 +86,40 @@ def _lorenzo_codes(field32: np.ndarray, rel_eb: float) -> tuple[np.ndarray, int]
     return np.clip(code, 0, 65535).astype(np.uint32).reshape(-1), clamped
 
 
-def lorenzo2d(seed: int, rows: int, cols: int, rel_eb: float, noise: float = 0.0,
-              zero_frac: float = 0.0) -> tuple[np.ndarray, int]:
+def field2d(seed: int, rows: int, cols: int, noise: float = 0.0, zero_frac: float = 0.0) -> np.ndarray:
+    """The float32 field behind the 2-D Lorenzo workloads."""
     rng = np.random.default_rng(seed)
     f = _sinusoid_field(rng, (rows, cols))
     if noise > 0:
         f = f + rng.normal(0.0, noise, size=f.shape)
     if zero_frac > 0:
         f[_zero_patches(rng, (rows, cols), zero_frac)] = 0.0
-    return _lorenzo_codes(f.astype(np.float32), rel_eb)
+    return f.astype(np.float32)
 
 
-def lorenzo3d(seed: int, nz: int, ny: int, nx: int, rel_eb: float, zero_frac: float = 0.0):
+def field3d(seed: int, nz: int, ny: int, nx: int, zero_frac: float = 0.0) -> np.ndarray:
+    """The float32 field behind the 3-D Lorenzo workload."""
     rng = np.random.default_rng(seed)
     f = _sinusoid_field(rng, (nz, ny, nx))
     if zero_frac > 0:
         f[_zero_patches(rng, (nz, ny, nx), zero_frac)] = 0.0
-    return _lorenzo_codes(f.astype(np.float32), rel_eb)
+    return f.astype(np.float32)
+
+
+def abs_error_bound(field32: np.ndarray, rel_eb: float) -> float:
+    """Absolute error bound of a relative one: rel_eb times the value range."""
+    f = field32.astype(np.float64)
+    rng_ = float(f.max() - f.min())
+    return rel_eb * (rng_ if rng_ > 0 else 1.0)
+
+
+def lorenzo2d(seed: int, rows: int, cols: int, rel_eb: float, noise: float = 0.0,
+              zero_frac: float = 0.0) -> tuple[np.ndarray, int]:
+    return _lorenzo_codes(field2d(seed, rows, cols, noise, zero_frac), rel_eb)
+
+
+def lorenzo3d(seed: int, nz: int, ny: int, nx: int, rel_eb: float, zero_frac: float = 0.0):
+    return _lorenzo_codes(field3d(seed, nz, ny, nx, zero_frac), rel_eb)
 
 
 def byte_mix(seed: int, n: int, fractions=(0.60, 0.25, 0.15)) -> tuple[np.ndarray, dict]:
@@ -231,6 +247,18 @@ WORKLOAD_NAMES = (
     "bytemix_64MiB_u8_cs4096",            # 64 MiB, ws 1, levels 0 and 1
     "stress_2GiB_u32_cs4096",             # 2 GiB, level 1 (+ level 0 row)
 )
+
+
+def field_of(idx: int) -> tuple[np.ndarray, float] | None:
+    """(float32 field, relative error bound) behind workload idx, for the
+    Lorenzo-field workloads (0, 1, 2); None for the others."""
+    if idx == 0:
+        return field2d(0, 512, 512, noise=0.01), 1e-3
+    if idx == 1:
+        return field2d(1, 1800, 3600, zero_frac=0.30), 1e-4
+    if idx == 2:
+        return field3d(2, 100, 256, 256, zero_frac=0.30), 1e-4
+    return None
 
 
 def workload(idx: int, scale_bytes: int | None = None) -> Workload:
