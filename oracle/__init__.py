@@ -81,6 +81,12 @@ def _load():
     lib.oracle_encode_split.restype = ctypes.c_int
     lib.oracle_decode_split.argtypes = [u8p, u64, u8p, u8p, u64, u8p, u64, u8p, u64]
     lib.oracle_decode_split.restype = ctypes.c_int64
+    lib.oracle_near_match_w.argtypes = [u8p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                        ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32)]
+    lib.oracle_near_match_w.restype = None
+    lib.oracle_encode_w.argtypes = [u8p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                    ctypes.c_uint32, u8p, ctypes.c_uint64]
+    lib.oracle_encode_w.restype = ctypes.c_int64
     lib.oracle_lorenzo_quant.argtypes = [u8p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_double, u8p]
     lib.oracle_lorenzo_quant.restype = ctypes.c_uint64
     _lib = lib
@@ -105,11 +111,15 @@ def hash2(w0: int, w1: int) -> int:
     return int(_load().oracle_hash(w0, w1))
 
 
-def near_match(x: np.ndarray, p: int) -> tuple[int, int]:
-    """(L, O) of the exact near-window search at element p of chunk x (uint32)."""
+def near_match(x: np.ndarray, p: int, window: int = 32) -> tuple[int, int]:
+    """(L, O) of the exact near-window search (offsets 1..window) at element p
+    of chunk x (uint32)."""
     x = np.ascontiguousarray(x, dtype=np.uint32)
     L, O = ctypes.c_uint32(), ctypes.c_uint32()
-    _load().oracle_near_match(_ptr(x), x.size, p, ctypes.byref(L), ctypes.byref(O))
+    if window == 32:
+        _load().oracle_near_match(_ptr(x), x.size, p, ctypes.byref(L), ctypes.byref(O))
+    else:
+        _load().oracle_near_match_w(_ptr(x), x.size, p, window, ctypes.byref(L), ctypes.byref(O))
     return L.value, O.value
 
 
@@ -134,14 +144,18 @@ def encode_chunk(chunk: bytes | np.ndarray, chunk_size: int, word_size: int, lev
     return f.value, d.value, pay[:pb.value].tobytes()
 
 
-def encode(data, chunk_size: int, word_size: int, level: int) -> np.ndarray:
-    """Encode a whole buffer; returns the stream as a uint8 array."""
+def encode(data, chunk_size: int, word_size: int, level: int, window: int = 32) -> np.ndarray:
+    """Encode a whole buffer (near window of `window` offsets: 32, 48 or 64);
+    returns the stream as a uint8 array."""
     a = _bytes(data)
     cap = max_stream_size(a.size, chunk_size)
     if cap == 0:
         raise ValueError("unsupported chunk_size")
     out = np.empty(cap, dtype=np.uint8)
-    r = _load().oracle_encode(_ptr(a), a.size, chunk_size, word_size, level, _ptr(out), cap)
+    if window == 32:
+        r = _load().oracle_encode(_ptr(a), a.size, chunk_size, word_size, level, _ptr(out), cap)
+    else:
+        r = _load().oracle_encode_w(_ptr(a), a.size, chunk_size, word_size, level, window, _ptr(out), cap)
     if r < 0:
         raise ValueError(f"oracle_encode status {r}")
     return out[:r]

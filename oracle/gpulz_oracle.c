@@ -97,18 +97,30 @@ static uint32_t run_at(const uint32_t* x, uint32_t E, uint32_t p, uint32_t o) {
   return k;
 }
 
-/* Exact longest match over the near window at position p (page: exact
- * longest-match search; offsets 1..32, never before the chunk start).
- * Ties on length go to the smallest offset.  L = 0 means no offset matches. */
-void oracle_near_match(const uint32_t* x, uint32_t E, uint32_t p, uint32_t* L, uint32_t* O) {
+/* Near windows the encoder accepts: the fixed 32 of the stage, and the 48
+ * and 64 the page measured (window-width paragraph: ratio 4.36x at 32,
+ * 4.82x at 48, 5.13x at 64).  The window is an encode-side choice only:
+ * offsets up to 64 fit the token's offset byte, the stream is unchanged. */
+static int window_ok(uint32_t w) { return w == 32u || w == 48u || w == 64u; }
+
+/* Exact longest match over a near window of `window` offsets at position p
+ * (page: exact longest-match search; offsets 1..window, never before the
+ * chunk start).  Ties on length go to the smallest offset.  L = 0 means no
+ * offset matches. */
+void oracle_near_match_w(const uint32_t* x, uint32_t E, uint32_t p, uint32_t window, uint32_t* L, uint32_t* O) {
   uint32_t bestL = 0, bestO = 0;
-  uint32_t omax = p < OR_WINDOW ? p : OR_WINDOW;
+  uint32_t omax = p < window ? p : window;
   for (uint32_t o = 1; o <= omax; ++o) {
     uint32_t k = run_at(x, E, p, o);
     if (k > bestL) { bestL = k; bestO = o; }
   }
   *L = bestL;
   *O = bestO;
+}
+
+/* The stage's own near window: offsets 1..32 (page: window paragraph). */
+void oracle_near_match(const uint32_t* x, uint32_t E, uint32_t p, uint32_t* L, uint32_t* O) {
+  oracle_near_match_w(x, E, p, OR_WINDOW, L, O);
 }
 
 /* Level-1 candidates for every position of one chunk (page: hashed
@@ -156,10 +168,10 @@ static uint32_t min_match(uint32_t ws) { return ws >= 4u ? 1u : (ws == 2u ? 2u :
  * *flag_size / *data_size hold the 8-byte size-table entry and payload[]
  * (capacity >= cs) holds *payload_bytes bytes.
  * Returns OR_OK or OR_EINVAL. */
-int oracle_encode_chunk(const uint8_t* bytes, uint32_t bc, uint32_t cs, uint32_t ws, uint32_t level,
-                        uint32_t* flag_size, uint32_t* data_size, uint8_t* payload,
-                        uint32_t* payload_bytes) {
-  if (!cs_ok(cs) || !ws_ok(ws) || level > 1u || bc == 0 || bc > cs) return OR_EINVAL;
+int oracle_encode_chunk_w(const uint8_t* bytes, uint32_t bc, uint32_t cs, uint32_t ws, uint32_t level,
+                          uint32_t window, uint32_t* flag_size, uint32_t* data_size, uint8_t* payload,
+                          uint32_t* payload_bytes) {
+  if (!cs_ok(cs) || !ws_ok(ws) || level > 1u || !window_ok(window) || bc == 0 || bc > cs) return OR_EINVAL;
   uint32_t E = cs / ws;
   uint8_t* padded = (uint8_t*)calloc(cs, 1);
   memcpy(padded, bytes, bc);
@@ -194,7 +206,7 @@ int oracle_encode_chunk(const uint8_t* bytes, uint32_t bc, uint32_t cs, uint32_t
   uint32_t p = 0;
   while (p < E) {
     uint32_t L, O;
-    oracle_near_match(x, E, p, &L, &O);
+    oracle_near_match_w(x, E, p, window, &L, &O);
     if (cand && cand[p] != 0) {
       uint32_t r = run_at(x, E, p, cand[p]);
       if (r > L) { L = r; O = cand[p]; } /* hash wins only when strictly longer */
@@ -245,14 +257,19 @@ int oracle_encode_chunk(const uint8_t* bytes, uint32_t bc, uint32_t cs, uint32_t
   return OR_OK;
 }
 
+int oracle_encode_chunk(const uint8_t* bytes, uint32_t bc, uint32_t cs, uint32_t ws, uint32_t level,
+                        uint32_t* flag_size, uint32_t* data_size, uint8_t* payload, uint32_t* payload_bytes) {
+  return oracle_encode_chunk_w(bytes, bc, cs, ws, level, OR_WINDOW, flag_size, data_size, payload, payload_bytes);
+}
+
 /* Encode a whole buffer into one stream:
  *   32-byte header | num_chunks x {u32 flag_size, u32 data_size} | payloads
  * Payloads are packed back to back in chunk order; chunk offsets are not
  * stored (page: CUDA-graph paragraph, the inverse derives them from sizes).
  * Returns the stream length, or a negative status. */
-int64_t oracle_encode(const uint8_t* in, uint64_t n, uint32_t cs, uint32_t ws, uint32_t level,
-                      uint8_t* out, uint64_t cap) {
-  if (!cs_ok(cs) || !ws_ok(ws) || level > 1u) return OR_EINVAL;
+int64_t oracle_encode_w(const uint8_t* in, uint64_t n, uint32_t cs, uint32_t ws, uint32_t level, uint32_t window,
+                        uint8_t* out, uint64_t cap) {
+  if (!cs_ok(cs) || !ws_ok(ws) || level > 1u || !window_ok(window)) return OR_EINVAL;
   if (n > 0 && in == NULL) return OR_EINVAL;
   uint64_t chunks = (n + cs - 1) / cs;
   if (chunks > 0xFFFFFFFFull) return OR_EINVAL;
@@ -265,7 +282,7 @@ int64_t oracle_encode(const uint8_t* in, uint64_t n, uint32_t cs, uint32_t ws, u
     uint64_t start = c * cs;
     uint32_t bc = (uint32_t)((n - start) < cs ? (n - start) : cs);
     uint32_t f, d, pb;
-    int st = oracle_encode_chunk(in + start, bc, cs, ws, level, &f, &d, pay + total, &pb);
+    int st = oracle_encode_chunk_w(in + start, bc, cs, ws, level, window, &f, &d, pay + total, &pb);
     if (st != OR_OK) return st;
     put_u32(table + OR_ENTRY_BYTES * c, f);
     put_u32(table + OR_ENTRY_BYTES * c + 4, d);
@@ -281,6 +298,11 @@ int64_t oracle_encode(const uint8_t* in, uint64_t n, uint32_t cs, uint32_t ws, u
   put_u64(out + 16, n);
   put_u64(out + 24, total);
   return (int64_t)(OR_HEADER_BYTES + OR_ENTRY_BYTES * chunks + total);
+}
+
+int64_t oracle_encode(const uint8_t* in, uint64_t n, uint32_t cs, uint32_t ws, uint32_t level, uint8_t* out,
+                      uint64_t cap) {
+  return oracle_encode_w(in, n, cs, ws, level, OR_WINDOW, out, cap);
 }
 
 /* Read the header.  Returns OR_OK or OR_ECORRUPT. */

@@ -165,6 +165,57 @@ def test_near_match_cap_and_window(oracle_mod):
         assert oracle_mod.near_match(x[:300], p) == brute_near(list(x[:300]), p)
 
 
+# ------------------------------------------------ wider near windows ------
+
+def brute_near_w(x, p, window):
+    """brute_near with offsets 1..window."""
+    E = len(x)
+    best, bo = 0, 0
+    for o in range(1, min(window, p) + 1):
+        L = 0
+        while L < 255 and p + L < E and x[p + L] == x[p + L - o]:
+            L += 1
+        if L > best:
+            best, bo = L, o
+    return best, bo
+
+
+@pytest.mark.parametrize("window", [48, 64])
+def test_near_match_window_brute_force(oracle_mod, window):
+    rng = np.random.default_rng(window)
+    for _ in range(20):
+        x = rng.integers(0, 3, size=int(rng.integers(60, 200))).astype(np.uint32)
+        seq = x.tolist()
+        for p in range(x.size):
+            assert oracle_mod.near_match(x, p, window) == brute_near_w(seq, p, window), (window, p)
+
+
+@pytest.mark.parametrize("window", [48, 64])
+def test_near_match_window_periods(oracle_mod, window):
+    # a period is reachable exactly when it is at most the window
+    for per, want in [(window, window), (window + 1, 0), (33, 33), (32, 32)]:
+        z = np.resize(np.arange(per, dtype=np.uint32), 400)
+        L, O = oracle_mod.near_match(z, 150, window)
+        assert O == want and (L == 0) == (want == 0), (per, L, O)
+    # window 32 still behaves as the stage's own search
+    z = np.resize(np.arange(40, dtype=np.uint32), 300)
+    assert oracle_mod.near_match(z, 100, 32) == oracle_mod.near_match(z, 100) == (0, 0)
+
+
+@pytest.mark.parametrize("window", [32, 48, 64])
+def test_encode_window_round_trip(oracle_mod, window):
+    rng = np.random.default_rng(window + 1)
+    base = rng.integers(0, 1000, size=60).astype(np.uint32)
+    x = np.concatenate([np.resize(base[:per], 1000) for per in (20, 40, 50, 60, 70)]).astype("<u4")
+    data = x.view(np.uint8)
+    s = oracle_mod.encode(data, 2048, 4, 0, window)
+    assert np.array_equal(oracle_mod.decode(s), data)
+    if window == 32:
+        assert np.array_equal(s, oracle_mod.encode(data, 2048, 4, 0))
+    # wider windows never code the periodic segments worse
+    assert s.size <= oracle_mod.encode(data, 2048, 4, 0, 32).size
+
+
 # ----------------------------------------------------------- level 1 ------
 
 def closed_form_candidates(x: np.ndarray):
