@@ -5,6 +5,7 @@
 #include "gpulz_timing.h"
 #include "gpulz_split.h"
 #include "gpulz_baseline.h"
+#include "gpulz_window.h"
 
 #include "common.h"
 
@@ -102,11 +103,14 @@ uint64_t gpulz_encode_workspace_size(uint64_t n_bytes, uint32_t chunk_size) {
 
 uint64_t gpulz_decode_workspace_size(uint64_t in_bytes) { return dec_layout(dec_chunks_bound(in_bytes)).total; }
 
-int gpulz_encode_timed(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, uint32_t word_size,
-                       uint32_t match_level, void* d_out, uint64_t out_capacity, uint64_t* d_out_bytes,
-                       void* d_workspace, uint64_t workspace_bytes, hipStream_t stream, hipEvent_t ev_start,
-                       hipEvent_t ev_stop) {
+}  // extern "C"
+
+namespace {
+int encode_common(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, uint32_t word_size, uint32_t match_level,
+                  uint32_t window, void* d_out, uint64_t out_capacity, uint64_t* d_out_bytes, void* d_workspace,
+                  uint64_t workspace_bytes, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (!chunk_size_ok(chunk_size) || !word_size_ok(word_size) || match_level > 1u) return GPULZ_ERR_INVALID_ARG;
+  if (window != 32u && window != 48u && window != 64u) return GPULZ_ERR_INVALID_ARG;
   if ((n_bytes > 0 && d_in == nullptr) || d_out == nullptr || d_out_bytes == nullptr || d_workspace == nullptr)
     return GPULZ_ERR_INVALID_ARG;
   const uint64_t chunks = num_chunks_of(n_bytes, chunk_size);
@@ -123,6 +127,7 @@ int gpulz_encode_timed(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, 
   ea.cs = chunk_size;
   ea.ws = word_size;
   ea.level = match_level;
+  ea.window = window;
   ea.num_chunks = (uint32_t)chunks;
   ea.out = (uint8_t*)d_out;
   ea.out_bytes = d_out_bytes;
@@ -134,6 +139,24 @@ int gpulz_encode_timed(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, 
   if (ev_stop && hipEventRecord(ev_stop, stream) != hipSuccess) return GPULZ_ERR_HIP;
   if (launch_compact(ea, stream) != hipSuccess) return GPULZ_ERR_HIP;
   return GPULZ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int gpulz_encode_timed(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, uint32_t word_size,
+                       uint32_t match_level, void* d_out, uint64_t out_capacity, uint64_t* d_out_bytes,
+                       void* d_workspace, uint64_t workspace_bytes, hipStream_t stream, hipEvent_t ev_start,
+                       hipEvent_t ev_stop) {
+  return encode_common(d_in, n_bytes, chunk_size, word_size, match_level, kWindow, d_out, out_capacity,
+                       d_out_bytes, d_workspace, workspace_bytes, stream, ev_start, ev_stop);
+}
+
+int gpulz_encode_window(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, uint32_t word_size,
+                        uint32_t match_level, uint32_t window, void* d_out, uint64_t out_capacity,
+                        uint64_t* d_out_bytes, void* d_workspace, uint64_t workspace_bytes, hipStream_t stream) {
+  return encode_common(d_in, n_bytes, chunk_size, word_size, match_level, window, d_out, out_capacity, d_out_bytes,
+                       d_workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
 int gpulz_encode(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, uint32_t word_size, uint32_t match_level,

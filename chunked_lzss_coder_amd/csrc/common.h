@@ -238,6 +238,7 @@ struct EncodeArgs {
   uint8_t* lens = nullptr;
   uint8_t* offs = nullptr;
   uint64_t* port_bytes = nullptr;  // [4]: literals, lengths, offsets, meta
+  uint32_t window = kWindow;        // near-window offsets: 32, 48 or 64
 };
 uint64_t encode_ctl_bytes();
 uint64_t encode_tiles(uint32_t num_chunks);

@@ -174,32 +174,49 @@ struct EncCtl {
 constexpr uint32_t kCTile = 64;  // chunks per compaction tile
 __host__ __device__ inline uint32_t num_tiles_of(uint32_t chunks) { return (chunks + kCTile - 1u) / kCTile; }
 
-template <int WS, int E, int LEVEL>
+// Offset masks: one bit per near-window offset, 32 or 64 bits.
+template <int W>
+struct MaskOf {
+  using T = uint32_t;
+};
+template <>
+struct MaskOf<48> {
+  using T = uint64_t;
+};
+template <>
+struct MaskOf<64> {
+  using T = uint64_t;
+};
+
+template <int WS, int E, int LEVEL, int W>
 struct Lay {
   static constexpr uint32_t CS = (uint32_t)E * WS;
+  static constexpr uint32_t MW = W > 32 ? 2u : 1u;  // words per offset mask
   static constexpr uint32_t NW64 = E / 64;  // 64-position words
   static constexpr uint32_t NSEG = E / 8;   // 8-position parse segments
   // Word offsets inside the per-chunk region, after X[E]:
-  //   search: LV = S_1 | S_4 | S_16 | S_64, each E words followed by zero
-  //           padding that the descent may read (3, 9, 33, 129 words, rounded)
+  //   search: LV = S_1 | S_4 | S_16 | S_64, each E masks followed by zero
+  //           padding that the descent may read (3, 9, 33, 129 masks, rounded)
   //   level 1: LO (E) | hash table (2048)
   //   parse:   LO (E) | XQ (E) | ISB (E/32) | LMB (E/32) | FLG (E/32) | STG (CS/4 + 8)
   static constexpr uint32_t RP = 2u * E + 3u * (E / 32u) + CS / 4u + 8u;
-  static constexpr uint32_t TOFF[4] = {0u, E + 4u, 2u * E + 16u, 3u * E + 52u};  // table offsets in LV
-  static constexpr uint32_t SEARCH = 4u * E + 184u;
+  static constexpr uint32_t TOFF[4] = {0u, E + 4u, 2u * E + 16u, 3u * E + 52u};  // table offsets, in masks
+  static constexpr uint32_t SEARCH = MW * (4u * E + 184u);
   static constexpr uint32_t R = (cmax(cmax(SEARCH, LEVEL ? (uint32_t)E + kHashSize : 0u), RP) + 3u) & ~3u;
   static constexpr uint32_t MISC = 2u * (E / 64u + 1u) + 8u;
   static constexpr uint32_t TOTAL = (E + R + MISC + 3u) & ~3u;  // words per chunk, 16-byte multiple
 };
 
-template <int WS, int E, int LEVEL, int WPC, int CPW>
+template <int WS, int E, int LEVEL, int W, int WPC, int CPW>
 __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* __restrict__ in, uint64_t n,
                                                                  uint32_t num_chunks, uint8_t* __restrict__ out,
                                                                  uint8_t* __restrict__ staging,
                                                                  uint64_t* __restrict__ tile_flags,
                                                                  uint32_t num_tiles, uint32_t flag_sets,
                                                                  uint2* __restrict__ km, EncCtl* __restrict__ ctl) {
-  using L = Lay<WS, E, LEVEL>;
+  using L = Lay<WS, E, LEVEL, W>;
+  using Mask = typename MaskOf<W>::T;
+  static_assert(W == 32 || W == 48 || W == 64, "near window");
   constexpr uint32_t CS = L::CS;
   constexpr uint32_t TL = 64u * WPC;  // lanes per team
   constexpr uint32_t PPL = E / TL;    // positions per lane (strided p = g + i*TL)
@@ -213,6 +230,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
   const uint32_t lane = lane_id();
   uint32_t* X = lds_all + team * L::TOTAL;
   uint32_t* LV = X + E;
+  Mask* LVm = (Mask*)LV;  // the search tables
   uint32_t* LO = LV;
   uint32_t* XQ = LV + E;
   uint32_t* T = LV + E;
@@ -281,7 +299,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
   uint32_t kb[WPC == 1 ? NR : 1], mb[WPC == 1 ? NR : 1];
   if (nonzero) {
     // ---- 2. omask: 8 consecutive positions per lane, window in registers -------------
-    uint32_t any_om = 0;  // OR of this lane's masks
+    Mask any_om = 0;  // OR of this lane's masks
     {
       constexpr uint32_t PPASS = (E == 256 ? 4u : 8u);  // positions per lane per pass
       constexpr uint32_t NPASS = E / (PPASS * TL);
@@ -305,7 +323,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             w[i] = idx >= 0 ? X[idx] : 0u;
           }
         }
-        uint32_t om[PPASS];
+        Mask om[PPASS];
 #pragma unroll
         for (uint32_t q = 0; q < PPASS; ++q) {
           // offsets 32..17, then 16..1: bit o-1 compares w[32+q] with w[32+q-o]
@@ -314,11 +332,43 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
           match_bits16(m, &w[q + 16], w[32 + q]);
           const uint32_t p = p0 + q;
           om[q] = p >= 32u ? m : (m & ((1u << p) - 1u));
-          any_om |= om[q];
+        }
+        if constexpr (W > 32) {
+          // offsets 33..W into bits 32..W-1, from the W - 32 + PPASS words
+          // X[p0 - W ..]; offsets past the chunk start are masked off
+          constexpr uint32_t HW = (uint32_t)W - 32u;
+          uint32_t w2[HW + PPASS];
+          if (p0 >= (uint32_t)W) {
+#pragma unroll
+            for (uint32_t i = 0; i < (HW + PPASS) / 4; ++i) {
+              const uint4 v = *(const uint4*)(X + p0 - (uint32_t)W + 4u * i);
+              w2[4 * i] = v.x;
+              w2[4 * i + 1] = v.y;
+              w2[4 * i + 2] = v.z;
+              w2[4 * i + 3] = v.w;
+            }
+          } else {
+#pragma unroll
+            for (uint32_t i = 0; i < HW + PPASS; ++i) {
+              const int32_t idx = (int32_t)p0 - W + (int32_t)i;
+              w2[i] = idx >= 0 ? X[idx] : 0u;
+            }
+          }
+#pragma unroll
+          for (uint32_t q = 0; q < PPASS; ++q) {
+            uint32_t hm = 0;
+#pragma unroll
+            for (uint32_t h = 0; h < HW / 16u; ++h) match_bits16(hm, &w2[q + 16u * h], w[32 + q]);
+            const uint32_t p = p0 + q;
+            hm = p >= (uint32_t)W ? hm : (p > 32u ? (hm & ((1u << (p - 32u)) - 1u)) : 0u);
+            om[q] |= (Mask)hm << 32;
+          }
         }
 #pragma unroll
-        for (uint32_t i = 0; i < PPASS / 4; ++i)
-          *(uint4*)(LV + p0 + 4 * i) = make_uint4(om[4 * i], om[4 * i + 1], om[4 * i + 2], om[4 * i + 3]);
+        for (uint32_t q = 0; q < PPASS; ++q) {
+          any_om |= om[q];
+          LVm[p0 + q] = om[q];
+        }
       }
     }
     // No near match anywhere in the chunk: every length is 0.  At level 0 the
@@ -326,10 +376,10 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
     // and the search and parse are skipped; level 1 still runs its table.
     bool near;
     if (WPC == 1) {
-      near = __ballot(any_om != 0u) != 0ull;
+      near = __ballot(any_om != 0) != 0ull;
       wave_sync();
     } else {
-      near = __syncthreads_or(any_om != 0u);
+      near = __syncthreads_or(any_om != 0);
     }
     if (LEVEL == 0 && !near) {
       K = (uint32_t)E;
@@ -341,17 +391,17 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
         // bounds checks.
         for (uint32_t i = g; i < 184u; i += TL) {  // padding word i of level lv is at (lv + 1) E + i
           const uint32_t lv = i < 4u ? 0u : (i < 16u ? 1u : (i < 52u ? 2u : 3u));
-          LV[(lv + 1u) * (uint32_t)E + i] = 0u;
+          LVm[(lv + 1u) * (uint32_t)E + i] = 0;
         }
 #pragma unroll
         for (uint32_t lv = 1; lv < 4; ++lv) {
           const uint32_t k = 1u << (2 * lv), step = k >> 2;
-          const uint32_t* prev = LV + L::TOFF[lv - 1];
-          uint32_t* cur = LV + L::TOFF[lv];
+          const Mask* prev = LVm + L::TOFF[lv - 1];
+          Mask* cur = LVm + L::TOFF[lv];
 #pragma unroll
           for (uint32_t i = 0; i < PPL; ++i) {
             const uint32_t p = g + i * TL;
-            uint32_t v = 0;
+            Mask v = 0;
             if (p + k <= (uint32_t)E) v = prev[p] & prev[p + step] & prev[p + 2 * step] & prev[p + 3 * step];
             cur[p] = v;
           }
@@ -361,7 +411,8 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
 #pragma unroll
         for (uint32_t i = 0; i < PPL; ++i) {
           const uint32_t p = g + i * TL;
-          uint32_t surv = ~0u, Ln = 0;
+          Mask surv = ~(Mask)0;
+          uint32_t Ln = 0;
           // digits of L in base 4, most significant first: at most 3 steps of k per
           // round, so L <= 3 * (64 + 16 + 4 + 1) = 255, the length cap
 #pragma unroll
@@ -369,13 +420,14 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             const uint32_t k = 1u << (2 * lv);
             // p + Ln <= E (every surviving position is inside the chunk), so the
             // three reads end within the table's padding
-            const uint32_t* S = LV + L::TOFF[lv] + p + Ln;
-            const uint32_t t1 = surv & S[0], t2 = t1 & S[k], t3 = t2 & S[2u * k];
-            const uint32_t n = (uint32_t)(t1 != 0u) + (uint32_t)(t2 != 0u) + (uint32_t)(t3 != 0u);
+            const Mask* S = LVm + L::TOFF[lv] + p + Ln;
+            const Mask t1 = surv & S[0], t2 = t1 & S[k], t3 = t2 & S[2u * k];
+            const uint32_t n = (uint32_t)(t1 != 0) + (uint32_t)(t2 != 0) + (uint32_t)(t3 != 0);
             surv = t3 ? t3 : (t2 ? t2 : (t1 ? t1 : surv));
             Ln += n << (2 * lv);
           }
-          lo[i] = Ln ? (Ln | (((uint32_t)__builtin_ctz(surv) + 1u) << 8)) : 0u;
+          const uint32_t o = W > 32 ? (uint32_t)__builtin_ctzll((uint64_t)surv) : (uint32_t)__builtin_ctz((uint32_t)surv);
+          lo[i] = Ln ? (Ln | ((o + 1u) << 8)) : 0u;
         }
         team_sync<WPC>();
 #pragma unroll
@@ -977,7 +1029,7 @@ __global__ __launch_bounds__(kBlock) void split_compact_kernel(
   }
 }
 
-template <int WS, int E, int LEVEL>
+template <int WS, int E, int LEVEL, int W>
 hipError_t launch_one(const EncodeArgs& a, hipStream_t stream) {
   // waves per chunk: one up to 512 elements (two chunks per workgroup), then
   // one per 512 elements, so LDS per wave stays the same and occupancy holds
@@ -985,15 +1037,25 @@ hipError_t launch_one(const EncodeArgs& a, hipStream_t stream) {
   constexpr int CPW = E <= 512 ? 2 : 1;
   constexpr uint32_t threads = 64u * WPC * CPW;
   const uint32_t grid = (a.num_chunks + CPW - 1) / CPW;  // one chunk per team
-  hipLaunchKernelGGL((encode_kernel<WS, E, LEVEL, WPC, CPW>), dim3(grid), dim3(threads), 0, stream, a.in, a.n,
+  hipLaunchKernelGGL((encode_kernel<WS, E, LEVEL, W, WPC, CPW>), dim3(grid), dim3(threads), 0, stream, a.in, a.n,
                      a.num_chunks, a.out, a.staging, a.tile_flags, num_tiles_of(a.num_chunks),
                      a.km ? 3u : 1u, a.km, (EncCtl*)a.ctl);
   return hipGetLastError();
 }
 
-template <int WS, int E>
+template <int WS, int E, int W>
 hipError_t launch_level(const EncodeArgs& a, hipStream_t stream) {
-  return a.level ? launch_one<WS, E, 1>(a, stream) : launch_one<WS, E, 0>(a, stream);
+  return a.level ? launch_one<WS, E, 1, W>(a, stream) : launch_one<WS, E, 0, W>(a, stream);
+}
+
+template <int WS, int E>
+hipError_t launch_window(const EncodeArgs& a, hipStream_t stream) {
+  switch (a.window) {
+    case 32u: return launch_level<WS, E, 32>(a, stream);
+    case 48u: return launch_level<WS, E, 48>(a, stream);
+    case 64u: return launch_level<WS, E, 64>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -1019,15 +1081,15 @@ hipError_t launch_split_compact(const EncodeArgs& a, hipStream_t stream) {
 hipError_t launch_encode_chunks(const EncodeArgs& a, hipStream_t stream) {
   if (a.num_chunks == 0) return hipSuccess;
   switch (a.cs * 8u + a.ws) {
-    case 1024u * 8u + 1u: return launch_level<1, 1024>(a, stream);
-    case 1024u * 8u + 2u: return launch_level<2, 512>(a, stream);
-    case 1024u * 8u + 4u: return launch_level<4, 256>(a, stream);
-    case 2048u * 8u + 1u: return launch_level<1, 2048>(a, stream);
-    case 2048u * 8u + 2u: return launch_level<2, 1024>(a, stream);
-    case 2048u * 8u + 4u: return launch_level<4, 512>(a, stream);
-    case 4096u * 8u + 1u: return launch_level<1, 4096>(a, stream);
-    case 4096u * 8u + 2u: return launch_level<2, 2048>(a, stream);
-    case 4096u * 8u + 4u: return launch_level<4, 1024>(a, stream);
+    case 1024u * 8u + 1u: return launch_window<1, 1024>(a, stream);
+    case 1024u * 8u + 2u: return launch_window<2, 512>(a, stream);
+    case 1024u * 8u + 4u: return launch_window<4, 256>(a, stream);
+    case 2048u * 8u + 1u: return launch_window<1, 2048>(a, stream);
+    case 2048u * 8u + 2u: return launch_window<2, 1024>(a, stream);
+    case 2048u * 8u + 4u: return launch_window<4, 512>(a, stream);
+    case 4096u * 8u + 1u: return launch_window<1, 4096>(a, stream);
+    case 4096u * 8u + 2u: return launch_window<2, 2048>(a, stream);
+    case 4096u * 8u + 4u: return launch_window<4, 1024>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
                                          "gpulz_split_bounds", "gpulz_encode_split_workspace_size",
                                          "gpulz_encode_split", "gpulz_decode_split_workspace_size",
                                          "gpulz_decode_split", "gpulz_decode_one_thread_per_chunk",
-                                         "gpulz_lorenzo_quant"])
+                                         "gpulz_lorenzo_quant", "gpulz_encode_window"])
 
 
 def test_library_exports_every_declared_symbol(g):
@@ -175,3 +175,12 @@ def test_lorenzo_quant_rejects_bad_arguments(g):
     assert q(ctypes.c_void_p(0x1002), 4, 4, 1, 0.1, p, p) == g.ERR_INVALID_ARG
     assert q(p, 4, 4, 1, 0.1, ctypes.c_void_p(0x1001), p) == g.ERR_INVALID_ARG
     assert q(p, 4, 4, 1, 0.1, p, ctypes.c_void_p(0x1004)) == g.ERR_INVALID_ARG
+
+
+def test_encode_window_rejects_bad_windows(g):
+    lib = g.lib()
+    p = ctypes.c_void_p(0x1000)
+    for window in (0, 16, 31, 33, 40, 96, 128):
+        # a bad window fails before any launch (pointers never dereferenced)
+        assert lib.gpulz_encode_window(p, 4096, 2048, 4, 0, window, p, 1 << 20, p, p, 1 << 30, None) \
+            == g.ERR_INVALID_ARG
