@@ -429,6 +429,35 @@ def main(argv=None) -> int:
             print("bench.py: device Lorenzo codes differ from the coder input", file=sys.stderr)
             return 1
         del d_f, codes, clamped
+    # Near-window and chunk-size sweep (the pages' ratio trade): ratio and
+    # encode kernel time for windows 32 / 48 / 64, both levels, chunk sizes
+    # 2048 and 4096, on the same input.
+    sweep = None
+    if not args.no_split and ws == 4 and n <= (64 << 20):
+        sweep = []
+        s_ = torch.cuda.current_stream()
+        for cs_ in (2048, 4096):
+            cap_ = g.max_compressed_size(n, cs_)
+            o_ = torch.empty(cap_, dtype=torch.uint8, device=dev)
+            nb_ = torch.zeros(1, dtype=torch.uint64, device=dev)
+            w_ = torch.empty(g.encode_workspace_size(n, cs_), dtype=torch.uint8, device=dev)
+            for lv in (0, 1):
+                for win in (32, 48, 64):
+                    g.encode_window_into(x, cs_, ws, lv, win, o_, nb_, w_)
+                    ts_ = []
+                    for i in range(3 + 5):
+                        e_ = ev.pair()
+                        ev.hip.hipEventRecord(e_[0], ctypes.c_void_p(s_.cuda_stream))
+                        g.encode_window_into(x, cs_, ws, lv, win, o_, nb_, w_)
+                        ev.hip.hipEventRecord(e_[1], ctypes.c_void_p(s_.cuda_stream))
+                        if i >= 3:
+                            ts_.append(e_)
+                    torch.cuda.synchronize()
+                    sb_ = int(nb_.item())
+                    me_ = float(np.median([ev.ms(p_) for p_ in ts_]))
+                    sweep.append({"chunk_size": cs_, "level": lv, "window": win, "ratio": round(n / sb_, 4),
+                                  "encode_ms": round(me_, 4), "encode_gbps": round(n / (me_ * 1e-3) / 1e9, 3)})
+            del o_, nb_, w_
     ev.close()
     if args.calibration_copy_mib > 0:
         a_ = torch.empty(args.calibration_copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -501,6 +530,7 @@ def main(argv=None) -> int:
         "split": split,
         "decode_baseline": baseline,
         "lorenzo_front_end": front,
+        "window_sweep": sweep,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
