@@ -12,7 +12,8 @@
 //      before them in registers, so the 256 comparisons per lane read LDS once;
 //      no bit set anywhere -> at level 0 the chunk is raw, steps 3-6 skipped;
 //   3. a base-4 doubling table S_k[p] = AND of omask over [p, p+k) for
-//      k = 1, 4, 16, 64, and a 4-round descent per position (up to three
+//      k = 1, 4, 16 (S_64 read as the AND of four S_16 entries, not stored),
+//      and a 4-round descent per position (up to three
 //      steps of k per round, so L <= 255) giving the exact longest run of any
 //      offset, capped at 255, and the smallest offset reaching it
 //      [exact-search and long-match paragraphs];
@@ -195,13 +196,14 @@ struct Lay {
   static constexpr uint32_t NW64 = E / 64;  // 64-position words
   static constexpr uint32_t NSEG = E / 8;   // 8-position parse segments
   // Word offsets inside the per-chunk region, after X[E]:
-  //   search: LV = S_1 | S_4 | S_16 | S_64, each E masks followed by zero
-  //           padding that the descent may read (3, 9, 33, 129 masks, rounded)
+  //   search: LV = S_1 | S_4 | S_16, each E masks followed by zero padding
+  //           that the descent may read (3, 9 and 177 masks, rounded); S_64
+  //           is not stored: its values are ANDs of four S_16 entries
   //   level 1: LO (E) | hash table (2048)
   //   parse:   LO (E) | XQ (E) | ISB (E/32) | LMB (E/32) | FLG (E/32) | STG (CS/4 + 8)
   static constexpr uint32_t RP = 2u * E + 3u * (E / 32u) + CS / 4u + 8u;
-  static constexpr uint32_t TOFF[4] = {0u, E + 4u, 2u * E + 16u, 3u * E + 52u};  // table offsets, in masks
-  static constexpr uint32_t SEARCH = MW * (4u * E + 184u);
+  static constexpr uint32_t TOFF[3] = {0u, E + 4u, 2u * E + 16u};  // table offsets, in masks
+  static constexpr uint32_t SEARCH = MW * (3u * E + 196u);
   static constexpr uint32_t R = (cmax(cmax(SEARCH, LEVEL ? (uint32_t)E + kHashSize : 0u), RP) + 3u) & ~3u;
   static constexpr uint32_t MISC = 2u * (E / 64u + 1u) + 8u;
   static constexpr uint32_t TOTAL = (E + R + MISC + 3u) & ~3u;  // words per chunk, 16-byte multiple
@@ -385,16 +387,18 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
       K = (uint32_t)E;
     } else {
       if (near) {
-        // ---- 3. base-4 doubling table S_4, S_16, S_64 and a 4-round descent ------------
+        // ---- 3. base-4 doubling table S_4, S_16 and a 4-round descent -----------------
         // S_k[p] = AND of omask over [p, p+k) when p + k <= E, else 0; every
         // table is followed by zeros, so descent reads past the chunk need no
-        // bounds checks.
-        for (uint32_t i = g; i < 184u; i += TL) {  // padding word i of level lv is at (lv + 1) E + i
-          const uint32_t lv = i < 4u ? 0u : (i < 16u ? 1u : (i < 52u ? 2u : 3u));
+        // bounds checks.  S_64[p] = S_16[p] & S_16[p+16] & S_16[p+32] &
+        // S_16[p+48] is read that way in the first round instead of being
+        // stored: one table less in LDS, so more chunks per CU.
+        for (uint32_t i = g; i < 196u; i += TL) {  // padding word i of level lv is at (lv + 1) E + i
+          const uint32_t lv = i < 4u ? 0u : (i < 16u ? 1u : 2u);
           LVm[(lv + 1u) * (uint32_t)E + i] = 0;
         }
 #pragma unroll
-        for (uint32_t lv = 1; lv < 4; ++lv) {
+        for (uint32_t lv = 1; lv < 3; ++lv) {
           const uint32_t k = 1u << (2 * lv), step = k >> 2;
           const Mask* prev = LVm + L::TOFF[lv - 1];
           Mask* cur = LVm + L::TOFF[lv];
@@ -415,8 +419,20 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
           uint32_t Ln = 0;
           // digits of L in base 4, most significant first: at most 3 steps of k per
           // round, so L <= 3 * (64 + 16 + 4 + 1) = 255, the length cap
+          {
+            // round of k = 64 (Ln = 0): S_64 at p, p + 64, p + 128 from S_16,
+            // reads up to p + 176, inside S_16's padding
+            const Mask* S = LVm + L::TOFF[2] + p;
+            const Mask s0 = S[0] & S[16] & S[32] & S[48];
+            const Mask s1 = S[64] & S[80] & S[96] & S[112];
+            const Mask s2 = S[128] & S[144] & S[160] & S[176];
+            const Mask t1 = surv & s0, t2 = t1 & s1, t3 = t2 & s2;
+            const uint32_t n = (uint32_t)(t1 != 0) + (uint32_t)(t2 != 0) + (uint32_t)(t3 != 0);
+            surv = t3 ? t3 : (t2 ? t2 : (t1 ? t1 : surv));
+            Ln += n << 6;
+          }
 #pragma unroll
-          for (int lv = 3; lv >= 0; --lv) {
+          for (int lv = 2; lv >= 0; --lv) {
             const uint32_t k = 1u << (2 * lv);
             // p + Ln <= E (every surviving position is inside the chunk), so the
             // three reads end within the table's padding
