@@ -195,7 +195,9 @@ struct Lay {
   static constexpr uint32_t MW = W > 32 ? 2u : 1u;  // words per offset mask
   static constexpr uint32_t NW64 = E / 64;  // 64-position words
   static constexpr uint32_t NSEG = E / 8;   // 8-position parse segments
-  // Word offsets inside the per-chunk region, after X[E]:
+  // Word offsets inside the per-chunk region, after X[E] (level 1 only: at
+  // level 0 the words are needed only by the offset masks, so X shares its
+  // place with S_1 and the literal words are read again from the input):
   //   search: LV = S_1 | S_4 | S_16, each E masks followed by zero padding
   //           that the descent may read (3, 9 and 177 masks, rounded); S_64
   //           is not stored: its values are ANDs of four S_16 entries
@@ -206,7 +208,8 @@ struct Lay {
   static constexpr uint32_t SEARCH = MW * (3u * E + 196u);
   static constexpr uint32_t R = (cmax(cmax(SEARCH, LEVEL ? (uint32_t)E + kHashSize : 0u), RP) + 3u) & ~3u;
   static constexpr uint32_t MISC = 2u * (E / 64u + 1u) + 8u;
-  static constexpr uint32_t TOTAL = (E + R + MISC + 3u) & ~3u;  // words per chunk, 16-byte multiple
+  static constexpr uint32_t XW = LEVEL ? (uint32_t)E : 0u;       // words of the X region
+  static constexpr uint32_t TOTAL = (XW + R + MISC + 3u) & ~3u;  // words per chunk, 16-byte multiple
 };
 
 template <int WS, int E, int LEVEL, int W, int WPC, int CPW>
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
   const uint32_t g = threadIdx.x % TL;  // lane within the team
   const uint32_t lane = lane_id();
   uint32_t* X = lds_all + team * L::TOTAL;
-  uint32_t* LV = X + E;
+  uint32_t* LV = X + L::XW;  // level 0: X and S_1 share their words
   Mask* LVm = (Mask*)LV;  // the search tables
   uint32_t* LO = LV;
   uint32_t* XQ = LV + E;
@@ -366,6 +369,8 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             om[q] |= (Mask)hm << 32;
           }
         }
+        // level 0: the masks overwrite X, which the whole team has read by now
+        if (LEVEL == 0) team_sync<WPC>();
 #pragma unroll
         for (uint32_t q = 0; q < PPASS; ++q) {
           any_om |= om[q];
@@ -630,7 +635,22 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
   // in the stream; the compaction kernel moves it to its final offset.
   uint32_t* STG32 = (uint32_t*)STG;
   uint32_t* slot = (uint32_t*)(staging + base);
+  // element p of the chunk (0 past its real bytes), from the input
+  const bool fast = bc == CS && (((uintptr_t)src) & 3u) == 0;
+  auto word_at = [&](uint32_t p) -> uint32_t {
+    const uint32_t b = p * (uint32_t)WS;
+    uint32_t v = fast ? (((const uint32_t*)src)[b >> 2] >> (8u * (b & 3u))) : load4_unaligned(src + b, src + bc);
+    return WS == 4 ? v : (WS == 2 ? (v & 0xFFFFu) : (v & 0xFFu));
+  };
   if (nonzero && !raw) {
+    // this lane's literal words: X at level 1, the input at level 0 (loaded
+    // here so the loads overlap the flag bitmap's construction)
+    uint32_t xv[PPL];
+#pragma unroll
+    for (uint32_t i = 0; i < PPL; ++i) {
+      const uint32_t p = WPC == 1 ? 64u * i + lane : g + i * TL;
+      xv[i] = LEVEL ? X[p] : word_at(p);
+    }
     for (uint32_t i = g; i < (F + 3u) / 4u; i += TL) STG32[i] = 0u;
     team_sync<WPC>();
     if constexpr (WPC == 1) {
@@ -656,7 +676,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
           STG[off] = (uint8_t)v;
           STG[off + 1] = (uint8_t)(v >> 8);
         } else {
-          const uint32_t v = X[p];
+          const uint32_t v = xv[i];
 #pragma unroll
           for (int b = 0; b < WS; ++b) STG[off + b] = (uint8_t)(v >> (8 * b));
         }
@@ -692,7 +712,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
           STG[off] = (uint8_t)v;
           STG[off + 1] = (uint8_t)(v >> 8);
         } else {
-          const uint32_t v = X[p];
+          const uint32_t v = xv[i];
 #pragma unroll
           for (int b = 0; b < WS; ++b) STG[off + b] = (uint8_t)(v >> (8 * b));
         }
@@ -701,18 +721,10 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
     team_sync<WPC>();
     for (uint32_t i = g; i < (F + D + 3u) / 4u; i += TL) slot[i] = STG32[i];
   } else if (raw && km) {
-    // split mode stages raw bytes for the literals port; the one-stream
-    // assembly copies a raw chunk straight from the input
-    if (WS == 4) {
-      for (uint32_t i = g; i < CS / 4u; i += TL) slot[i] = X[i];
-    } else {
-      for (uint32_t i = g; i < CS / 4u; i += TL) {  // repack the words as bytes
-        uint32_t v;
-        if (WS == 2) v = X[2 * i] | (X[2 * i + 1] << 16);
-        else v = X[4 * i] | (X[4 * i + 1] << 8) | (X[4 * i + 2] << 16) | (X[4 * i + 3] << 24);
-        slot[i] = v;
-      }
-    }
+    // split mode stages raw bytes for the literals port (the one-stream
+    // assembly copies a raw chunk straight from the input)
+    for (uint32_t i = g; i < (bc + 3u) / 4u; i += TL)
+      slot[i] = fast ? ((const uint32_t*)src)[i] : load4_unaligned(src + 4u * i, src + bc);
   }
   if (g == 0) {
     const uint2 ent = !nonzero ? make_uint2(0u, 0u) : (raw ? make_uint2(0u, kRawBit | bc) : make_uint2(F, D));
