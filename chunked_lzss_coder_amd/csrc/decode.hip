@@ -580,35 +580,52 @@ __device__ __forceinline__ void decode_group(const DecP& p, const uint8_t* in, c
   constexpr uint32_t CPW = kWaves / G::TW;  // chunks per workgroup
   const uint32_t team = threadIdx.x / TL, g = threadIdx.x % TL;
   uint8_t* arena = arena_all + team * (G::TW * kSlot);
-  // A chunk's metadata (size-table row, offset within its tile, a lane's
-  // share of the earlier tiles' totals) is fetched one chunk ahead, so those
-  // loads are in flight while the previous chunk is decoded.
+  // The metadata of 64 of the team's chunks (size-table row and payload
+  // offset) is loaded at once, one chunk per lane, and handed out by
+  // readlane: one load latency per 64 chunks, not one per chunk.  A payload
+  // offset is its tile's offset (the earlier tiles' totals: lane t of `pre`
+  // for streams of up to 64 tiles) plus its offset within the tile.
   const uint64_t stride = (uint64_t)gridDim.x * CPW;
-  uint64_t c = (uint64_t)blockIdx.x * CPW + team;
-  uint2 e_n = make_uint2(0u, 0u);
-  uint32_t loc_n = 0;
-  uint64_t tps_n = 0;
-  auto fetch = [&](uint64_t cc) {
-    e_n = read_row(in, cc);
-    loc_n = loc[cc];
-    const uint32_t t = (uint32_t)(cc / p.T);
-    tps_n = lane_id() < t ? tile_sum[lane_id()] : 0ull;
+  const uint64_t c0 = (uint64_t)blockIdx.x * CPW + team;
+  const uint32_t lane = lane_id();
+  uint64_t pre = 0;
+  if (p.ntiles <= 64u) {
+    const uint64_t v = lane < p.ntiles ? tile_sum[lane] : 0ull;
+    pre = wave_incl_add64(v) - v;
+  }
+  uint2 me = make_uint2(0u, 0u);
+  uint64_t moff = 0;
+  auto batch = [&](uint64_t k0) {
+    const uint64_t cc = c0 + (k0 + lane) * stride;
+    const bool live = cc < p.nc;
+    const uint32_t t = live ? (uint32_t)(cc / p.T) : 0u;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((t & 63u) << 2), (int)(uint32_t)pre);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((t & 63u) << 2), (int)(uint32_t)(pre >> 32));
+    uint64_t tp = (uint64_t)lo | ((uint64_t)hi << 32);
+    me = make_uint2(0u, 0u);
+    moff = 0;
+    if (live) {
+      me = read_row(in, cc);
+      if (p.ntiles > 64u) {  // huge streams only: this lane adds the earlier tiles itself
+        tp = 0;
+        for (uint32_t i = 0; i < t; ++i) tp += tile_sum[i];
+      }
+      moff = tp + loc[cc];
+    }
   };
-  if (c < p.nc) fetch(c);
-  for (; c < p.nc; c += stride) {  // CPW > 1 only for one-wave teams: no workgroup barrier below
-    const uint2 e = e_n;
-    const uint32_t loc_c = loc_n;
-    uint64_t tp = tps_n;
-    if (c + stride < p.nc) fetch(c + stride);
+  for (uint64_t k = 0;; ++k) {  // CPW > 1 only for one-wave teams: no workgroup barrier below
+    const uint64_t c = c0 + k * stride;
+    if (c >= p.nc) break;
+    if ((k & 63u) == 0u) batch(k);
+    const int j = (int)(k & 63u);
+    const uint2 e = make_uint2((uint32_t)__builtin_amdgcn_readlane((int)me.x, j),
+                               (uint32_t)__builtin_amdgcn_readlane((int)me.y, j));
+    const uint64_t off = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)moff, j) |
+                         ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(moff >> 32), j) << 32);
     const uint64_t start = c * CS;
     const uint32_t bc = (uint32_t)((p.n - start) < CS ? (p.n - start) : CS);
     if (!row_ok(e, bc)) continue;  // reported by the scan kernel
     const uint32_t size = entry_payload(e.x, e.y);
-    // payload offset = earlier tiles' totals + offset within the tile
-    const uint32_t t = (uint32_t)(c / p.T);
-    for (uint32_t i = lane_id() + 64u; i < t; i += 64u) tp += tile_sum[i];  // over 64 tiles: huge streams only
-    tp = lane63_64(wave_incl_add64(tp));
-    const uint64_t off = tp + loc_c;
     if (off + size > p.pb) continue;  // sizes inconsistent with the header: reported by wave 0 below
     const uint8_t* pay = in + p.base + off;
     uint8_t* dst = out + start;
