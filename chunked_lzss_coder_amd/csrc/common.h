@@ -220,6 +220,49 @@ __device__ __forceinline__ void copy_bytes16(uint8_t* dst, const uint8_t* src, u
   if (t < n) dst[t] = src[t];
 }
 
+// copy_bytes16 with one block per lane per round (fewer registers, for
+// callers under register pressure).
+__device__ __forceinline__ void copy_bytes16_r1(uint8_t* dst, const uint8_t* src, uint32_t n, uint32_t l) {
+  const uint32_t h0 = (uint32_t)((16u - ((uintptr_t)dst & 15u)) & 15u);
+  const uint32_t h = h0 < n ? h0 : n;
+  if (l < h) dst[l] = src[l];
+  const uint32_t nb = (n - h) >> 4;
+  const uintptr_t s = (uintptr_t)(src + h);
+  const uint32_t sh = (uint32_t)(s & 15u);
+  const uint32_t ns = nb + (sh ? 1u : 0u);
+  const uint4* sb = (const uint4*)(s - sh);
+  uint4* db = (uint4*)(dst + h);
+  const uint32_t q = sh >> 2, r = sh & 3u;
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll 1
+  for (uint32_t k0 = 0; k0 < nb; k0 += 64u) {
+    const uint32_t k = k0 + l;
+    const uint4 a = k < ns ? sb[k] : z;
+    const uint4 x = (l == 63u && sh && k0 + 64u < ns) ? sb[k0 + 64u] : z;  // lane 63's next block
+    uint4 b;
+    b.x = dpp0<kWaveShl1>(a.x);
+    b.y = dpp0<kWaveShl1>(a.y);
+    b.z = dpp0<kWaveShl1>(a.z);
+    b.w = dpp0<kWaveShl1>(a.w);
+    if (l == 63u) b = x;
+    if (k < nb) db[k] = sh ? funnel16(a, b, q, r) : a;
+  }
+  const uint32_t t = h + 16u * nb + l;
+  if (t < n) dst[t] = src[t];
+}
+
+// Zero n bytes at dst (any alignment) with one wave (this is lane l).
+__device__ __forceinline__ void zero_bytes16(uint8_t* dst, uint32_t n, uint32_t l) {
+  const uint32_t h0 = (uint32_t)((16u - ((uintptr_t)dst & 15u)) & 15u);
+  const uint32_t h = h0 < n ? h0 : n;
+  if (l < h) dst[l] = 0u;
+  const uint32_t nb = (n - h) >> 4;
+  uint4* db = (uint4*)(dst + h);
+  for (uint32_t k = l; k < nb; k += 64u) db[k] = make_uint4(0u, 0u, 0u, 0u);
+  const uint32_t t = h + 16u * nb + l;
+  if (t < n) dst[t] = 0u;
+}
+
 // ---- launchers (host side, one per kernel family) -------------------------
 struct EncodeArgs {
   const uint8_t* in;

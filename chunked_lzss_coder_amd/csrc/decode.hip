@@ -629,31 +629,15 @@ __device__ __forceinline__ void decode_group(const DecP& p, const uint8_t* in, c
     if (off + size > p.pb) continue;  // sizes inconsistent with the header: reported by wave 0 below
     const uint8_t* pay = in + p.base + off;
     uint8_t* dst = out + start;
-    const bool al = (((uintptr_t)dst) & 3u) == 0;
     if (e.x == 0u) {
-      // zero or raw chunk: four loads per lane in flight before their stores
-      const bool zero = e.y == 0u;
-      const uint32_t nw = (bc + 3u) / 4u;
-#pragma unroll 1
-      for (uint32_t i0 = 0; i0 < nw; i0 += 4u * TL) {
-        uint32_t v[4];
-#pragma unroll
-        for (uint32_t r = 0; r < 4u; ++r) {
-          const uint32_t i = i0 + g + r * TL;
-          v[r] = (!zero && i < nw) ? load4_unaligned(pay + 4u * i, lim) : 0u;
-        }
-#pragma unroll
-        for (uint32_t r = 0; r < 4u; ++r) {
-          const uint32_t i = i0 + g + r * TL;
-          if (i >= nw) continue;
-          if (al && 4u * i + 4u <= bc) {
-            *(uint32_t*)(dst + 4u * i) = v[r];
-          } else {
-            for (uint32_t b = 0; b < 4u; ++b)
-              if (4u * i + b < bc) dst[4u * i + b] = (uint8_t)(v[r] >> (8u * b));
-          }
-        }
-      }
+      // zero or raw chunk: each wave of the team fills or copies its share
+      // (whole 16-byte blocks but the last), one block per lane per round
+      constexpr uint32_t TW = G::TW;
+      const uint32_t share = ((bc + 16u * TW - 1u) / (16u * TW)) * 16u;
+      const uint32_t w0 = (g >> 6) * share;
+      const uint32_t len = w0 < bc ? (bc - w0 < share ? bc - w0 : share) : 0u;
+      if (e.y == 0u) zero_bytes16(dst + w0, len, lane);
+      else copy_bytes16_r1(dst + w0, pay + w0, len, lane);
     } else {
       if (!decode_coded<CS, WS>(pay, lim, e.x, e.y, bc, dst, arena, sh, SplitSrc{}) && g == 0)
         raise_status(status, out_bytes, kStatusCorrupt);
