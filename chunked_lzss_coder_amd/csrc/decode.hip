@@ -37,6 +37,7 @@ constexpr uint32_t kScanPer = 4;         // chunks per thread per scan round
 constexpr uint32_t kScanRound = kScanPer * kBlock;
 constexpr uint32_t kDecodeGrid = 8192;   // chunk-kernel workgroups at most
 constexpr uint32_t kMaxTilesAlloc = 4096; // split mode: stride of the three tile-total arrays
+constexpr uint32_t kWideMinChunks = 32768; // wide chunks: one per wave from this many chunks on
 static_assert(kTileMin % kScanRound == 0 && (uint64_t)kTileMax * 4096u <= (1ull << 32), "tile sizes");
 
 __device__ __forceinline__ uint32_t ld_u32_bytes(const uint8_t* p) {
@@ -165,17 +166,22 @@ constexpr uint32_t kSlot = 5376;
 static_assert(kSlot % 16 == 0, "arenas must stay 16-byte aligned (64-bit LDS atomics)");
 constexpr uint32_t kArena = kWaves * kSlot;
 
-template <uint32_t CS, uint32_t WS>
+template <uint32_t CS, uint32_t WS, bool TEAMS = false>
 struct Geo {
   static constexpr uint32_t E = CS / WS;                       // elements per chunk
   static constexpr uint32_t PBB = (CS > 2u * E ? CS : 2u * E) + 16u;
   static constexpr uint32_t NEED = CS + PBB + E + E / 8u;
-  static constexpr uint32_t TW = NEED <= kSlot ? 1u : kWaves;  // waves per chunk
+  // WIDE: a chunk that needs two slots but has few enough elements per lane
+  // for the one-wave decoder (1024 elements: chunk 4096 at word size 4) is
+  // decoded by one wave over two slots; see decode_group_wide.
+  static constexpr bool WIDE = !TEAMS && NEED > kSlot && NEED <= 2u * kSlot && E <= 1024u;
+  static constexpr uint32_t TW = (NEED <= kSlot || WIDE) ? 1u : kWaves;  // waves per chunk
+  static constexpr uint32_t SLOTS = WIDE ? 2u : TW;                        // arena slots per chunk
   static constexpr uint32_t TL = 64u * TW;                     // lanes per chunk
   static constexpr uint32_t J = E / TL;                        // elements per lane
   static constexpr uint32_t NB = E / 64u;                      // 64-element blocks
   static constexpr uint32_t RMAX = J + 1u;                     // items per lane, at most
-  static_assert(NEED <= TW * kSlot, "chunk working set exceeds its arena");
+  static_assert(NEED <= SLOTS * kSlot, "chunk working set exceeds its arena");
   static_assert(E % TL == 0 && NB <= 64u && RMAX < 25u, "lane mapping");
 };
 
@@ -273,10 +279,10 @@ struct SplitSrc {
 // data bytes), lim the end of the readable input.  Split mode: sp locates
 // its items in the ports (pay, lim, F, D unused).  bc: the chunk's real
 // bytes, written to dst.  Returns false on a rule violation.
-template <uint32_t CS, uint32_t WS, bool SPLIT = false>
+template <uint32_t CS, uint32_t WS, bool SPLIT = false, bool TEAMS = false>
 __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* lim, uint32_t F, uint32_t D, uint32_t bc,
                              uint8_t* dst, uint8_t* arena, uint32_t* sh, const SplitSrc& sp) {
-  using G = Geo<CS, WS>;
+  using G = Geo<CS, WS, TEAMS>;
   constexpr uint32_t E = G::E, TW = G::TW, TL = G::TL, J = G::J, NB = G::NB;
   TeamX<TW> tx{sh, 0u};
   const uint32_t g = threadIdx.x % TL, lane = lane_id();
@@ -571,11 +577,89 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
   return !tx.any(padbad);
 }
 
+// Wide chunks (two slots, one wave): a workgroup takes chunks blockIdx.x +
+// k * gridDim.x, 64 at a time.  Waves 0 and 2 decode the coded ones (each
+// in two slots), waves 1 and 3 fill or copy the zero and raw ones (all four
+// share the stored ones when a batch has no coded chunk), so the copies run
+// beside the decodes and no wave waits for another: there is no barrier.
 template <uint32_t CS, uint32_t WS>
-__device__ __forceinline__ void decode_group(const DecP& p, const uint8_t* in, const uint8_t* lim, uint8_t* out,
-                             const uint32_t* loc, const uint64_t* tile_sum, uint32_t* status, uint64_t* out_bytes,
-                             uint8_t* arena_all, uint32_t* sh) {
+__device__ __forceinline__ void decode_group_wide(const DecP& p, const uint8_t* in, const uint8_t* lim, uint8_t* out,
+                                                  const uint32_t* loc, const uint64_t* tile_sum, uint32_t* status,
+                                                  uint64_t* out_bytes, uint8_t* arena_all, uint32_t* sh) {
   using G = Geo<CS, WS>;
+  static_assert(kWaves == 4 && G::SLOTS == 2, "two decoding and two copying waves");
+  const uint32_t lane = lane_id(), w = threadIdx.x >> 6;
+  uint8_t* arena = arena_all + (w & 2u) * kSlot;  // waves 0 and 2: slots 0-1 and 2-3
+  const uint64_t stride = gridDim.x;
+  uint64_t pre = 0;
+  if (p.ntiles <= 64u) {
+    const uint64_t v = lane < p.ntiles ? tile_sum[lane] : 0ull;
+    pre = wave_incl_add64(v) - v;
+  }
+  for (uint64_t k0 = 0;; k0 += 64u) {
+    if ((uint64_t)blockIdx.x + k0 * stride >= p.nc) break;
+    // this batch's metadata, one chunk per lane (every wave loads it)
+    const uint64_t cc = (uint64_t)blockIdx.x + (k0 + lane) * stride;
+    const bool live = cc < p.nc;
+    const uint32_t t = live ? (uint32_t)(cc / p.T) : 0u;
+    const uint32_t plo = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((t & 63u) << 2), (int)(uint32_t)pre);
+    const uint32_t phi = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((t & 63u) << 2), (int)(uint32_t)(pre >> 32));
+    uint64_t tp = (uint64_t)plo | ((uint64_t)phi << 32);
+    uint2 e = make_uint2(0u, 0u);
+    uint64_t off = 0;
+    uint32_t bc = 0;
+    bool ok = false;
+    if (live) {
+      e = read_row(in, cc);
+      if (p.ntiles > 64u) {  // huge streams only: this lane adds the earlier tiles itself
+        tp = 0;
+        for (uint32_t i = 0; i < t; ++i) tp += tile_sum[i];
+      }
+      off = tp + loc[cc];
+      const uint64_t start = cc * CS;
+      bc = (uint32_t)((p.n - start) < CS ? (p.n - start) : CS);
+      // bad rows are reported by the scan kernel, sizes inconsistent with
+      // the header by wave 0 of workgroup 0
+      ok = row_ok(e, bc) && off + entry_payload(e.x, e.y) <= p.pb;
+    }
+    const uint64_t coded = __ballot(ok && e.x != 0u), stored = __ballot(ok && e.x == 0u);
+    const uint64_t below = lane == 0u ? 0ull : (~0ull >> (64u - lane));
+    // my chunks: coded ones of my parity (waves 0, 2), stored ones of my
+    // parity (waves 1, 3), or every fourth stored one when none is coded
+    const uint32_t crank = (uint32_t)__builtin_popcountll(coded & below);
+    const uint32_t srank = (uint32_t)__builtin_popcountll(stored & below);
+    uint64_t mine;
+    if (coded == 0ull) mine = __ballot(((stored >> lane) & 1ull) && (srank & 3u) == w);
+    else if ((w & 1u) == 0u) mine = __ballot(((coded >> lane) & 1ull) && (crank & 1u) == (w >> 1));
+    else mine = __ballot(((stored >> lane) & 1ull) && (srank & 1u) == (w >> 1));
+    while (mine) {
+      const int j = (int)__builtin_ctzll(mine);
+      mine &= mine - 1ull;
+      const uint2 ej = make_uint2((uint32_t)__builtin_amdgcn_readlane((int)e.x, j),
+                                  (uint32_t)__builtin_amdgcn_readlane((int)e.y, j));
+      const uint32_t bj = (uint32_t)__builtin_amdgcn_readlane((int)bc, j);
+      const uint64_t oj = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)off, j) |
+                          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(off >> 32), j) << 32);
+      const uint64_t c = (uint64_t)blockIdx.x + (k0 + (uint64_t)j) * stride;
+      const uint8_t* pay = in + p.base + oj;
+      uint8_t* dst = out + c * CS;
+      if (ej.x == 0u) {
+        if (ej.y == 0u) zero_bytes16(dst, bj, lane);
+        else copy_bytes16_r1(dst, pay, bj, lane);
+      } else {
+        if (!decode_coded<CS, WS>(pay, lim, ej.x, ej.y, bj, dst, arena, sh + 2u * w, SplitSrc{}) && lane == 0u)
+          raise_status(status, out_bytes, kStatusCorrupt);
+        wave_sync();
+      }
+    }
+  }
+}
+
+template <uint32_t CS, uint32_t WS>
+__device__ __forceinline__ void decode_group_teams(const DecP& p, const uint8_t* in, const uint8_t* lim, uint8_t* out,
+                                                   const uint32_t* loc, const uint64_t* tile_sum, uint32_t* status,
+                                                   uint64_t* out_bytes, uint8_t* arena_all, uint32_t* sh) {
+  using G = Geo<CS, WS, true>;
   constexpr uint32_t TL = G::TL;
   constexpr uint32_t CPW = kWaves / G::TW;  // chunks per workgroup
   const uint32_t team = threadIdx.x / TL, g = threadIdx.x % TL;
@@ -639,11 +723,26 @@ __device__ __forceinline__ void decode_group(const DecP& p, const uint8_t* in, c
       if (e.y == 0u) zero_bytes16(dst + w0, len, lane);
       else copy_bytes16_r1(dst + w0, pay + w0, len, lane);
     } else {
-      if (!decode_coded<CS, WS>(pay, lim, e.x, e.y, bc, dst, arena, sh, SplitSrc{}) && g == 0)
+      if (!decode_coded<CS, WS, false, true>(pay, lim, e.x, e.y, bc, dst, arena, sh, SplitSrc{}) && g == 0)
         raise_status(status, out_bytes, kStatusCorrupt);
     }
     team_sync<G::TW>();
   }
+}
+
+template <uint32_t CS, uint32_t WS>
+__device__ __forceinline__ void decode_group(const DecP& p, const uint8_t* in, const uint8_t* lim, uint8_t* out,
+                             const uint32_t* loc, const uint64_t* tile_sum, uint32_t* status, uint64_t* out_bytes,
+                             uint8_t* arena_all, uint32_t* sh) {
+  // Wide chunks go one per wave only when there are enough of them to keep
+  // every CU busy; a small stream decodes faster with a workgroup per chunk.
+  if constexpr (Geo<CS, WS>::WIDE) {
+    if (p.nc >= kWideMinChunks) {
+      decode_group_wide<CS, WS>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena_all, sh);
+      return;
+    }
+  }
+  decode_group_teams<CS, WS>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena_all, sh);
 }
 
 template <uint32_t CS>
@@ -798,9 +897,11 @@ __device__ __forceinline__ void decode_group_split(const DecP& p, const SplitDec
                                                    const uint64_t* tile_sum, uint8_t* arena_all, uint32_t* sh) {
   using G = Geo<CS, WS>;
   constexpr uint32_t TL = G::TL;
-  constexpr uint32_t CPW = kWaves / G::TW;  // chunks per workgroup
-  const uint32_t team = threadIdx.x / TL, g = threadIdx.x % TL, lane = lane_id();
-  uint8_t* arena = arena_all + team * (G::TW * kSlot);
+  constexpr uint32_t CPW = kWaves / G::SLOTS;  // chunks per workgroup
+  // a wide chunk is one wave's in two slots: waves 0 and 2 decode, 1 and 3 rest
+  if (G::WIDE && ((threadIdx.x >> 6) & 1u)) return;
+  const uint32_t team = threadIdx.x / (64u * G::SLOTS), g = threadIdx.x % TL, lane = lane_id();
+  uint8_t* arena = arena_all + team * (G::SLOTS * kSlot);
   const uint8_t* flags = a.meta + p.base;
   const uint8_t* meta_lim = a.meta + a.meta_bytes;
   const uint64_t stride = (uint64_t)gridDim.x * CPW;

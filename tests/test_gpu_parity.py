@@ -248,3 +248,45 @@ def test_corrupted_streams(g, oracle_mod):
         else:  # the flip produced another valid stream: same result as the oracle
             assert status == 0 and int(db.item()) == r
             assert np.array_equal(dbuf[:r].cpu().numpy(), ref_out)
+
+
+def test_many_wide_chunks(g, oracle_mod):
+    """A stream of 33,000 chunks of 4096 bytes at word size 4 (enough that
+    each chunk is decoded by one wave, with separate copying waves): the
+    oracle's stream decodes to the input, and corrupting one coded chunk's
+    match token gives the oracle's verdict."""
+    from chunked_lzss_coder_amd import synth
+    cs, ws = 4096, 4
+    n = 33000 * cs - 1000  # ragged tail
+    w = synth.workload(4, scale_bytes=n + 1000)
+    data = w.data[:n].copy()
+    stream = oracle_mod.encode(data, cs, ws, 0)
+    st, nb, out = gpu_decode(g, stream, n)
+    assert st == 0 and nb == n and np.array_equal(out, data)
+    # first coded chunk with a match: zero its first match's offset byte
+    chunks = -(-n // cs)
+    table = stream[32:32 + 8 * chunks].view("<u4").reshape(chunks, 2).astype(np.int64)
+    f, d = table[:, 0], table[:, 1]
+    sizes = np.where(f > 0, f + d, np.where(d & 0x80000000, d & 0x7FFFFFFF, 0))
+    offs = 32 + 8 * chunks + np.concatenate([[0], np.cumsum(sizes)])
+    bad = stream.copy()
+    hit = False
+    for c in np.flatnonzero(f > 0)[5000:]:
+        pay = bad[offs[c]: offs[c] + sizes[c]]
+        F = int(f[c])
+        k, pos = 0, F
+        while pos < pay.size and k < 8 * F:
+            if (pay[k >> 3] >> (k & 7)) & 1:
+                pay[pos + 1] = 0  # offset 0 is never valid
+                hit = True
+                break
+            pos += ws
+            k += 1
+        if hit:
+            bad[offs[c]: offs[c] + sizes[c]] = pay
+            break
+    assert hit
+    want, _ = oracle_mod.decode_status(bad, n)
+    assert want == oracle_mod.ECORRUPT
+    st, nb, _ = gpu_decode(g, bad, n)
+    assert st == 3 and nb == 0
