@@ -474,32 +474,44 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
     // source before the window already holds its final value; one inside it
     // is followed over the window's lanes (pointer jumping on lane indices;
     // every link goes to a lower lane, so six rounds suffice) to a literal
-    // or to an element before the window.
+    // or to an element before the window.  The sources of four windows are
+    // found first (indices only, independent of each other), then their
+    // values are copied window by window.
+    static_assert(NB % 4u == 0u, "windows in groups of four");
 #pragma unroll 1
-    for (uint32_t w = 0; w < NB; ++w) {
-      const uint32_t base = 64u * w, q = base + lane;
-      const uint64_t m = STB[w] & upto;
-      const uint32_t st = m ? base + 63u - (uint32_t)__builtin_clzll(m)
-                            : (uint32_t)__builtin_amdgcn_readlane((int)before, (int)w);
-      const uint32_t O = OB[st];
-      const uint32_t e0 = O ? st - O + small_mod(q - st, O) : q;
-      const uint64_t lit = __ballot(O == 0u);
-      uint32_t link = 64u;  // 64: e is final
-      if (O && e0 >= base && !((lit >> (e0 - base)) & 1ull)) link = e0 - base;
-      uint32_t x = e0 | (link << 16);
-      for (uint32_t round = 0; __ballot(link < 64u); ++round) {
-        if (round == 6u) return false;  // unreachable for validated items
-        const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((link & 63u) << 2), (int)x);
-        if (link < 64u) {
-          x = y;
-          link = y >> 16;
+    for (uint32_t w0 = 0; w0 < NB; w0 += 4u) {
+      uint32_t src[4];
+#pragma unroll
+      for (uint32_t j = 0; j < 4u; ++j) {
+        const uint32_t w = w0 + j;
+        const uint32_t base = 64u * w, q = base + lane;
+        const uint64_t m = STB[w] & upto;
+        const uint32_t st = m ? base + 63u - (uint32_t)__builtin_clzll(m)
+                              : (uint32_t)__builtin_amdgcn_readlane((int)before, (int)w);
+        const uint32_t O = OB[st];
+        const uint32_t e0 = O ? st - O + small_mod(q - st, O) : q;
+        const uint64_t lit = __ballot(O == 0u);
+        uint32_t link = 64u;  // 64: e is final
+        if (O && e0 >= base && !((lit >> (e0 - base)) & 1ull)) link = e0 - base;
+        uint32_t x = e0 | (link << 16);
+        for (uint32_t round = 0; __ballot(link < 64u); ++round) {
+          if (round == 6u) return false;  // unreachable for validated items
+          const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((link & 63u) << 2), (int)x);
+          if (link < 64u) {
+            x = y;
+            link = y >> 16;
+          }
         }
+        src[j] = x & 0xFFFFu;
       }
-      const uint32_t e = x & 0xFFFFu;
-      if (e != q) {
-        if constexpr (WS == 4) *(uint32_t*)(VAL + 4u * q) = *(const uint32_t*)(VAL + 4u * e);
-        else if constexpr (WS == 2) *(uint16_t*)(VAL + 2u * q) = *(const uint16_t*)(VAL + 2u * e);
-        else VAL[q] = VAL[e];
+#pragma unroll
+      for (uint32_t j = 0; j < 4u; ++j) {
+        const uint32_t q = 64u * (w0 + j) + lane, e = src[j];
+        if (e != q) {
+          if constexpr (WS == 4) *(uint32_t*)(VAL + 4u * q) = *(const uint32_t*)(VAL + 4u * e);
+          else if constexpr (WS == 2) *(uint16_t*)(VAL + 2u * q) = *(const uint16_t*)(VAL + 2u * e);
+          else VAL[q] = VAL[e];
+        }
       }
     }
   } else {
