@@ -28,8 +28,7 @@
 //   7. the size-table row goes straight into the stream; a coded payload
 //      (flag bitmap, then data bytes) is built in LDS and written to the
 //      chunk's fixed-stride staging slot.  A raw chunk's payload is its input
-//      bytes: it is staged only when the assembly cannot read it from the
-//      input (input not 16-byte aligned, or split mode).
+//      bytes: it is never staged, the assembly copies it from the input.
 // compact_kernel: one workgroup per tile of 64 chunks scans the tile's sizes,
 //   finds the tile's offset by decoupled look-back over the tiles before it
 //   and moves every payload to its place in the stream with 16-byte stores;
@@ -720,11 +719,6 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
     }
     team_sync<WPC>();
     for (uint32_t i = g; i < (F + D + 3u) / 4u; i += TL) slot[i] = STG32[i];
-  } else if (raw && km) {
-    // split mode stages raw bytes for the literals port (the one-stream
-    // assembly copies a raw chunk straight from the input)
-    for (uint32_t i = g; i < (bc + 3u) / 4u; i += TL)
-      slot[i] = fast ? ((const uint32_t*)src)[i] : load4_unaligned(src + 4u * i, src + bc);
   }
   if (g == 0) {
     const uint2 ent = !nonzero ? make_uint2(0u, 0u) : (raw ? make_uint2(0u, kRawBit | bc) : make_uint2(F, D));
@@ -889,43 +883,26 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(const uint8_t* __restri
   }
 }
 
-// Copy n bytes from a 4-byte-aligned source to any destination with one
-// wave: single bytes up to dst's next 4-byte boundary, then aligned dwords
-// realigned from two source dwords, then single bytes.  Reads may run up to
-// 3 bytes past src + n (inside the staging area and its slack).
-__device__ __forceinline__ void wave_copy_to(uint8_t* dst, const uint8_t* src, uint32_t n) {
-  const uint32_t lane = lane_id();
-  const uint32_t a4 = (uint32_t)((4u - ((uintptr_t)dst & 3u)) & 3u);
-  const uint32_t h = a4 > n ? n : a4;
-  if (lane < h) dst[lane] = src[lane];
-  const uint32_t nb = (n - h) / 4u;
-  const uint32_t* sw = (const uint32_t*)src;
-  uint32_t* dw = (uint32_t*)(dst + h);
-  for (uint32_t k = lane; k < nb; k += 64u) {
-    const uint32_t lo = sw[k];
-    const uint32_t hi = h ? sw[k + 1u] : 0u;
-    dw[k] = __builtin_amdgcn_alignbyte(hi, lo, h);
-  }
-  const uint32_t t0 = h + 4u * nb;
-  if (t0 + lane < n) dst[t0 + lane] = src[t0 + lane];
-}
-
 // Split-mode assembly (codebase notes CN-GPULZ-1, split mode; GPULZStage page,
 // split-mode paragraphs): one workgroup per tile of kCTile chunks.  A chunk
 // contributes flag bytes to the meta port, literal bytes (its literal words,
 // or all its bytes when raw) to the literals port and one byte per match to
 // each of the lengths and offsets ports; three scans with decoupled look-back
 // (one flag set each) place them.  Coded chunks' rows become {items,
-// matches}; then every wave deals its chunks' items from the staging slots
-// into the ports.  The last tile writes the header and the port lengths.
+// matches}; then every wave copies its raw chunks from the input and deals
+// its coded chunks' items into the ports, each payload first brought from
+// its staging slot into LDS with 16-byte loads.  The last tile writes the
+// header and the port lengths.
 __global__ __launch_bounds__(kBlock) void split_compact_kernel(
-    const uint8_t* __restrict__ staging, const uint2* __restrict__ km, uint32_t cs, uint32_t ws, uint64_t n,
+    const uint8_t* __restrict__ in, const uint8_t* __restrict__ staging, const uint2* __restrict__ km, uint32_t cs,
+    uint32_t ws, uint64_t n,
     uint32_t num_chunks, uint32_t num_tiles, uint8_t* __restrict__ meta, uint8_t* __restrict__ lit,
     uint8_t* __restrict__ lens, uint8_t* __restrict__ offs, uint64_t* __restrict__ port_bytes,
     uint64_t* __restrict__ tile_flags, EncCtl* __restrict__ ctl) {
   __shared__ uint32_t s_kind[kCTile], s_f[kCTile], s_k[kCTile], s_m[kCTile], s_lb[kCTile];
   __shared__ uint32_t s_fo[kCTile], s_lo[kCTile], s_mo[kCTile];
   __shared__ uint64_t s_pre[3];
+  __shared__ __attribute__((aligned(16))) uint8_t s_pay[kWaves][4096];  // one staged payload per wave
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   uint8_t* table = meta + kHeaderBytes;
   uint8_t* mflags = table + (uint64_t)kEntryBytes * num_chunks;
@@ -1020,18 +997,37 @@ __global__ __launch_bounds__(kBlock) void split_compact_kernel(
   __syncthreads();
   const uint64_t pf = s_pre[0], pl = s_pre[1], pm = s_pre[2];
   constexpr uint32_t PW = kCTile / kWaves;
+  uint8_t* buf = s_pay[wave];
   for (uint32_t u = 0; u < PW; ++u) {
     const uint32_t j = wave * PW + u;
     const uint64_t c = c0 + j;
     if (c >= num_chunks) break;
     const uint32_t kind = s_kind[j];
     const uint8_t* src = staging + c * cs;
-    if (kind == 1u) {
-      wave_copy_to(lit + pl + s_lo[j], src, s_lb[j]);
+    if (kind == 1u) {  // a raw chunk's bytes, straight from the input
+      copy_bytes16(lit + pl + s_lo[j], in + c * cs, s_lb[j], lane);
     } else if (kind == 2u) {
       const uint32_t F = s_f[j], K = s_k[j];
-      wave_copy_to(mflags + pf + s_fo[j], src, F);
-      const uint8_t* data = src + F;
+      copy_bytes16(mflags + pf + s_fo[j], src, F, lane);
+      // the payload (flags, then data) into LDS with 16-byte loads, the
+      // items dealt out from there
+      const uint32_t nbk = (F + ws * (K - s_m[j]) + 2u * s_m[j] + 15u) / 16u;
+      for (uint32_t b0 = 0; b0 < nbk; b0 += 256u) {
+        uint4 v[4];
+#pragma unroll
+        for (uint32_t r = 0; r < 4u; ++r) {
+          const uint32_t b = b0 + lane + 64u * r;
+          v[r] = b < nbk ? ((const uint4*)src)[b] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (uint32_t r = 0; r < 4u; ++r) {
+          const uint32_t b = b0 + lane + 64u * r;
+          if (b < nbk) ((uint4*)buf)[b] = v[r];
+        }
+      }
+      wave_sync();
+      const uint8_t* flg = buf;
+      const uint8_t* data = buf + F;
       uint8_t* L = lit + pl + s_lo[j];
       uint8_t* LN = lens + pm + s_mo[j];
       uint8_t* OF = offs + pm + s_mo[j];
@@ -1039,7 +1035,7 @@ __global__ __launch_bounds__(kBlock) void split_compact_kernel(
       for (uint32_t k0 = 0; k0 < K; k0 += 64u) {
         const uint32_t k = k0 + lane;
         const bool live = k < K;
-        const bool mt = live && ((src[k >> 3] >> (k & 7u)) & 1u);
+        const bool mt = live && ((flg[k >> 3] >> (k & 7u)) & 1u);
         const uint64_t mw = __ballot(mt);
         const uint32_t mb = mg + mbcnt64(mw);  // matches before item k
         if (live) {
@@ -1053,6 +1049,7 @@ __global__ __launch_bounds__(kBlock) void split_compact_kernel(
         }
         mg += (uint32_t)__builtin_popcountll(mw);
       }
+      wave_sync();  // every item read before the next payload lands
     }
   }
 }
@@ -1100,7 +1097,7 @@ hipError_t launch_compact(const EncodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_split_compact(const EncodeArgs& a, hipStream_t stream) {
   const uint32_t tiles = num_tiles_of(a.num_chunks);
-  hipLaunchKernelGGL(split_compact_kernel, dim3(tiles ? tiles : 1u), dim3(kBlock), 0, stream, a.staging,
+  hipLaunchKernelGGL(split_compact_kernel, dim3(tiles ? tiles : 1u), dim3(kBlock), 0, stream, a.in, a.staging,
                      (const uint2*)a.km, a.cs, a.ws, a.n, a.num_chunks, tiles, a.out, a.lit, a.lens, a.offs,
                      a.port_bytes, a.tile_flags, (EncCtl*)a.ctl);
   return hipGetLastError();
