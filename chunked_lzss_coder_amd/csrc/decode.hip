@@ -480,7 +480,7 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
     static_assert(NB % 4u == 0u, "windows in groups of four");
 #pragma unroll 1
     for (uint32_t w0 = 0; w0 < NB; w0 += 4u) {
-      uint32_t src[4];
+      uint32_t x[4], link[4];  // link 64: x's source index is final
 #pragma unroll
       for (uint32_t j = 0; j < 4u; ++j) {
         const uint32_t w = w0 + j;
@@ -491,19 +491,28 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
         const uint32_t O = OB[st];
         const uint32_t e0 = O ? st - O + small_mod(q - st, O) : q;
         const uint64_t lit = __ballot(O == 0u);
-        uint32_t link = 64u;  // 64: e is final
-        if (O && e0 >= base && !((lit >> (e0 - base)) & 1ull)) link = e0 - base;
-        uint32_t x = e0 | (link << 16);
-        for (uint32_t round = 0; __ballot(link < 64u); ++round) {
-          if (round == 6u) return false;  // unreachable for validated items
-          const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((link & 63u) << 2), (int)x);
-          if (link < 64u) {
-            x = y;
-            link = y >> 16;
-          }
-        }
-        src[j] = x & 0xFFFFu;
+        link[j] = 64u;
+        if (O && e0 >= base && !((lit >> (e0 - base)) & 1ull)) link[j] = e0 - base;
+        x[j] = e0 | (link[j] << 16);
       }
+      // the four windows jump in step: one exchange per window per round
+      for (uint32_t round = 0;
+           __ballot(link[0] < 64u || link[1] < 64u || link[2] < 64u || link[3] < 64u); ++round) {
+        if (round == 6u) return false;  // unreachable for validated items
+        uint32_t y[4];
+#pragma unroll
+        for (uint32_t j = 0; j < 4u; ++j)
+          y[j] = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((link[j] & 63u) << 2), (int)x[j]);
+#pragma unroll
+        for (uint32_t j = 0; j < 4u; ++j)
+          if (link[j] < 64u) {
+            x[j] = y[j];
+            link[j] = y[j] >> 16;
+          }
+      }
+      uint32_t src[4];
+#pragma unroll
+      for (uint32_t j = 0; j < 4u; ++j) src[j] = x[j] & 0xFFFFu;
 #pragma unroll
       for (uint32_t j = 0; j < 4u; ++j) {
         const uint32_t q = 64u * (w0 + j) + lane, e = src[j];
