@@ -466,35 +466,67 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
         constexpr uint32_t SB = E / kSubBlocks;
 #pragma unroll 1
         for (uint32_t s = 0; s < kSubBlocks; ++s) {
+          // One position per lane (consecutive lanes, consecutive positions).
+          // A candidate replaces the near match only if its run is strictly
+          // longer, so it must match at p + Lnear, and Lnear must leave room.
+          // Each lane first measures its candidate's run itself, up to 8
+          // compares.  Runs still open after that are shared along lanes:
+          // when lanes l and l + 1 are open at the same offset, run(p) =
+          // min(lim(p), run(p + 1) + 1), so only the last lane of such a chain
+          // measures on, with the whole wave, 64 compares per step.
           for (uint32_t p = s * SB + g; p < (s + 1) * SB; p += TL) {
-            if (p + 1 >= (uint32_t)E) continue;
-            const uint32_t v = T[bucket_of(X[p], X[p + 1])];
-            if (v == 0) continue;
-            const uint32_t o = p - (v - 1u);  // entries come from earlier sub-blocks: o >= 1
-            if (o > kMaxFar) continue;
-            // the candidate replaces the near match only if its run is strictly
-            // longer, so it must match at p + Lnear, and Lnear must leave room
-            const uint32_t lim = (uint32_t)E - p < kMaxLen ? (uint32_t)E - p : kMaxLen;
-            const uint32_t Lnear = LO[p] & 0xFFu;
-            if (Lnear >= lim || X[p + Lnear] != X[p + Lnear - o]) continue;
-            // run at offset o, capped at lim, eight compares per step (reads past
-            // the chunk's words stay inside the team's LDS and are masked)
+            uint32_t o = 0, Lnear = 0, lim = 0;
+            bool need = false;
+            if (p + 1 < (uint32_t)E) {
+              const uint32_t v = T[bucket_of(X[p], X[p + 1])];
+              o = p - (v - 1u);  // entries come from earlier sub-blocks: o >= 1
+              lim = (uint32_t)E - p < kMaxLen ? (uint32_t)E - p : kMaxLen;
+              Lnear = LO[p] & 0xFFu;
+              need = v != 0u && o <= kMaxFar && Lnear < lim && X[p + Lnear] == X[p + Lnear - o];
+            }
             uint32_t r = 0;
-            while (true) {
+            bool open = need;
+            if (open) {
               uint32_t stop = 0;
 #pragma unroll
-              for (uint32_t j = 0; j < 8u; ++j) {
-                const uint32_t idx = r + j;
-                const uint32_t a = X[p + idx], b = X[p + idx - o];
-                stop |= (uint32_t)(idx >= lim || a != b) << j;
-              }
-              if (stop) {
-                r += (uint32_t)__builtin_ctz(stop);
-                break;
-              }
-              r += 8u;
+              for (uint32_t j = 0; j < 8u; ++j) stop |= (uint32_t)(j >= lim || X[p + j] != X[p + j - o]) << j;
+              r = stop ? (uint32_t)__builtin_ctz(stop) : 8u;
+              open = stop == 0u;
             }
-            if (r > Lnear) LO[p] = r | (o << 8);
+            const uint64_t openm = __ballot(open);
+            if (openm) {  // long runs (lim > 8 for every open lane)
+              const uint32_t o_next =
+                  (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((lane + 1u) & 63u) << 2), (int)o);
+              const bool link = open && lane < 63u && ((openm >> (lane + 1u)) & 1ull) && o_next == o;
+              const uint64_t ends = openm & ~__ballot(link);
+              uint32_t r_end = r;
+              for (uint64_t m = ends; m;) {
+                const uint32_t e = (uint32_t)__builtin_ctzll(m);
+                m &= m - 1ull;
+                const uint32_t pe = (uint32_t)__builtin_amdgcn_readlane((int)p, (int)e);
+                const uint32_t oe = (uint32_t)__builtin_amdgcn_readlane((int)o, (int)e);
+                const uint32_t le = (uint32_t)__builtin_amdgcn_readlane((int)lim, (int)e);
+                uint32_t re = 8u;  // its first 8 matched
+                for (uint32_t k0 = 8u; k0 < le; k0 += 64u) {
+                  const uint32_t idx = k0 + lane;
+                  const bool stop = idx >= le || X[pe + idx] != X[pe + idx - oe];
+                  const uint64_t sm = __ballot(stop);
+                  if (sm) {
+                    re = k0 + (uint32_t)__builtin_ctzll(sm);
+                    break;
+                  }
+                  re = k0 + 64u;
+                }
+                if (lane == e) r_end = re;
+              }
+              // chain members: run = min(lim, distance to the chain's end + its run)
+              const uint64_t after = lane == 63u ? 0ull : (ends >> (lane + 1u)) << (lane + 1u);
+              const uint32_t e = ((ends >> lane) & 1ull) ? lane : (after ? (uint32_t)__builtin_ctzll(after) : lane);
+              const uint32_t re = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(e << 2), (int)r_end);
+              const uint32_t run = re + (e - lane);
+              if (open) r = run < lim ? run : lim;
+            }
+            if (need && r > Lnear) LO[p] = r | (o << 8);
           }
           team_sync<WPC>();
           for (uint32_t p = s * SB + g; p < (s + 1) * SB; p += TL)
