@@ -257,7 +257,7 @@ struct TeamX {
 // truncated quotient is exact.
 __device__ __forceinline__ uint32_t small_mod(uint32_t d, uint32_t o) {
   const uint32_t q = (uint32_t)(((float)d + 0.5f) * __builtin_amdgcn_rcpf((float)o));
-  return d - q * o;
+  return d - __umul24(q, o);  // q, o < 256: a full-rate 24-bit product
 }
 
 // Split mode: where a coded chunk's items are (the GPULZStage page's
@@ -480,7 +480,10 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
     static_assert(NB % 4u == 0u, "windows in groups of four");
 #pragma unroll 1
     for (uint32_t w0 = 0; w0 < NB; w0 += 4u) {
-      uint32_t x[4], link[4];  // link 64: x's source index is final
+      // x: bits 0-15 the source element; bits 16+ the byte address (4 x lane)
+      // of the lane it still links to, or 256 once the source is final
+      // (ds_bpermute reads lane (address / 4) mod 64, so 256 stays harmless)
+      uint32_t x[4];
 #pragma unroll
       for (uint32_t j = 0; j < 4u; ++j) {
         const uint32_t w = w0 + j;
@@ -491,24 +494,28 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
         const uint32_t O = OB[st];
         const uint32_t e0 = O ? st - O + small_mod(q - st, O) : q;
         const uint64_t lit = __ballot(O == 0u);
-        link[j] = 64u;
-        if (O && e0 >= base && !((lit >> (e0 - base)) & 1ull)) link[j] = e0 - base;
-        x[j] = e0 | (link[j] << 16);
+        const uint32_t r = e0 - base;  // < 64 iff the source lies in this window
+        const uint32_t half = (r & 32u) ? (uint32_t)(lit >> 32) : (uint32_t)lit;
+        const bool open = O && r < 64u && __builtin_amdgcn_ubfe(half, r & 31u, 1u) == 0u;
+        x[j] = e0 | ((open ? r << 2 : 256u) << 16);
       }
       // the four windows jump in step: one exchange per window per round
-      for (uint32_t round = 0;
-           __ballot(link[0] < 64u || link[1] < 64u || link[2] < 64u || link[3] < 64u); ++round) {
+      for (uint32_t round = 0;; ++round) {
+        bool open[4];
+        uint64_t any = 0;
+#pragma unroll
+        for (uint32_t j = 0; j < 4u; ++j) {
+          open[j] = (x[j] >> 16) < 256u;
+          any |= __ballot(open[j]);
+        }
+        if (!any) break;
         if (round == 6u) return false;  // unreachable for validated items
         uint32_t y[4];
 #pragma unroll
-        for (uint32_t j = 0; j < 4u; ++j)
-          y[j] = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((link[j] & 63u) << 2), (int)x[j]);
+        for (uint32_t j = 0; j < 4u; ++j) y[j] = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(x[j] >> 16), (int)x[j]);
 #pragma unroll
         for (uint32_t j = 0; j < 4u; ++j)
-          if (link[j] < 64u) {
-            x[j] = y[j];
-            link[j] = y[j] >> 16;
-          }
+          if (open[j]) x[j] = y[j];
       }
       uint32_t src[4];
 #pragma unroll
