@@ -37,7 +37,7 @@ constexpr uint32_t kScanPer = 4;         // chunks per thread per scan round
 constexpr uint32_t kScanRound = kScanPer * kBlock;
 constexpr uint32_t kDecodeGrid = 8192;   // chunk-kernel workgroups at most
 constexpr uint32_t kMaxTilesAlloc = 4096; // split mode: stride of the three tile-total arrays
-constexpr uint32_t kWideMinChunks = 32768; // wide chunks: one per wave from this many chunks on
+constexpr uint32_t kOneWaveMinChunks = 32768; // overlaid chunks: one per wave from this many chunks on
 static_assert(kTileMin % kScanRound == 0 && (uint64_t)kTileMax * 4096u <= (1ull << 32), "tile sizes");
 
 __device__ __forceinline__ uint32_t ld_u32_bytes(const uint8_t* p) {
@@ -162,6 +162,9 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(const uint8_t* __restrict_
 //        after the items are read, SRC, a u16 source index per element;
 //   OB   per element, the offset of the match item starting there (0: none);
 //   STB  the item-start bitmap, one u64 per 64 elements.
+// A one-wave chunk that would not fit one slot this way (chunk 4096 at word
+// size 4) stages its payload over VAL instead (OVL): every lane reads all of
+// its items into registers before any value is stored.
 constexpr uint32_t kSlot = 5376;
 static_assert(kSlot % 16 == 0, "arenas must stay 16-byte aligned (64-bit LDS atomics)");
 constexpr uint32_t kArena = kWaves * kSlot;
@@ -171,17 +174,19 @@ struct Geo {
   static constexpr uint32_t E = CS / WS;                       // elements per chunk
   static constexpr uint32_t PBB = (CS > 2u * E ? CS : 2u * E) + 16u;
   static constexpr uint32_t NEED = CS + PBB + E + E / 8u;
-  // WIDE: a chunk that needs two slots but has few enough elements per lane
-  // for the one-wave decoder (1024 elements: chunk 4096 at word size 4) is
-  // decoded by one wave over two slots; see decode_group_wide.
-  static constexpr bool WIDE = !TEAMS && NEED > kSlot && NEED <= 2u * kSlot && E <= 1024u;
-  static constexpr uint32_t TW = (NEED <= kSlot || WIDE) ? 1u : kWaves;  // waves per chunk
-  static constexpr uint32_t SLOTS = WIDE ? 2u : TW;                        // arena slots per chunk
+  // OVL: the payload (at most CS + 3 bytes, staged in whole dwords) shares
+  // VAL's bytes, so the chunk needs CS + 16 + E + E / 8 bytes: one slot for
+  // 1024 elements (chunk 4096 at word size 4), decoded by one wave.
+  static constexpr bool OVL = !TEAMS && NEED > kSlot && CS + 16u + E + E / 8u <= kSlot && E <= 1024u;
+  static constexpr uint32_t TW = (NEED <= kSlot || OVL) ? 1u : kWaves;  // waves per chunk
+  static constexpr uint32_t PB_AT = OVL ? 0u : CS;               // byte offsets in the arena
+  static constexpr uint32_t OB_AT = OVL ? CS + 16u : CS + PBB;
+  static constexpr uint32_t STB_AT = OB_AT + E;
   static constexpr uint32_t TL = 64u * TW;                     // lanes per chunk
   static constexpr uint32_t J = E / TL;                        // elements per lane
   static constexpr uint32_t NB = E / 64u;                      // 64-element blocks
   static constexpr uint32_t RMAX = J + 1u;                     // items per lane, at most
-  static_assert(NEED <= SLOTS * kSlot, "chunk working set exceeds its arena");
+  static_assert(STB_AT + E / 8u <= TW * kSlot && STB_AT % 16u == 0u, "chunk working set exceeds its arena");
   static_assert(E % TL == 0 && NB <= 64u && RMAX < 25u, "lane mapping");
 };
 
@@ -287,10 +292,10 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
   TeamX<TW> tx{sh, 0u};
   const uint32_t g = threadIdx.x % TL, lane = lane_id();
   uint8_t* VAL = arena;
-  uint8_t* PB = arena + CS;
-  uint16_t* SRC = (uint16_t*)PB;
-  uint8_t* OB = PB + G::PBB;
-  uint64_t* STB = (uint64_t*)(OB + E);
+  uint8_t* PB = arena + G::PB_AT;
+  uint16_t* SRC = (uint16_t*)PB;  // several waves per chunk only (never OVL)
+  uint8_t* OB = arena + G::OB_AT;
+  uint64_t* STB = (uint64_t*)(arena + G::STB_AT);
 
   if constexpr (SPLIT) F = (sp.K + 7u) / 8u;
   // every live item covers at least one element: at most E items, so at most
@@ -386,53 +391,92 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
       m += mt ? 1u : 0u;
     }
   };
+  // an item's record: a match's length | offset << 8 (0 if unreadable), a
+  // literal's value (0 if unreadable; its length follows from cur alone)
+  auto item_rec = [&](uint32_t cur, uint32_t m, bool mt) -> uint32_t {
+    const uint32_t len = item_len(cur, m, mt);
+    if (len == 0u) return 0u;
+    if (mt) return len | ((uint32_t)(SPLIT ? OFFB[m] : PD[cur + 1u]) << 8);
+    const uint8_t* w = SPLIT ? LITB + WS * cur : PD + cur;  // 2-byte aligned for WS >= 2
+    if constexpr (WS == 4) return (uint32_t)*(const uint16_t*)w | ((uint32_t)*(const uint16_t*)(w + 2u) << 16);
+    else if constexpr (WS == 2) return (uint32_t)*(const uint16_t*)w;
+    else return (uint32_t)*w;
+  };
+  uint32_t rec[G::OVL ? G::RMAX : 1u];  // OVL: this lane's item records
   uint32_t sum = 0;
   {
     uint32_t cur = c0, m = m0;
+    if constexpr (G::OVL) {
+#pragma unroll
+      for (uint32_t r = 0; r < G::RMAX; ++r) {
+        rec[r] = 0u;
+        if (r < nit) {
+          const bool mt = (fb >> r) & 1u;
+          rec[r] = item_rec(cur, m, mt);
+          sum += mt ? (rec[r] & 0xFFu) : item_len(cur, m, false);
+          advance(cur, m, mt);
+        }
+      }
+    } else {
 #pragma unroll 4
-    for (uint32_t r = 0; r < G::RMAX; ++r) {
-      if (r < nit) {
-        const bool mt = (fb >> r) & 1u;
-        sum += item_len(cur, m, mt);
-        advance(cur, m, mt);
+      for (uint32_t r = 0; r < G::RMAX; ++r) {
+        if (r < nit) {
+          const bool mt = (fb >> r) & 1u;
+          sum += item_len(cur, m, mt);
+          advance(cur, m, mt);
+        }
       }
     }
   }
   uint32_t len_total;
   uint32_t op = tx.scan(sum, &len_total);
+  // split mode: the flag bits past the last item must be 0 (read here, before
+  // OVL values may land on the flag bytes)
+  const bool pad = SPLIT && (sp.K & 7u) != 0u && (FL[F - 1u] >> (sp.K & 7u)) != 0u;
+  // OVL: every lane's payload reads are issued before any value store below
+  if constexpr (G::OVL) wave_sync();
   uint32_t K = 0, MK = 0, bad = 0, ends = 0;
+  // place one item starting at element op
+  auto place = [&](uint32_t len, bool mt, uint32_t rc) {
+    if (op < E) {  // live: starts before the chunk's end
+      ++K;
+      if (len == 0u) {
+        bad = 1u;  // unreadable, or a zero-length match
+      } else if (mt) {
+        ++MK;
+        const uint32_t O = rc >> 8;
+        if (O == 0u || O > op || op + len > E) bad = 1u;
+        else OB[op] = (uint8_t)O;
+      } else {
+        if constexpr (WS == 4) *(uint32_t*)(VAL + 4u * op) = rc;
+        else if constexpr (WS == 2) *(uint16_t*)(VAL + 2u * op) = (uint16_t)rc;
+        else VAL[op] = (uint8_t)rc;
+      }
+      if (len != 0u) atomicOr((unsigned long long*)&STB[op >> 6], 1ull << (op & 63u));
+      if (op + len == E) ends = 1u;
+    }
+    op += len;
+  };
   {
     uint32_t cur = c0, m = m0;
-#pragma unroll 4
-    for (uint32_t r = 0; r < G::RMAX; ++r) {
-      if (r < nit) {
-        const bool mt = (fb >> r) & 1u;
-        const uint32_t len = item_len(cur, m, mt);
-        if (op < E) {  // live: starts before the chunk's end
-          ++K;
-          if (len == 0u) {
-            bad = 1u;  // unreadable, or a zero-length match
-          } else if (mt) {
-            ++MK;
-            const uint32_t O = SPLIT ? OFFB[m] : PD[cur + 1u];
-            if (O == 0u || O > op || op + len > E) bad = 1u;
-            else OB[op] = (uint8_t)O;
-          } else {
-            const uint8_t* w = SPLIT ? LITB + WS * cur : PD + cur;  // 2-byte aligned for WS >= 2
-            if constexpr (WS == 4) {
-              *(uint32_t*)(VAL + 4u * op) =
-                  (uint32_t)*(const uint16_t*)w | ((uint32_t)*(const uint16_t*)(w + 2u) << 16);
-            } else if constexpr (WS == 2) {
-              *(uint16_t*)(VAL + 2u * op) = *(const uint16_t*)w;
-            } else {
-              VAL[op] = *w;
-            }
-          }
-          if (len != 0u) atomicOr((unsigned long long*)&STB[op >> 6], 1ull << (op & 63u));
-          if (op + len == E) ends = 1u;
+    if constexpr (G::OVL) {
+#pragma unroll
+      for (uint32_t r = 0; r < G::RMAX; ++r) {
+        if (r < nit) {
+          const bool mt = (fb >> r) & 1u;
+          place(mt ? (rec[r] & 0xFFu) : item_len(cur, m, false), mt, rec[r]);
+          advance(cur, m, mt);
         }
-        op += len;
-        advance(cur, m, mt);
+      }
+    } else {
+#pragma unroll 4
+      for (uint32_t r = 0; r < G::RMAX; ++r) {
+        if (r < nit) {
+          const bool mt = (fb >> r) & 1u;
+          const uint32_t rc = item_rec(cur, m, mt);
+          place(mt ? (rc & 0xFFu) : item_len(cur, m, false), mt, rc);
+          advance(cur, m, mt);
+        }
       }
     }
   }
@@ -444,7 +488,6 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
     if constexpr (SPLIT) {
       // all K items are live and cover exactly E elements, M of them are
       // matches, and the flag bits past the last item are 0
-      const bool pad = (sp.K & 7u) != 0u && (FL[F - 1u] >> (sp.K & 7u)) != 0u;
       if (badt || endst != 1u || Kt != sp.K || MKt != sp.M || mt_total != sp.M || pad) return false;
     } else {
       // the live items cover exactly E elements, use exactly D data bytes and
@@ -605,89 +648,11 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
   return !tx.any(padbad);
 }
 
-// Wide chunks (two slots, one wave): a workgroup takes chunks blockIdx.x +
-// k * gridDim.x, 64 at a time.  Waves 0 and 2 decode the coded ones (each
-// in two slots), waves 1 and 3 fill or copy the zero and raw ones (all four
-// share the stored ones when a batch has no coded chunk), so the copies run
-// beside the decodes and no wave waits for another: there is no barrier.
-template <uint32_t CS, uint32_t WS>
-__device__ __forceinline__ void decode_group_wide(const DecP& p, const uint8_t* in, const uint8_t* lim, uint8_t* out,
-                                                  const uint32_t* loc, const uint64_t* tile_sum, uint32_t* status,
-                                                  uint64_t* out_bytes, uint8_t* arena_all, uint32_t* sh) {
-  using G = Geo<CS, WS>;
-  static_assert(kWaves == 4 && G::SLOTS == 2, "two decoding and two copying waves");
-  const uint32_t lane = lane_id(), w = threadIdx.x >> 6;
-  uint8_t* arena = arena_all + (w & 2u) * kSlot;  // waves 0 and 2: slots 0-1 and 2-3
-  const uint64_t stride = gridDim.x;
-  uint64_t pre = 0;
-  if (p.ntiles <= 64u) {
-    const uint64_t v = lane < p.ntiles ? tile_sum[lane] : 0ull;
-    pre = wave_incl_add64(v) - v;
-  }
-  for (uint64_t k0 = 0;; k0 += 64u) {
-    if ((uint64_t)blockIdx.x + k0 * stride >= p.nc) break;
-    // this batch's metadata, one chunk per lane (every wave loads it)
-    const uint64_t cc = (uint64_t)blockIdx.x + (k0 + lane) * stride;
-    const bool live = cc < p.nc;
-    const uint32_t t = live ? (uint32_t)(cc / p.T) : 0u;
-    const uint32_t plo = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((t & 63u) << 2), (int)(uint32_t)pre);
-    const uint32_t phi = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((t & 63u) << 2), (int)(uint32_t)(pre >> 32));
-    uint64_t tp = (uint64_t)plo | ((uint64_t)phi << 32);
-    uint2 e = make_uint2(0u, 0u);
-    uint64_t off = 0;
-    uint32_t bc = 0;
-    bool ok = false;
-    if (live) {
-      e = read_row(in, cc);
-      if (p.ntiles > 64u) {  // huge streams only: this lane adds the earlier tiles itself
-        tp = 0;
-        for (uint32_t i = 0; i < t; ++i) tp += tile_sum[i];
-      }
-      off = tp + loc[cc];
-      const uint64_t start = cc * CS;
-      bc = (uint32_t)((p.n - start) < CS ? (p.n - start) : CS);
-      // bad rows are reported by the scan kernel, sizes inconsistent with
-      // the header by wave 0 of workgroup 0
-      ok = row_ok(e, bc) && off + entry_payload(e.x, e.y) <= p.pb;
-    }
-    const uint64_t coded = __ballot(ok && e.x != 0u), stored = __ballot(ok && e.x == 0u);
-    const uint64_t below = lane == 0u ? 0ull : (~0ull >> (64u - lane));
-    // my chunks: coded ones of my parity (waves 0, 2), stored ones of my
-    // parity (waves 1, 3), or every fourth stored one when none is coded
-    const uint32_t crank = (uint32_t)__builtin_popcountll(coded & below);
-    const uint32_t srank = (uint32_t)__builtin_popcountll(stored & below);
-    uint64_t mine;
-    if (coded == 0ull) mine = __ballot(((stored >> lane) & 1ull) && (srank & 3u) == w);
-    else if ((w & 1u) == 0u) mine = __ballot(((coded >> lane) & 1ull) && (crank & 1u) == (w >> 1));
-    else mine = __ballot(((stored >> lane) & 1ull) && (srank & 1u) == (w >> 1));
-    while (mine) {
-      const int j = (int)__builtin_ctzll(mine);
-      mine &= mine - 1ull;
-      const uint2 ej = make_uint2((uint32_t)__builtin_amdgcn_readlane((int)e.x, j),
-                                  (uint32_t)__builtin_amdgcn_readlane((int)e.y, j));
-      const uint32_t bj = (uint32_t)__builtin_amdgcn_readlane((int)bc, j);
-      const uint64_t oj = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)off, j) |
-                          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(off >> 32), j) << 32);
-      const uint64_t c = (uint64_t)blockIdx.x + (k0 + (uint64_t)j) * stride;
-      const uint8_t* pay = in + p.base + oj;
-      uint8_t* dst = out + c * CS;
-      if (ej.x == 0u) {
-        if (ej.y == 0u) zero_bytes16(dst, bj, lane);
-        else copy_bytes16_r1(dst, pay, bj, lane);
-      } else {
-        if (!decode_coded<CS, WS>(pay, lim, ej.x, ej.y, bj, dst, arena, sh + 2u * w, SplitSrc{}) && lane == 0u)
-          raise_status(status, out_bytes, kStatusCorrupt);
-        wave_sync();
-      }
-    }
-  }
-}
-
-template <uint32_t CS, uint32_t WS>
+template <uint32_t CS, uint32_t WS, bool TEAMS>
 __device__ __forceinline__ void decode_group_teams(const DecP& p, const uint8_t* in, const uint8_t* lim, uint8_t* out,
                                                    const uint32_t* loc, const uint64_t* tile_sum, uint32_t* status,
                                                    uint64_t* out_bytes, uint8_t* arena_all, uint32_t* sh) {
-  using G = Geo<CS, WS, true>;
+  using G = Geo<CS, WS, TEAMS>;
   constexpr uint32_t TL = G::TL;
   constexpr uint32_t CPW = kWaves / G::TW;  // chunks per workgroup
   const uint32_t team = threadIdx.x / TL, g = threadIdx.x % TL;
@@ -751,7 +716,7 @@ __device__ __forceinline__ void decode_group_teams(const DecP& p, const uint8_t*
       if (e.y == 0u) zero_bytes16(dst + w0, len, lane);
       else copy_bytes16_r1(dst + w0, pay + w0, len, lane);
     } else {
-      if (!decode_coded<CS, WS, false, true>(pay, lim, e.x, e.y, bc, dst, arena, sh, SplitSrc{}) && g == 0)
+      if (!decode_coded<CS, WS, false, TEAMS>(pay, lim, e.x, e.y, bc, dst, arena, sh, SplitSrc{}) && g == 0)
         raise_status(status, out_bytes, kStatusCorrupt);
     }
     team_sync<G::TW>();
@@ -762,15 +727,16 @@ template <uint32_t CS, uint32_t WS>
 __device__ __forceinline__ void decode_group(const DecP& p, const uint8_t* in, const uint8_t* lim, uint8_t* out,
                              const uint32_t* loc, const uint64_t* tile_sum, uint32_t* status, uint64_t* out_bytes,
                              uint8_t* arena_all, uint32_t* sh) {
-  // Wide chunks go one per wave only when there are enough of them to keep
-  // every CU busy; a small stream decodes faster with a workgroup per chunk.
-  if constexpr (Geo<CS, WS>::WIDE) {
-    if (p.nc >= kWideMinChunks) {
-      decode_group_wide<CS, WS>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena_all, sh);
+  // Chunks that fit one slot only with the payload over the values go one
+  // per wave when there are enough of them to keep every CU busy; a small
+  // stream decodes faster with a workgroup per chunk.
+  if constexpr (Geo<CS, WS>::OVL) {
+    if (p.nc >= kOneWaveMinChunks) {
+      decode_group_teams<CS, WS, false>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena_all, sh);
       return;
     }
   }
-  decode_group_teams<CS, WS>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena_all, sh);
+  decode_group_teams<CS, WS, true>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena_all, sh);
 }
 
 template <uint32_t CS>
@@ -925,11 +891,9 @@ __device__ __forceinline__ void decode_group_split(const DecP& p, const SplitDec
                                                    const uint64_t* tile_sum, uint8_t* arena_all, uint32_t* sh) {
   using G = Geo<CS, WS>;
   constexpr uint32_t TL = G::TL;
-  constexpr uint32_t CPW = kWaves / G::SLOTS;  // chunks per workgroup
-  // a wide chunk is one wave's in two slots: waves 0 and 2 decode, 1 and 3 rest
-  if (G::WIDE && ((threadIdx.x >> 6) & 1u)) return;
-  const uint32_t team = threadIdx.x / (64u * G::SLOTS), g = threadIdx.x % TL, lane = lane_id();
-  uint8_t* arena = arena_all + team * (G::SLOTS * kSlot);
+  constexpr uint32_t CPW = kWaves / G::TW;  // chunks per workgroup
+  const uint32_t team = threadIdx.x / TL, g = threadIdx.x % TL, lane = lane_id();
+  uint8_t* arena = arena_all + team * (G::TW * kSlot);
   const uint8_t* flags = a.meta + p.base;
   const uint8_t* meta_lim = a.meta + a.meta_bytes;
   const uint64_t stride = (uint64_t)gridDim.x * CPW;

@@ -250,11 +250,11 @@ def test_corrupted_streams(g, oracle_mod):
             assert np.array_equal(dbuf[:r].cpu().numpy(), ref_out)
 
 
-def test_many_wide_chunks(g, oracle_mod):
+def test_many_one_wave_chunks(g, oracle_mod):
     """A stream of 33,000 chunks of 4096 bytes at word size 4 (enough that
-    each chunk is decoded by one wave, with separate copying waves): the
-    oracle's stream decodes to the input, and corrupting one coded chunk's
-    match token gives the oracle's verdict."""
+    each chunk is decoded by one wave, its payload staged over its decoded
+    bytes): the oracle's stream decodes to the input, and corrupting one
+    coded chunk's match token gives the oracle's verdict."""
     from chunked_lzss_coder_amd import synth
     cs, ws = 4096, 4
     n = 33000 * cs - 1000  # ragged tail
