@@ -497,6 +497,11 @@ def main(argv=None) -> int:
         "measured_copy_gbps": copy_gbps,
         "kernel_ms": r0["encode_kernel_ms"],
         "algorithmic_bytes_per_launch": r0["algorithmic_bytes"],
+        # the stricter reading: input bytes only over the same kernel time
+        "frac_input_only": round(w.n / (r0["encode_kernel_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 5),
+        # the decode kernel of the same level against the same peak
+        "decode_frac": round(r0["decode_kernel_hbm_gbps"] / HBM_PEAK_GBPS, 5),
+        "decode_frac_input_only": round(w.n / (r0["decode_kernel_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 5),
     }
 
     cpu = None
