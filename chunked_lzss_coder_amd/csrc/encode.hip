@@ -460,10 +460,15 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
       }
 
       // ---- 4. level 1 ----------------------------------------------------------------------
+      // matched: some position has a match (near or hashed); otherwise the
+      // parse would be E literals, so the chunk is raw without one
+      bool matched = true;
       if (LEVEL == 1) {
+        bool hit = false;
         for (uint32_t i = g; i < kHashSize; i += TL) T[i] = 0u;
         team_sync<WPC>();  // T overlays dead table levels
         constexpr uint32_t SB = E / kSubBlocks;
+        static_assert(SB <= TL, "one position per lane per sub-block");
 #pragma unroll 1
         for (uint32_t s = 0; s < kSubBlocks; ++s) {
           // One position per lane (consecutive lanes, consecutive positions).
@@ -473,12 +478,17 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
           // compares.  Runs still open after that are shared along lanes:
           // when lanes l and l + 1 are open at the same offset, run(p) =
           // min(lim(p), run(p + 1) + 1), so only the last lane of such a chain
-          // measures on, with the whole wave, 64 compares per step.
-          for (uint32_t p = s * SB + g; p < (s + 1) * SB; p += TL) {
+          // measures on, with the whole wave, 64 compares per step.  A
+          // sub-block has at most one position per lane (SB <= TL); its
+          // bucket is kept for the insert below.
+          const uint32_t p = s * SB + g;
+          const bool ins = g < SB && p + 1 < (uint32_t)E;
+          const uint32_t bk = ins ? bucket_of(X[p], X[p + 1]) : 0u;
+          if (g < SB) {
             uint32_t o = 0, Lnear = 0, lim = 0;
             bool need = false;
-            if (p + 1 < (uint32_t)E) {
-              const uint32_t v = T[bucket_of(X[p], X[p + 1])];
+            if (ins) {
+              const uint32_t v = T[bk];
               o = p - (v - 1u);  // entries come from earlier sub-blocks: o >= 1
               lim = (uint32_t)E - p < kMaxLen ? (uint32_t)E - p : kMaxLen;
               Lnear = LO[p] & 0xFFu;
@@ -526,133 +536,141 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
               const uint32_t run = re + (e - lane);
               if (open) r = run < lim ? run : lim;
             }
-            if (need && r > Lnear) LO[p] = r | (o << 8);
+            if (need && r > Lnear) {
+              LO[p] = r | (o << 8);
+              hit = true;
+            }
           }
           team_sync<WPC>();
-          for (uint32_t p = s * SB + g; p < (s + 1) * SB; p += TL)
-            if (p + 1 < (uint32_t)E) atomicMax(&T[bucket_of(X[p], X[p + 1])], p + 1u);
+          if (ins) atomicMax(&T[bk], p + 1u);
           team_sync<WPC>();
         }
+        if (WPC == 1) matched = near || __ballot(hit) != 0ull;
+        else matched = near || __syncthreads_or(hit);
       }
 
-      // ---- 5. parallel greedy parse --------------------------------------------------------
-      // (a) per segment of 8 positions: for every entry q, the exit position and
-      //     the item-start mask of the parse walked from q.
-      for (uint32_t sg = g; sg < L::NSEG; sg += TL) {
-        const uint32_t p0 = sg * 8u;
-        const uint4 a = *(const uint4*)(LO + p0);
-        const uint4 b = *(const uint4*)(LO + p0 + 4);
-        const uint32_t l8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        uint32_t ex[8], im[8], lmb = 0;
-#pragma unroll
-        for (int q = 7; q >= 0; --q) {
-          const uint32_t len = l8[q] & 0xFFu;
-          const bool mt = len >= MM;
-          lmb |= (mt ? 1u : 0u) << q;
-          const uint32_t nq = (uint32_t)q + (mt ? len : 1u);
-          uint32_t e = p0 + nq, m = 1u << q;
-#pragma unroll
-          for (int r = q + 1; r < 8; ++r)
-            if (nq == (uint32_t)r) {
-              e = ex[r];
-              m = (1u << q) | im[r];
-            }
-          ex[q] = e;
-          im[q] = m;
-        }
-        *(uint4*)(XQ + p0) = make_uint4(ex[0] | (im[0] << 16), ex[1] | (im[1] << 16), ex[2] | (im[2] << 16),
-                                        ex[3] | (im[3] << 16));
-        *(uint4*)(XQ + p0 + 4) = make_uint4(ex[4] | (im[4] << 16), ex[5] | (im[5] << 16),
-                                            ex[6] | (im[6] << 16), ex[7] | (im[7] << 16));
-        if (WPC > 1) {
-          ((uint8_t*)LMB)[sg] = (uint8_t)lmb;
-          ((uint8_t*)ISB)[sg] = 0;
-        }
-      }
-      team_sync<WPC>();
-      // (b) hops: the parse's real entry into every segment it passes through
-      if constexpr (WPC == 1) {
-        // exits held in registers (lane j of word i = position 64i + j); the hop
-        // position P is uniform, so each hop is one readlane
-        uint32_t xqr[NR];
-#pragma unroll
-        for (uint32_t i = 0; i < NR; ++i) {
-          const uint32_t p = 64u * i + lane;
-          xqr[i] = XQ[p];
-          lmw[i] = __ballot((LO[p] & 0xFFu) >= MM);
-        }
-        uint32_t P = 0;
-#pragma unroll
-        for (uint32_t i = 0; i < NR; ++i) {
-          uint64_t acc = 0;
-          while (P < 64u * (i + 1u)) {
-            const uint32_t xq = __builtin_amdgcn_readlane(xqr[i], P & 63u);
-            acc |= (uint64_t)(xq >> 16) << (P & 56u);
-            P = xq & 0xFFFFu;
-          }
-          isw[i] = acc;
-        }
-        // ---- 6. counts -------------------------------------------------------------------
-#pragma unroll
-        for (uint32_t i = 0; i < NR; ++i) {
-          kb[i] = K;
-          mb[i] = M;
-          K += (uint32_t)__builtin_popcountll(isw[i]);
-          M += (uint32_t)__builtin_popcountll(isw[i] & lmw[i]);
-        }
+      if (!matched) {
+        K = (uint32_t)E;
       } else {
-        if (g < 64u) {
-          // the first wave hops word by word: the exits of 64 positions in one
-          // VGPR (the next word's load in flight), one readlane per hop
-          uint64_t* IS64w = (uint64_t*)ISB;
-          uint32_t P = 0;
-          uint32_t xq_next = XQ[lane];
-#pragma unroll 1
+        // ---- 5. parallel greedy parse --------------------------------------------------------
+        // (a) per segment of 8 positions: for every entry q, the exit position and
+        //     the item-start mask of the parse walked from q.
+        for (uint32_t sg = g; sg < L::NSEG; sg += TL) {
+          const uint32_t p0 = sg * 8u;
+          const uint4 a = *(const uint4*)(LO + p0);
+          const uint4 b = *(const uint4*)(LO + p0 + 4);
+          const uint32_t l8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+          uint32_t ex[8], im[8], lmb = 0;
+#pragma unroll
+          for (int q = 7; q >= 0; --q) {
+            const uint32_t len = l8[q] & 0xFFu;
+            const bool mt = len >= MM;
+            lmb |= (mt ? 1u : 0u) << q;
+            const uint32_t nq = (uint32_t)q + (mt ? len : 1u);
+            uint32_t e = p0 + nq, m = 1u << q;
+#pragma unroll
+            for (int r = q + 1; r < 8; ++r)
+              if (nq == (uint32_t)r) {
+                e = ex[r];
+                m = (1u << q) | im[r];
+              }
+            ex[q] = e;
+            im[q] = m;
+          }
+          *(uint4*)(XQ + p0) = make_uint4(ex[0] | (im[0] << 16), ex[1] | (im[1] << 16), ex[2] | (im[2] << 16),
+                                          ex[3] | (im[3] << 16));
+          *(uint4*)(XQ + p0 + 4) = make_uint4(ex[4] | (im[4] << 16), ex[5] | (im[5] << 16),
+                                              ex[6] | (im[6] << 16), ex[7] | (im[7] << 16));
+          if (WPC > 1) {
+            ((uint8_t*)LMB)[sg] = (uint8_t)lmb;
+            ((uint8_t*)ISB)[sg] = 0;
+          }
+        }
+        team_sync<WPC>();
+        // (b) hops: the parse's real entry into every segment it passes through
+        if constexpr (WPC == 1) {
+          // exits held in registers (lane j of word i = position 64i + j); the hop
+          // position P is uniform, so each hop is one readlane
+          uint32_t xqr[NR];
+#pragma unroll
           for (uint32_t i = 0; i < NR; ++i) {
-            const uint32_t xqr = xq_next;
-            if (i + 1u < NR) xq_next = XQ[64u * (i + 1u) + lane];
+            const uint32_t p = 64u * i + lane;
+            xqr[i] = XQ[p];
+            lmw[i] = __ballot((LO[p] & 0xFFu) >= MM);
+          }
+          uint32_t P = 0;
+#pragma unroll
+          for (uint32_t i = 0; i < NR; ++i) {
             uint64_t acc = 0;
             while (P < 64u * (i + 1u)) {
-              const uint32_t xq = __builtin_amdgcn_readlane(xqr, P & 63u);
+              const uint32_t xq = __builtin_amdgcn_readlane(xqr[i], P & 63u);
               acc |= (uint64_t)(xq >> 16) << (P & 56u);
               P = xq & 0xFFFFu;
             }
-            if (lane == 0u) IS64w[i] = acc;
+            isw[i] = acc;
           }
-        }
-        team_sync<WPC>();
-        // ---- 6. counts (first wave) --------------------------------------------------------
-        const uint64_t* IS64 = (const uint64_t*)ISB;
-        const uint64_t* LM64 = (const uint64_t*)LMB;
-        if (g < 64u) {
-          uint32_t kc = 0, mc = 0;
-          if (g < NR) {
-            const uint64_t is = IS64[g];
-            kc = __builtin_popcountll(is);
-            mc = __builtin_popcountll(is & LM64[g]);
-          }
-          uint32_t ki = kc, mi = mc;
+          // ---- 6. counts -------------------------------------------------------------------
 #pragma unroll
-          for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t a = __shfl_up(ki, d, 64), b = __shfl_up(mi, d, 64);
-            if (lane >= (uint32_t)d) {
-              ki += a;
-              mi += b;
+          for (uint32_t i = 0; i < NR; ++i) {
+            kb[i] = K;
+            mb[i] = M;
+            K += (uint32_t)__builtin_popcountll(isw[i]);
+            M += (uint32_t)__builtin_popcountll(isw[i] & lmw[i]);
+          }
+        } else {
+          if (g < 64u) {
+            // the first wave hops word by word: the exits of 64 positions in one
+            // VGPR (the next word's load in flight), one readlane per hop
+            uint64_t* IS64w = (uint64_t*)ISB;
+            uint32_t P = 0;
+            uint32_t xq_next = XQ[lane];
+#pragma unroll 1
+            for (uint32_t i = 0; i < NR; ++i) {
+              const uint32_t xqr = xq_next;
+              if (i + 1u < NR) xq_next = XQ[64u * (i + 1u) + lane];
+              uint64_t acc = 0;
+              while (P < 64u * (i + 1u)) {
+                const uint32_t xq = __builtin_amdgcn_readlane(xqr, P & 63u);
+                acc |= (uint64_t)(xq >> 16) << (P & 56u);
+                P = xq & 0xFFFFu;
+              }
+              if (lane == 0u) IS64w[i] = acc;
             }
           }
-          if (g < NR) {
-            KB[g] = ki - kc;
-            MB[g] = mi - mc;
+          team_sync<WPC>();
+          // ---- 6. counts (first wave) --------------------------------------------------------
+          const uint64_t* IS64 = (const uint64_t*)ISB;
+          const uint64_t* LM64 = (const uint64_t*)LMB;
+          if (g < 64u) {
+            uint32_t kc = 0, mc = 0;
+            if (g < NR) {
+              const uint64_t is = IS64[g];
+              kc = __builtin_popcountll(is);
+              mc = __builtin_popcountll(is & LM64[g]);
+            }
+            uint32_t ki = kc, mi = mc;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+              const uint32_t a = __shfl_up(ki, d, 64), b = __shfl_up(mi, d, 64);
+              if (lane >= (uint32_t)d) {
+                ki += a;
+                mi += b;
+              }
+            }
+            if (g < NR) {
+              KB[g] = ki - kc;
+              MB[g] = mi - mc;
+            }
+            if (g == NR - 1u) {
+              SC[1] = ki;
+              SC[2] = mi;
+            }
           }
-          if (g == NR - 1u) {
-            SC[1] = ki;
-            SC[2] = mi;
-          }
+          team_sync<WPC>();
+          K = SC[1];
+          M = SC[2];
         }
-        team_sync<WPC>();
-        K = SC[1];
-        M = SC[2];
-      }
+      }  // some match
     }  // near match, or level 1
   }  // nonzero
   const uint32_t F = (K + 7u) / 8u;
