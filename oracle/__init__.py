@@ -89,6 +89,12 @@ def _load():
     lib.oracle_encode_w.restype = ctypes.c_int64
     lib.oracle_lorenzo_quant.argtypes = [u8p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_double, u8p]
     lib.oracle_lorenzo_quant.restype = ctypes.c_uint64
+    lib.oracle_advancing_match.argtypes = [u8p, ctypes.c_uint32, ctypes.c_uint32,
+                                           ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32)]
+    lib.oracle_advancing_match.restype = None
+    lib.oracle_encode_advancing.argtypes = [u8p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, u8p,
+                                            ctypes.c_uint64]
+    lib.oracle_encode_advancing.restype = ctypes.c_int64
     _lib = lib
     return lib
 
@@ -121,6 +127,29 @@ def near_match(x: np.ndarray, p: int, window: int = 32) -> tuple[int, int]:
     else:
         _load().oracle_near_match_w(_ptr(x), x.size, p, window, ctypes.byref(L), ctypes.byref(O))
     return L.value, O.value
+
+
+def advancing_match(x: np.ndarray, p: int) -> tuple[int, int]:
+    """(L, O) of the upstream-style advancing-window search at element p of
+    chunk x (uint32): the reading in oracle_advancing_match."""
+    x = np.ascontiguousarray(x, dtype=np.uint32)
+    L, O = ctypes.c_uint32(), ctypes.c_uint32()
+    _load().oracle_advancing_match(_ptr(x), x.size, p, ctypes.byref(L), ctypes.byref(O))
+    return L.value, O.value
+
+
+def encode_advancing(data, chunk_size: int, word_size: int) -> np.ndarray:
+    """Level-0 stream with the advancing-window search in place of the exact
+    one; returns the stream as a uint8 array."""
+    a = _bytes(data)
+    cap = max_stream_size(a.size, chunk_size)
+    if cap == 0:
+        raise ValueError("unsupported chunk_size")
+    out = np.empty(cap, dtype=np.uint8)
+    r = _load().oracle_encode_advancing(_ptr(a), a.size, chunk_size, word_size, _ptr(out), cap)
+    if r < 0:
+        raise ValueError(f"oracle_encode_advancing status {r}")
+    return out[:r]
 
 
 def level1_candidates(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:

@@ -21,7 +21,9 @@
  * Parity pins: every function here is pinned by the CPU tests (hand-worked
  * streams, brute-force longest match on tiny inputs, an independent
  * omask-AND search, round trips, an independent Python stream walker, an
- * independent level-1 table simulation, corrupted-stream rejection).
+ * independent level-1 table simulation, corrupted-stream rejection; the
+ * upstream-style advancing search by hand-worked matches, a closed form on
+ * constant chunks and a hand-built stream).
  */
 #include <math.h>
 #include <stdint.h>
@@ -123,6 +125,35 @@ void oracle_near_match(const uint32_t* x, uint32_t E, uint32_t p, uint32_t* L, u
   oracle_near_match_w(x, E, p, OR_WINDOW, L, O);
 }
 
+/* The upstream-style search the page contrasts with its own (exact
+ * longest-match search paragraph): the window pointer advances on every
+ * step, so a match being extended carries the pointer with it and the
+ * candidate starts it passes over are never tried.  The page gives no more
+ * than that; the reading here: the pointer w walks the 32 elements before p
+ * (never before the chunk start), one comparison per step, of x[w] against
+ * the element the current partial match needs next, x[p + len].  Equal:
+ * the partial match (starting at w - len) grows by one; unequal: it is
+ * dropped and this w is spent.  The longest partial match seen is the
+ * result (the first one on ties); it never reaches past p - 1 as a source,
+ * so L <= 32, and never past the chunk end.  L = 0: nothing matched. */
+void oracle_advancing_match(const uint32_t* x, uint32_t E, uint32_t p, uint32_t* L, uint32_t* O) {
+  uint32_t best = 0, bestO = 0, len = 0;
+  uint32_t w = p < OR_WINDOW ? 0u : p - OR_WINDOW;
+  for (; w < p; ++w) {
+    if (p + len < E && x[w] == x[p + len]) {
+      len += 1;
+      if (len > best) {
+        best = len;
+        bestO = p - (w + 1u - len); /* the match starts at w + 1 - len */
+      }
+    } else {
+      len = 0;
+    }
+  }
+  *L = best;
+  *O = bestO;
+}
+
 /* Level-1 candidates for every position of one chunk (page: hashed
  * long-range paragraph; sub-block walk and atomicMax(position+1) insert).
  * Table entries hold position+1, 0 = empty.  For sub-block s, every
@@ -168,10 +199,11 @@ static uint32_t min_match(uint32_t ws) { return ws >= 4u ? 1u : (ws == 2u ? 2u :
  * *flag_size / *data_size hold the 8-byte size-table entry and payload[]
  * (capacity >= cs) holds *payload_bytes bytes.
  * Returns OR_OK or OR_EINVAL. */
-int oracle_encode_chunk_w(const uint8_t* bytes, uint32_t bc, uint32_t cs, uint32_t ws, uint32_t level,
-                          uint32_t window, uint32_t* flag_size, uint32_t* data_size, uint8_t* payload,
-                          uint32_t* payload_bytes) {
+static int encode_chunk_search(const uint8_t* bytes, uint32_t bc, uint32_t cs, uint32_t ws, uint32_t level,
+                               uint32_t window, int advancing, uint32_t* flag_size, uint32_t* data_size,
+                               uint8_t* payload, uint32_t* payload_bytes) {
   if (!cs_ok(cs) || !ws_ok(ws) || level > 1u || !window_ok(window) || bc == 0 || bc > cs) return OR_EINVAL;
+  if (advancing && level != 0u) return OR_EINVAL;
   uint32_t E = cs / ws;
   uint8_t* padded = (uint8_t*)calloc(cs, 1);
   memcpy(padded, bytes, bc);
@@ -206,7 +238,8 @@ int oracle_encode_chunk_w(const uint8_t* bytes, uint32_t bc, uint32_t cs, uint32
   uint32_t p = 0;
   while (p < E) {
     uint32_t L, O;
-    oracle_near_match_w(x, E, p, window, &L, &O);
+    if (advancing) oracle_advancing_match(x, E, p, &L, &O);
+    else oracle_near_match_w(x, E, p, window, &L, &O);
     if (cand && cand[p] != 0) {
       uint32_t r = run_at(x, E, p, cand[p]);
       if (r > L) { L = r; O = cand[p]; } /* hash wins only when strictly longer */
@@ -257,6 +290,12 @@ int oracle_encode_chunk_w(const uint8_t* bytes, uint32_t bc, uint32_t cs, uint32
   return OR_OK;
 }
 
+int oracle_encode_chunk_w(const uint8_t* bytes, uint32_t bc, uint32_t cs, uint32_t ws, uint32_t level,
+                          uint32_t window, uint32_t* flag_size, uint32_t* data_size, uint8_t* payload,
+                          uint32_t* payload_bytes) {
+  return encode_chunk_search(bytes, bc, cs, ws, level, window, 0, flag_size, data_size, payload, payload_bytes);
+}
+
 int oracle_encode_chunk(const uint8_t* bytes, uint32_t bc, uint32_t cs, uint32_t ws, uint32_t level,
                         uint32_t* flag_size, uint32_t* data_size, uint8_t* payload, uint32_t* payload_bytes) {
   return oracle_encode_chunk_w(bytes, bc, cs, ws, level, OR_WINDOW, flag_size, data_size, payload, payload_bytes);
@@ -267,9 +306,10 @@ int oracle_encode_chunk(const uint8_t* bytes, uint32_t bc, uint32_t cs, uint32_t
  * Payloads are packed back to back in chunk order; chunk offsets are not
  * stored (page: CUDA-graph paragraph, the inverse derives them from sizes).
  * Returns the stream length, or a negative status. */
-int64_t oracle_encode_w(const uint8_t* in, uint64_t n, uint32_t cs, uint32_t ws, uint32_t level, uint32_t window,
-                        uint8_t* out, uint64_t cap) {
+static int64_t encode_search(const uint8_t* in, uint64_t n, uint32_t cs, uint32_t ws, uint32_t level,
+                             uint32_t window, int advancing, uint8_t* out, uint64_t cap) {
   if (!cs_ok(cs) || !ws_ok(ws) || level > 1u || !window_ok(window)) return OR_EINVAL;
+  if (advancing && level != 0u) return OR_EINVAL;
   if (n > 0 && in == NULL) return OR_EINVAL;
   uint64_t chunks = (n + cs - 1) / cs;
   if (chunks > 0xFFFFFFFFull) return OR_EINVAL;
@@ -282,7 +322,7 @@ int64_t oracle_encode_w(const uint8_t* in, uint64_t n, uint32_t cs, uint32_t ws,
     uint64_t start = c * cs;
     uint32_t bc = (uint32_t)((n - start) < cs ? (n - start) : cs);
     uint32_t f, d, pb;
-    int st = oracle_encode_chunk_w(in + start, bc, cs, ws, level, window, &f, &d, pay + total, &pb);
+    int st = encode_chunk_search(in + start, bc, cs, ws, level, window, advancing, &f, &d, pay + total, &pb);
     if (st != OR_OK) return st;
     put_u32(table + OR_ENTRY_BYTES * c, f);
     put_u32(table + OR_ENTRY_BYTES * c + 4, d);
@@ -300,9 +340,21 @@ int64_t oracle_encode_w(const uint8_t* in, uint64_t n, uint32_t cs, uint32_t ws,
   return (int64_t)(OR_HEADER_BYTES + OR_ENTRY_BYTES * chunks + total);
 }
 
+int64_t oracle_encode_w(const uint8_t* in, uint64_t n, uint32_t cs, uint32_t ws, uint32_t level, uint32_t window,
+                        uint8_t* out, uint64_t cap) {
+  return encode_search(in, n, cs, ws, level, window, 0, out, cap);
+}
+
 int64_t oracle_encode(const uint8_t* in, uint64_t n, uint32_t cs, uint32_t ws, uint32_t level, uint8_t* out,
                       uint64_t cap) {
   return oracle_encode_w(in, n, cs, ws, level, OR_WINDOW, out, cap);
+}
+
+/* The same stream with the upstream-style advancing search in place of the
+ * exact one (level 0 only: the greedy parse, the item forms and the raw
+ * fallback are unchanged, so the stream decodes with the same decoder). */
+int64_t oracle_encode_advancing(const uint8_t* in, uint64_t n, uint32_t cs, uint32_t ws, uint8_t* out, uint64_t cap) {
+  return encode_search(in, n, cs, ws, 0u, OR_WINDOW, 1, out, cap);
 }
 
 /* Read the header.  Returns OR_OK or OR_ECORRUPT. */
