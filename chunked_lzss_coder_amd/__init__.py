@@ -19,7 +19,7 @@ SYMBOLS = ("gpulz_max_compressed_size", "gpulz_encode_workspace_size", "gpulz_de
            "gpulz_encode", "gpulz_decode", "gpulz_stream_info", "gpulz_encode_timed", "gpulz_decode_timed",
            "gpulz_split_bounds", "gpulz_encode_split_workspace_size", "gpulz_encode_split",
            "gpulz_decode_split_workspace_size", "gpulz_decode_split", "gpulz_decode_one_thread_per_chunk",
-           "gpulz_lorenzo_quant", "gpulz_encode_window")
+           "gpulz_lorenzo_quant", "gpulz_encode_window", "gpulz_encode_advancing_search")
 
 _lib = None
 
@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
     L.gpulz_decode_one_thread_per_chunk.argtypes = L.gpulz_decode.argtypes + [vp, vp]
     L.gpulz_decode_one_thread_per_chunk.restype = ctypes.c_int
     L.gpulz_encode_window.argtypes = [vp, u64, u32, u32, u32, u32, vp, u64, vp, vp, u64, vp]
+    L.gpulz_encode_advancing_search.argtypes = [vp, u64, u32, u32, vp, u64, vp, vp, u64, vp, vp, vp]
+    L.gpulz_encode_advancing_search.restype = ctypes.c_int
     L.gpulz_encode_window.restype = ctypes.c_int
     L.gpulz_lorenzo_quant.argtypes = [vp, u32, u32, u32, ctypes.c_double, vp, vp, vp]
     L.gpulz_lorenzo_quant.restype = ctypes.c_int
@@ -135,6 +137,18 @@ def encode_window_into(d_in, chunk_size: int, word_size: int, match_level: int, 
     _check(lib().gpulz_encode_window(_ptr(src), src.numel(), chunk_size, word_size, match_level, window, _ptr(out),
                                      out.numel(), _ptr(out_bytes), _ptr(workspace), workspace.numel(),
                                      _stream(stream)), "gpulz_encode_window")
+
+
+def encode_advancing_into(d_in, chunk_size: int, word_size: int, out, out_bytes, workspace, stream=None,
+                          events=None) -> None:
+    """Enqueue gpulz_encode_advancing_search (gpulz_baseline.h): the level-0
+    stream with the upstream-style advancing-window search, same buffers as
+    encode_into."""
+    src = _u8_view(d_in)
+    ev = events if events is not None else (None, None)
+    _check(lib().gpulz_encode_advancing_search(_ptr(src), src.numel(), chunk_size, word_size, _ptr(out),
+                                               out.numel(), _ptr(out_bytes), _ptr(workspace), workspace.numel(),
+                                               _stream(stream), ev[0], ev[1]), "gpulz_encode_advancing_search")
 
 
 def encode(d_in, chunk_size: int = 2048, word_size: int = 4, match_level: int = 0, stream=None):

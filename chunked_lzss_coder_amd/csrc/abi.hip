@@ -108,7 +108,8 @@ uint64_t gpulz_decode_workspace_size(uint64_t in_bytes) { return dec_layout(dec_
 namespace {
 int encode_common(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, uint32_t word_size, uint32_t match_level,
                   uint32_t window, void* d_out, uint64_t out_capacity, uint64_t* d_out_bytes, void* d_workspace,
-                  uint64_t workspace_bytes, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+                  uint64_t workspace_bytes, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
+                  bool advancing = false) {
   if (!chunk_size_ok(chunk_size) || !word_size_ok(word_size) || match_level > 1u) return GPULZ_ERR_INVALID_ARG;
   if (window != 32u && window != 48u && window != 64u) return GPULZ_ERR_INVALID_ARG;
   if ((n_bytes > 0 && d_in == nullptr) || d_out == nullptr || d_out_bytes == nullptr || d_workspace == nullptr)
@@ -135,7 +136,8 @@ int encode_common(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, uint3
   ea.tile_flags = (uint64_t*)(ws + L.tiles);
   ea.ctl = ws + L.ctl;
   if (ev_start && hipEventRecord(ev_start, stream) != hipSuccess) return GPULZ_ERR_HIP;
-  if (launch_encode_chunks(ea, stream) != hipSuccess) return GPULZ_ERR_HIP;
+  if ((advancing ? launch_encode_advancing(ea, stream) : launch_encode_chunks(ea, stream)) != hipSuccess)
+    return GPULZ_ERR_HIP;
   if (ev_stop && hipEventRecord(ev_stop, stream) != hipSuccess) return GPULZ_ERR_HIP;
   if (launch_compact(ea, stream) != hipSuccess) return GPULZ_ERR_HIP;
   return GPULZ_OK;
@@ -150,6 +152,14 @@ int gpulz_encode_timed(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, 
                        hipEvent_t ev_stop) {
   return encode_common(d_in, n_bytes, chunk_size, word_size, match_level, kWindow, d_out, out_capacity,
                        d_out_bytes, d_workspace, workspace_bytes, stream, ev_start, ev_stop);
+}
+
+int gpulz_encode_advancing_search(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, uint32_t word_size,
+                                  void* d_out, uint64_t out_capacity, uint64_t* d_out_bytes, void* d_workspace,
+                                  uint64_t workspace_bytes, hipStream_t stream, hipEvent_t ev_start,
+                                  hipEvent_t ev_stop) {
+  return encode_common(d_in, n_bytes, chunk_size, word_size, 0u, kWindow, d_out, out_capacity, d_out_bytes,
+                       d_workspace, workspace_bytes, stream, ev_start, ev_stop, true);
 }
 
 int gpulz_encode_window(const void* d_in, uint64_t n_bytes, uint32_t chunk_size, uint32_t word_size,

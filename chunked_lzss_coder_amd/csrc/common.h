@@ -286,6 +286,7 @@ struct EncodeArgs {
 uint64_t encode_ctl_bytes();
 uint64_t encode_tiles(uint32_t num_chunks);
 hipError_t launch_encode_chunks(const EncodeArgs& a, hipStream_t stream);
+hipError_t launch_encode_advancing(const EncodeArgs& a, hipStream_t stream);
 hipError_t launch_compact(const EncodeArgs& a, hipStream_t stream);
 hipError_t launch_split_compact(const EncodeArgs& a, hipStream_t stream);
 

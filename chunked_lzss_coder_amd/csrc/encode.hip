@@ -1104,6 +1104,133 @@ __global__ __launch_bounds__(kBlock) void split_compact_kernel(
   }
 }
 
+// Upstream-style baseline search (GPULZStage page, exact longest-match search
+// paragraph: upstream advances its window pointer on every step of the
+// search and settles for shorter matches).  Read as: the pointer w walks the
+// 32 words before p, one comparison per step of x[w] against x[p + len], the
+// word the partial match started at w - len needs next; equal grows it,
+// unequal drops it and spends w; the longest partial match seen is the
+// result, the first on ties.  Everything else is the level-0 stream.  One
+// wave per chunk: each lane searches its positions, lane 0 walks the greedy
+// parse and writes the payload into LDS, the wave copies it to the chunk's
+// staging slot; compact_kernel then assembles the stream.  A baseline for
+// the page's comparison, not a tuned path.
+template <int WS, uint32_t CS>
+__global__ __launch_bounds__(64) void advancing_encode_kernel(const uint8_t* __restrict__ in, uint64_t n,
+                                                              uint32_t num_chunks, uint8_t* __restrict__ out,
+                                                              uint8_t* __restrict__ staging,
+                                                              uint64_t* __restrict__ tile_flags, uint32_t num_tiles,
+                                                              EncCtl* __restrict__ ctl) {
+  constexpr uint32_t E = CS / (uint32_t)WS;
+  constexpr uint32_t MM = min_match<WS>();
+  __shared__ uint32_t X[E];
+  __shared__ uint32_t LO[E];
+  __shared__ __attribute__((aligned(16))) uint8_t P[CS];  // a coded payload: F + D < CS bytes
+  const uint32_t c = blockIdx.x, lane = lane_id();
+  const uint64_t base = (uint64_t)c * CS;
+  const uint32_t bc = (uint32_t)((n - base) < CS ? (n - base) : CS);
+  const uint8_t* src = in + base;
+  uint32_t any = 0;
+  for (uint32_t i = lane; i < E; i += 64u) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int b = 0; b < WS; ++b) {
+      const uint32_t j = i * (uint32_t)WS + (uint32_t)b;
+      if (j < bc) w |= (uint32_t)src[j] << (8 * b);
+    }
+    X[i] = w;
+    any |= w;
+  }
+  const bool nonzero = __ballot(any != 0u) != 0ull;
+  wave_sync();
+  uint32_t F = 0, D = 0;
+  bool raw = false;
+  if (nonzero) {
+    for (uint32_t p = lane; p < E; p += 64u) {
+      uint32_t best = 0, bo = 0, len = 0;
+      for (uint32_t w = p < kWindow ? 0u : p - kWindow; w < p; ++w) {
+        if (p + len < E && X[w] == X[p + len]) {
+          ++len;
+          if (len > best) {
+            best = len;
+            bo = p - (w + 1u - len);  // the match starts at w + 1 - len
+          }
+        } else {
+          len = 0;
+        }
+      }
+      LO[p] = best | (bo << 8);
+    }
+    wave_sync();
+    uint32_t K = 0, M = 0;
+    if (lane == 0u) {  // the greedy parse, counting items and matches
+      for (uint32_t p = 0; p < E;) {
+        const uint32_t L = LO[p] & 0xFFu;
+        if (L >= MM) {
+          ++M;
+          p += L;
+        } else {
+          ++p;
+        }
+        ++K;
+      }
+    }
+    K = (uint32_t)__builtin_amdgcn_readfirstlane((int)K);
+    M = (uint32_t)__builtin_amdgcn_readfirstlane((int)M);
+    F = (K + 7u) / 8u;
+    D = (uint32_t)WS * (K - M) + 2u * M;
+    raw = F + D >= bc;
+    if (!raw) {
+      for (uint32_t i = lane; i < (F + 3u) / 4u; i += 64u) ((uint32_t*)P)[i] = 0u;
+      wave_sync();
+      if (lane == 0u) {  // the same walk, writing flags and data
+        uint8_t* d = P + F;
+        uint32_t k = 0;
+        for (uint32_t p = 0; p < E; ++k) {
+          const uint32_t v = LO[p], L = v & 0xFFu;
+          if (L >= MM) {
+            P[k >> 3] |= (uint8_t)(1u << (k & 7u));
+            d[0] = (uint8_t)L;
+            d[1] = (uint8_t)(v >> 8);
+            d += 2;
+            p += L;
+          } else {
+            const uint32_t x = X[p];
+#pragma unroll
+            for (int b = 0; b < WS; ++b) d[b] = (uint8_t)(x >> (8 * b));
+            d += WS;
+            ++p;
+          }
+        }
+      }
+      wave_sync();
+      uint32_t* slot = (uint32_t*)(staging + base);
+      for (uint32_t i = lane; i < (F + D + 3u) / 4u; i += 64u) slot[i] = ((const uint32_t*)P)[i];
+    }
+  }
+  if (lane == 0u) {
+    const uint2 ent = !nonzero ? make_uint2(0u, 0u) : (raw ? make_uint2(0u, kRawBit | bc) : make_uint2(F, D));
+    uint8_t* row = out + kHeaderBytes + kEntryBytes * (uint64_t)c;
+    if ((((uintptr_t)row) & 7u) == 0) {
+      *(uint2*)row = ent;
+    } else {
+      put_le(row, ent.x, 4);
+      put_le(row + 4, ent.y, 4);
+    }
+    // tile flag c of the assembly kernel (never more tiles than chunks), and
+    // the error flag
+    if (c < num_tiles) tile_flags[c] = 0ull;
+    if (c == 0u) ctl->error = 0u;
+  }
+}
+
+template <int WS, uint32_t CS>
+hipError_t launch_advancing(const EncodeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((advancing_encode_kernel<WS, CS>), dim3(a.num_chunks), dim3(64), 0, stream, a.in, a.n,
+                     a.num_chunks, a.out, a.staging, a.tile_flags, num_tiles_of(a.num_chunks), (EncCtl*)a.ctl);
+  return hipGetLastError();
+}
+
 template <int WS, int E, int LEVEL, int W>
 hipError_t launch_one(const EncodeArgs& a, hipStream_t stream) {
   // waves per chunk: one up to 512 elements (two chunks per workgroup), then
@@ -1151,6 +1278,22 @@ hipError_t launch_split_compact(const EncodeArgs& a, hipStream_t stream) {
                      (const uint2*)a.km, a.cs, a.ws, a.n, a.num_chunks, tiles, a.out, a.lit, a.lens, a.offs,
                      a.port_bytes, a.tile_flags, (EncCtl*)a.ctl);
   return hipGetLastError();
+}
+
+hipError_t launch_encode_advancing(const EncodeArgs& a, hipStream_t stream) {
+  if (a.num_chunks == 0) return hipSuccess;
+  switch (a.cs * 8u + a.ws) {
+    case 1024u * 8u + 1u: return launch_advancing<1, 1024>(a, stream);
+    case 1024u * 8u + 2u: return launch_advancing<2, 1024>(a, stream);
+    case 1024u * 8u + 4u: return launch_advancing<4, 1024>(a, stream);
+    case 2048u * 8u + 1u: return launch_advancing<1, 2048>(a, stream);
+    case 2048u * 8u + 2u: return launch_advancing<2, 2048>(a, stream);
+    case 2048u * 8u + 4u: return launch_advancing<4, 2048>(a, stream);
+    case 4096u * 8u + 1u: return launch_advancing<1, 4096>(a, stream);
+    case 4096u * 8u + 2u: return launch_advancing<2, 4096>(a, stream);
+    case 4096u * 8u + 4u: return launch_advancing<4, 4096>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_encode_chunks(const EncodeArgs& a, hipStream_t stream) {

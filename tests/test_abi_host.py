@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
                                          "gpulz_split_bounds", "gpulz_encode_split_workspace_size",
                                          "gpulz_encode_split", "gpulz_decode_split_workspace_size",
                                          "gpulz_decode_split", "gpulz_decode_one_thread_per_chunk",
-                                         "gpulz_lorenzo_quant", "gpulz_encode_window"])
+                                         "gpulz_lorenzo_quant", "gpulz_encode_window",
+                                         "gpulz_encode_advancing_search"])
 
 
 def test_library_exports_every_declared_symbol(g):
@@ -184,3 +185,21 @@ def test_encode_window_rejects_bad_windows(g):
         # a bad window fails before any launch (pointers never dereferenced)
         assert lib.gpulz_encode_window(p, 4096, 2048, 4, 0, window, p, 1 << 20, p, p, 1 << 30, None) \
             == g.ERR_INVALID_ARG
+
+
+def test_encode_advancing_search_rejects_bad_arguments(g):
+    lib = g.lib()
+    p = ctypes.c_void_p(0x1000)
+    big = 1 << 40
+    # fails before any launch: pointers never dereferenced
+    for cs, ws in ((3000, 4), (2048, 3), (512, 1)):
+        assert lib.gpulz_encode_advancing_search(p, 100, cs, ws, p, big, p, p, big, None, None, None) \
+            == g.ERR_INVALID_ARG
+    assert lib.gpulz_encode_advancing_search(None, 100, 2048, 4, p, big, p, p, big, None, None, None) \
+        == g.ERR_INVALID_ARG
+    need = g.max_compressed_size(100, 2048)
+    assert lib.gpulz_encode_advancing_search(p, 100, 2048, 4, p, need - 1, p, p, big, None, None, None) \
+        == g.ERR_CAPACITY
+    wsn = g.encode_workspace_size(100, 2048)
+    assert lib.gpulz_encode_advancing_search(p, 100, 2048, 4, p, need, p, p, wsn - 1, None, None, None) \
+        == g.ERR_CAPACITY
