@@ -395,6 +395,34 @@ def main(argv=None) -> int:
         mb_, ms_ = float(np.mean([ev.ms(p) for p in kb])), float(np.mean([ev.ms(p) for p in ks]))
         baseline = {"level": lv, "block_decode_kernel_ms": round(mb_, 4),
                     "one_thread_per_chunk_decode_kernel_ms": round(ms_, 4), "speedup": round(ms_ / mb_, 2)}
+    # Baseline: the upstream-style advancing-window search (level 0), its
+    # stream's ratio and its chunk kernel time beside the exact search's.
+    search_base = None
+    if not args.no_split and 0 in levels:
+        a_out = torch.empty(g.max_compressed_size(n, cs), dtype=torch.uint8, device=dev)
+        a_nb = torch.zeros(1, dtype=torch.uint64, device=dev)
+        ews = bufs[0][2]
+        ka = []
+        for i in range(args.warmup + args.steps):
+            k = ev.pair()
+            g.encode_advancing_into(x, cs, ws, a_out, a_nb, ews, events=k)
+            if i >= args.warmup:
+                ka.append(k)
+        torch.cuda.synchronize()
+        a_bytes = int(a_nb.item())
+        _, _, _, dout, dnb, st, dws = bufs[0]
+        g.decode_into(a_out, a_bytes, dout, dnb, st, dws)
+        torch.cuda.synchronize()
+        if int(st.item()) != 0 or not torch.equal(dout[:n], x):
+            print("bench.py: advancing-search stream does not round-trip", file=sys.stderr)
+            return 1
+        ma_ = float(np.mean([ev.ms(p) for p in ka]))
+        search_base = {"level": 0, "exact_search_ratio": res[0]["ratio"],
+                       "advancing_search_ratio": round(n / a_bytes, 4),
+                       "exact_search_kernel_ms": res[0]["encode_kernel_ms"],
+                       "advancing_search_kernel_ms": round(ma_, 4),
+                       "exact_kernel_speedup": round(ma_ / res[0]["encode_kernel_ms"], 2)}
+        del a_out, a_nb
     # The Lorenzo-quantizer front end on the device: the workload's float
     # field -> its u32 codes (they must equal the coder's input), kernel time
     # and the front end's roofline (4 bytes read + 4 written per cell).
@@ -534,6 +562,7 @@ def main(argv=None) -> int:
         "levels": {str(k): v for k, v in res.items()},
         "split": split,
         "decode_baseline": baseline,
+        "search_baseline": search_base,
         "lorenzo_front_end": front,
         "window_sweep": sweep,
         "roofline": roof,
