@@ -797,7 +797,8 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
 // to its place in the stream: a coded chunk's from its staging slot, a raw
 // chunk's straight from the input.  The last tile writes the header and the
 // stream length.
-__global__ __launch_bounds__(kBlock) void compact_kernel(const uint8_t* __restrict__ in,
+template <uint32_t NB>
+__global__ __launch_bounds__(NB) void compact_kernel(const uint8_t* __restrict__ in,
                                                          const uint8_t* __restrict__ staging, uint32_t cs,
                                                          uint32_t ws, uint64_t n, uint32_t num_chunks,
                                                          uint32_t num_tiles, uint8_t* __restrict__ out,
@@ -825,11 +826,11 @@ __global__ __launch_bounds__(kBlock) void compact_kernel(const uint8_t* __restri
   }
   const uint32_t t = blockIdx.x;
   const uint64_t c0 = (uint64_t)t * kCTile;
-  // Wave w moves chunks 16w .. 16w + 15 of the tile.  The first 256 bytes of
-  // each of their staging slots (one dword per lane) are loaded before any
-  // size or offset is known, so the loads overlap the row reads and the
-  // look-back (a raw chunk's slot is never read past this).
-  constexpr uint32_t PW = kCTile / kWaves;
+  // Wave w moves chunks PW w .. PW w + PW - 1 of the tile.  The first 256
+  // bytes of each of their staging slots (one dword per lane) are loaded
+  // before any size or offset is known, so the loads overlap the row reads
+  // and the look-back (a raw chunk's slot is never read past this).
+  constexpr uint32_t PW = kCTile / (NB / 64u);
   typedef uint32_t pv_t __attribute__((ext_vector_type(PW)));  // a value, never memory
   pv_t pv;
 #pragma unroll
@@ -1266,9 +1267,15 @@ uint64_t encode_ctl_bytes() { return sizeof(EncCtl); }
 uint64_t encode_tiles(uint32_t num_chunks) { return num_tiles_of(num_chunks); }
 
 hipError_t launch_compact(const EncodeArgs& a, hipStream_t stream) {
+  // Few tiles (at most two per CU): 16 waves per tile, four chunks each, so
+  // the per-chunk placement latency is spread over more waves; otherwise 8.
   const uint32_t tiles = num_tiles_of(a.num_chunks);
-  hipLaunchKernelGGL(compact_kernel, dim3(tiles ? tiles : 1u), dim3(kBlock), 0, stream, a.in, a.staging, a.cs,
-                     a.ws, a.n, a.num_chunks, tiles, a.out, a.out_bytes, a.tile_flags, (EncCtl*)a.ctl);
+  if (tiles <= 512u)
+    hipLaunchKernelGGL(compact_kernel<1024>, dim3(tiles ? tiles : 1u), dim3(1024), 0, stream, a.in, a.staging,
+                       a.cs, a.ws, a.n, a.num_chunks, tiles, a.out, a.out_bytes, a.tile_flags, (EncCtl*)a.ctl);
+  else
+    hipLaunchKernelGGL(compact_kernel<512>, dim3(tiles), dim3(512), 0, stream, a.in, a.staging, a.cs, a.ws, a.n,
+                       a.num_chunks, tiles, a.out, a.out_bytes, a.tile_flags, (EncCtl*)a.ctl);
   return hipGetLastError();
 }
 
