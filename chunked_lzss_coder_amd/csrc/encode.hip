@@ -33,6 +33,9 @@
 //   finds the tile's offset by decoupled look-back over the tiles before it
 //   and moves every payload to its place in the stream with 16-byte stores;
 //   the last tile writes the header.
+// split_compact_kernel: the same assembly into the four split-mode ports.
+// advancing_encode_kernel: the upstream-style advancing-window search, a
+//   measured baseline with the same stream rules (its own comment says how).
 #include "common.h"
 
 namespace gpulz {
@@ -115,27 +118,6 @@ __device__ uint64_t look_back(uint64_t* flags, uint32_t c, uint64_t agg, uint32_
   if (lane == 0)
     __hip_atomic_store(&flags[c], kFlagIncl | (prefix + agg), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return prefix;
-}
-
-// Copy n bytes from an LDS byte buffer (4-aligned) to global dst (any
-// alignment): aligned dwords in the middle, single bytes at the two edges.
-// `lane` runs over `nl` cooperating lanes.
-__device__ __forceinline__ void lds_to_global(uint8_t* dst, const uint8_t* src, uint32_t n, uint32_t lane,
-                                              uint32_t nl) {
-  uint32_t head = (uint32_t)((4u - ((uintptr_t)dst & 3u)) & 3u);
-  if (head > n) head = n;
-  if (lane < head) dst[lane] = src[lane];
-  const uint32_t nbody = (n - head) >> 2;
-  const uint32_t* sw = (const uint32_t*)src;
-  uint32_t* dw = (uint32_t*)(dst + head);
-  for (uint32_t j = lane; j < nbody; j += nl) {
-    const uint32_t s = head + 4u * j;
-    const uint32_t lo = sw[s >> 2];
-    const uint32_t hi = head ? sw[(s >> 2) + 1u] : 0u;
-    dw[j] = __builtin_amdgcn_alignbyte(hi, lo, head);
-  }
-  const uint32_t t0 = head + 4u * nbody;
-  if (t0 + lane < n) dst[t0 + lane] = src[t0 + lane];
 }
 
 __device__ __forceinline__ void put_le(uint8_t* p, uint64_t v, int nb) {
