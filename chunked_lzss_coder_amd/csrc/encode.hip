@@ -176,20 +176,27 @@ struct Lay {
   static constexpr uint32_t MW = W > 32 ? 2u : 1u;  // words per offset mask
   static constexpr uint32_t NW64 = E / 64;  // 64-position words
   static constexpr uint32_t NSEG = E / 8;   // 8-position parse segments
-  // Word offsets inside the per-chunk region, after X[E] (level 1 only: at
-  // level 0 the words are needed only by the offset masks, so X shares its
-  // place with S_1 and the literal words are read again from the input):
-  //   search: LV = S_1 | S_4 | S_16, each E masks followed by zero padding
-  //           that the descent may read (3, 9 and 177 masks, rounded); S_64
-  //           is not stored: its values are ANDs of four S_16 entries
-  //   level 1: LO (E) | hash table (2048)
+  // Word offsets inside the per-chunk region.  The chunk's words X are
+  // loaded at its start.  At level 0 only the offset masks read them, so S_1
+  // overwrites them and the payload's literal words are read again from the
+  // input.  Level 1 needs the words again for the candidate checks: chunks
+  // of up to 1024 elements keep X in a region of its own ahead of the rest
+  // (XW = E); larger ones (XL) overlay X as level 0 does and load the words
+  // again from the input behind the hash table after the descent, which
+  // saves 8-16 KB per chunk, a third more chunks per CU.
+  //   search: S_1 | S_4 | S_16, each E masks followed by zero padding that
+  //           the descent may read (3, 9 and 177 masks, rounded); S_64 is
+  //           not stored: its values are ANDs of four S_16 entries
+  //   level 1: LO (E) | hash table (2048) [| X again (E), XL]
   //   parse:   LO (E) | XQ (E) | ISB (E/32) | LMB (E/32) | FLG (E/32) | STG (CS/4 + 8)
   static constexpr uint32_t RP = 2u * E + 3u * (E / 32u) + CS / 4u + 8u;
   static constexpr uint32_t TOFF[3] = {0u, E + 4u, 2u * E + 16u};  // table offsets, in masks
   static constexpr uint32_t SEARCH = MW * (3u * E + 196u);
-  static constexpr uint32_t R = (cmax(cmax(SEARCH, LEVEL ? (uint32_t)E + kHashSize : 0u), RP) + 3u) & ~3u;
+  static constexpr bool XL = LEVEL == 1 && E >= 2048;                // level 1, X reloaded
+  static constexpr uint32_t XW = LEVEL == 1 && !XL ? (uint32_t)E : 0u;  // words of a separate X
+  static constexpr uint32_t R =
+      (cmax(cmax(SEARCH, LEVEL ? (XL ? 2u : 1u) * E + kHashSize : 0u), RP) + 3u) & ~3u;
   static constexpr uint32_t MISC = 2u * (E / 64u + 1u) + 8u;
-  static constexpr uint32_t XW = LEVEL ? (uint32_t)E : 0u;       // words of the X region
   static constexpr uint32_t TOTAL = (XW + R + MISC + 3u) & ~3u;  // words per chunk, 16-byte multiple
 };
 
@@ -215,7 +222,10 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
   const uint32_t g = threadIdx.x % TL;  // lane within the team
   const uint32_t lane = lane_id();
   uint32_t* X = lds_all + team * L::TOTAL;
-  uint32_t* LV = X + L::XW;  // level 0: X and S_1 share their words
+  uint32_t* LV = X + L::XW;  // X and S_1 share their words unless X has its own region
+  // level 1: the words for the candidate checks (its own region, or loaded
+  // again behind the hash table)
+  uint32_t* XL = L::XL ? LV + E + kHashSize : X;
   Mask* LVm = (Mask*)LV;  // the search tables
   uint32_t* LO = LV;
   uint32_t* XQ = LV + E;
@@ -236,6 +246,13 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
   const uint64_t base = (uint64_t)c * CS;
   const uint32_t bc = (uint32_t)((n - base) < CS ? (n - base) : CS);
   const uint8_t* src = in + base;
+  // element p of the chunk (0 past its real bytes), from the input
+  const bool fast = bc == CS && (((uintptr_t)src) & 3u) == 0;
+  auto word_at = [&](uint32_t p) -> uint32_t {
+    const uint32_t b = p * (uint32_t)WS;
+    uint32_t v = fast ? (((const uint32_t*)src)[b >> 2] >> (8u * (b & 3u))) : load4_unaligned(src + b, src + bc);
+    return WS == 4 ? v : (WS == 2 ? (v & 0xFFFFu) : (v & 0xFFu));
+  };
 
   // ---- 1. load + zero vote ---------------------------------------------------------
   uint32_t any = 0;
@@ -350,8 +367,8 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             om[q] |= (Mask)hm << 32;
           }
         }
-        // level 0: the masks overwrite X, which the whole team has read by now
-        if (LEVEL == 0) team_sync<WPC>();
+        // the masks overwrite X, which the whole team has read by now
+        if (L::XW == 0) team_sync<WPC>();
 #pragma unroll
         for (uint32_t q = 0; q < PPASS; ++q) {
           any_om |= om[q];
@@ -362,6 +379,13 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
     // No near match anywhere in the chunk: every length is 0.  At level 0 the
     // parse is then E literals, F + D = E / 8 + CS > bc, so the chunk is raw
     // and the search and parse are skipped; level 1 still runs its table.
+    // reloaded words for the candidate checks, loaded from the input now so
+    // the loads overlap the descent (stored to XL after it)
+    uint32_t xr[L::XL ? PPL : 1];
+    if constexpr (L::XL) {
+#pragma unroll
+      for (uint32_t i = 0; i < PPL; ++i) xr[i] = word_at(g + i * TL);
+    }
     bool near;
     if (WPC == 1) {
       near = __ballot(any_om != 0) != 0ull;
@@ -448,7 +472,11 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
       if (LEVEL == 1) {
         bool hit = false;
         for (uint32_t i = g; i < kHashSize; i += TL) T[i] = 0u;
-        team_sync<WPC>();  // T overlays dead table levels
+        if constexpr (L::XL) {
+#pragma unroll
+          for (uint32_t i = 0; i < PPL; ++i) XL[g + i * TL] = xr[i];
+        }
+        team_sync<WPC>();  // T (and a reloaded XL) overlay dead table levels
         constexpr uint32_t SB = E / kSubBlocks;
         static_assert(SB <= TL, "one position per lane per sub-block");
 #pragma unroll 1
@@ -465,7 +493,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
           // bucket is kept for the insert below.
           const uint32_t p = s * SB + g;
           const bool ins = g < SB && p + 1 < (uint32_t)E;
-          const uint32_t bk = ins ? bucket_of(X[p], X[p + 1]) : 0u;
+          const uint32_t bk = ins ? bucket_of(XL[p], XL[p + 1]) : 0u;
           if (g < SB) {
             uint32_t o = 0, Lnear = 0, lim = 0;
             bool need = false;
@@ -474,14 +502,14 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
               o = p - (v - 1u);  // entries come from earlier sub-blocks: o >= 1
               lim = (uint32_t)E - p < kMaxLen ? (uint32_t)E - p : kMaxLen;
               Lnear = LO[p] & 0xFFu;
-              need = v != 0u && o <= kMaxFar && Lnear < lim && X[p + Lnear] == X[p + Lnear - o];
+              need = v != 0u && o <= kMaxFar && Lnear < lim && XL[p + Lnear] == XL[p + Lnear - o];
             }
             uint32_t r = 0;
             bool open = need;
             if (open) {
               uint32_t stop = 0;
 #pragma unroll
-              for (uint32_t j = 0; j < 8u; ++j) stop |= (uint32_t)(j >= lim || X[p + j] != X[p + j - o]) << j;
+              for (uint32_t j = 0; j < 8u; ++j) stop |= (uint32_t)(j >= lim || XL[p + j] != XL[p + j - o]) << j;
               r = stop ? (uint32_t)__builtin_ctz(stop) : 8u;
               open = stop == 0u;
             }
@@ -501,7 +529,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
                 uint32_t re = 8u;  // its first 8 matched
                 for (uint32_t k0 = 8u; k0 < le; k0 += 64u) {
                   const uint32_t idx = k0 + lane;
-                  const bool stop = idx >= le || X[pe + idx] != X[pe + idx - oe];
+                  const bool stop = idx >= le || XL[pe + idx] != XL[pe + idx - oe];
                   const uint64_t sm = __ballot(stop);
                   if (sm) {
                     re = k0 + (uint32_t)__builtin_ctzll(sm);
@@ -666,21 +694,14 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
   // in the stream; the compaction kernel moves it to its final offset.
   uint32_t* STG32 = (uint32_t*)STG;
   uint32_t* slot = (uint32_t*)(staging + base);
-  // element p of the chunk (0 past its real bytes), from the input
-  const bool fast = bc == CS && (((uintptr_t)src) & 3u) == 0;
-  auto word_at = [&](uint32_t p) -> uint32_t {
-    const uint32_t b = p * (uint32_t)WS;
-    uint32_t v = fast ? (((const uint32_t*)src)[b >> 2] >> (8u * (b & 3u))) : load4_unaligned(src + b, src + bc);
-    return WS == 4 ? v : (WS == 2 ? (v & 0xFFFFu) : (v & 0xFFu));
-  };
   if (nonzero && !raw) {
-    // this lane's literal words: X at level 1, the input at level 0 (loaded
-    // here so the loads overlap the flag bitmap's construction)
+    // this lane's literal words: from X's own region, else from the input
+    // (loaded here so the loads overlap the flag bitmap's construction)
     uint32_t xv[PPL];
 #pragma unroll
     for (uint32_t i = 0; i < PPL; ++i) {
       const uint32_t p = WPC == 1 ? 64u * i + lane : g + i * TL;
-      xv[i] = LEVEL ? X[p] : word_at(p);
+      xv[i] = L::XW ? X[p] : word_at(p);
     }
     for (uint32_t i = g; i < (F + 3u) / 4u; i += TL) STG32[i] = 0u;
     team_sync<WPC>();
