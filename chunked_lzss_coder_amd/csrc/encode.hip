@@ -628,26 +628,88 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             M += (uint32_t)__builtin_popcountll(isw[i] & lmw[i]);
           }
         } else {
-          if (g < 64u) {
-            // the first wave hops word by word: the exits of 64 positions in one
-            // VGPR (the next word's load in flight), one readlane per hop
-            uint64_t* IS64w = (uint64_t*)ISB;
-            uint32_t P = 0;
-            uint32_t xq_next = XQ[lane];
+          if constexpr (WPC < 4) {
+            // two waves: the first wave hops word by word (the other's chunk
+            // work is done; other workgroups keep the CU busy meanwhile): the
+            // exits of 64 positions in one VGPR (the next word's load in
+            // flight), one readlane per hop
+            if (g < 64u) {
+              uint64_t* IS64w = (uint64_t*)ISB;
+              uint32_t P = 0;
+              uint32_t xq_next = XQ[lane];
 #pragma unroll 1
-            for (uint32_t i = 0; i < NR; ++i) {
-              const uint32_t xqr = xq_next;
-              if (i + 1u < NR) xq_next = XQ[64u * (i + 1u) + lane];
-              uint64_t acc = 0;
-              while (P < 64u * (i + 1u)) {
-                const uint32_t xq = __builtin_amdgcn_readlane(xqr, P & 63u);
-                acc |= (uint64_t)(xq >> 16) << (P & 56u);
-                P = xq & 0xFFFFu;
+              for (uint32_t i = 0; i < NR; ++i) {
+                const uint32_t xqr = xq_next;
+                if (i + 1u < NR) xq_next = XQ[64u * (i + 1u) + lane];
+                uint64_t acc = 0;
+                while (P < 64u * (i + 1u)) {
+                  const uint32_t xq = __builtin_amdgcn_readlane(xqr, P & 63u);
+                  acc |= (uint64_t)(xq >> 16) << (P & 56u);
+                  P = xq & 0xFFFFu;
+                }
+                if (lane == 0u) IS64w[i] = acc;
               }
-              if (lane == 0u) IS64w[i] = acc;
             }
+            team_sync<WPC>();
+          } else {
+            // four or more waves (a serial walk would leave all but one of them
+            // idle for E / 8 hops): two levels of hops.  First, for every
+            // position p, where the parse leaves p's 64-position word if it
+            // enters the word at p (at most 8 segment hops: a segment's exit
+            // lies past its end), all positions at once.  Then the first wave
+            // follows the real parse one word at a time (at most NR hops, one
+            // readlane each) and lane w rebuilds word w's item-start bits from
+            // its real entry (at most 8 hops).  WX, a u16 per position, uses
+            // space that is free here: the staging area (word sizes 2 and 4)
+            // or the dead search tables past the parse region (word size 1).
+            static_assert(NR <= 64u, "one lane per 64-position word");
+            static_assert(WS >= 2 || L::RP + E / 2u <= L::R, "word exits fit past the parse region");
+            uint16_t* WX = (uint16_t*)(WS >= 2 ? (uint32_t*)STG : LV + L::RP);
+            {
+              uint32_t P[PPL];
+#pragma unroll
+              for (uint32_t i = 0; i < PPL; ++i) P[i] = g + i * TL;
+#pragma unroll
+              for (uint32_t h = 0; h < 8u; ++h) {
+#pragma unroll
+                for (uint32_t i = 0; i < PPL; ++i) {
+                  const uint32_t wend = ((g + i * TL) | 63u) + 1u;
+                  if (P[i] < wend) P[i] = XQ[P[i]] & 0xFFFFu;
+                }
+              }
+#pragma unroll
+              for (uint32_t i = 0; i < PPL; ++i) WX[g + i * TL] = (uint16_t)P[i];
+            }
+            team_sync<WPC>();
+            if (g < 64u) {
+              uint32_t P = 0, ent = 0xFFFFu;  // lane w: the parse's entry into word w
+              uint32_t wx_next = WX[lane];
+#pragma unroll 1
+              for (uint32_t w = 0; w < NR; ++w) {
+                const uint32_t wx = wx_next;
+                if (w + 1u < NR) wx_next = WX[64u * (w + 1u) + lane];
+                if (P < 64u * (w + 1u)) {  // else a match spans the whole word
+                  if (lane == w) ent = P;
+                  P = (uint32_t)__builtin_amdgcn_readlane((int)wx, (int)(P & 63u));
+                }
+              }
+              uint64_t acc = 0;
+              if (lane < NR && ent != 0xFFFFu) {
+                const uint32_t wend = 64u * (lane + 1u);
+                uint32_t Q = ent;
+#pragma unroll
+                for (uint32_t h = 0; h < 8u; ++h) {
+                  if (Q < wend) {
+                    const uint32_t xq = XQ[Q];
+                    acc |= (uint64_t)(xq >> 16) << (Q & 56u);
+                    Q = xq & 0xFFFFu;
+                  }
+                }
+              }
+              if (lane < NR) ((uint64_t*)ISB)[lane] = acc;
+            }
+            team_sync<WPC>();
           }
-          team_sync<WPC>();
           // ---- 6. counts (first wave) --------------------------------------------------------
           const uint64_t* IS64 = (const uint64_t*)ISB;
           const uint64_t* LM64 = (const uint64_t*)LMB;
