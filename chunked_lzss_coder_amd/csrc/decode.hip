@@ -37,7 +37,7 @@ constexpr uint32_t kScanPer = 4;         // chunks per thread per scan round
 constexpr uint32_t kScanRound = kScanPer * kBlock;
 constexpr uint32_t kDecodeGrid = 8192;   // chunk-kernel workgroups at most
 constexpr uint32_t kMaxTilesAlloc = 4096; // split mode: stride of the three tile-total arrays
-constexpr uint32_t kOneWaveMinChunks = 32768; // overlaid chunks: one per wave from this many chunks on
+constexpr uint32_t kOneWaveMinChunks = 2048;  // overlaid chunks: one per wave from this many chunks on
 static_assert(kTileMin % kScanRound == 0 && (uint64_t)kTileMax * 4096u <= (1ull << 32), "tile sizes");
 
 __device__ __forceinline__ uint32_t ld_u32_bytes(const uint8_t* p) {
