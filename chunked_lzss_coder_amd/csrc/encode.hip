@@ -185,13 +185,19 @@ struct Lay {
   // again from the input behind the hash table after the descent, which
   // saves 8-16 KB per chunk, a third more chunks per CU.
   //   search: S_1 | S_4 | S_16, each E masks followed by zero padding that
-  //           the descent may read (3, 9 and 177 masks, rounded); S_64 is
+  //           the descent may read (3, 9 and 177 or 33 masks, rounded); S_64 is
   //           not stored: its values are ANDs of four S_16 entries
   //   level 1: LO (E) | hash table (2048) [| X again (E), XL]
   //   parse:   LO (E) | XQ (E) | ISB (E/32) | LMB (E/32) | FLG (E/32) | STG (CS/4 + 8)
   static constexpr uint32_t RP = 2u * E + 3u * (E / 32u) + CS / 4u + 8u;
   static constexpr uint32_t TOFF[3] = {0u, E + 4u, 2u * E + 16u};  // table offsets, in masks
-  static constexpr uint32_t SEARCH = MW * (3u * E + 196u);
+  // Chunks of up to 512 elements guard the descent's first-round reads with
+  // the chunk's end, so S_16 needs 33 padding masks instead of 177 (a 7 %
+  // smaller chunk, one more workgroup per CU); larger chunks are bound by the
+  // parse region and skip the guards.
+  static constexpr bool GUARD64 = E <= 512;
+  static constexpr uint32_t PAD = GUARD64 ? 52u : 196u;  // padding words of S_1, S_4, S_16 (4, 12, rest)
+  static constexpr uint32_t SEARCH = MW * (3u * E + PAD);
   static constexpr bool XL = LEVEL == 1 && E >= 2048;                // level 1, X reloaded
   static constexpr uint32_t XW = LEVEL == 1 && !XL ? (uint32_t)E : 0u;  // words of a separate X
   static constexpr uint32_t R =
@@ -403,7 +409,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
         // bounds checks.  S_64[p] = S_16[p] & S_16[p+16] & S_16[p+32] &
         // S_16[p+48] is read that way in the first round instead of being
         // stored: one table less in LDS, so more chunks per CU.
-        for (uint32_t i = g; i < 196u; i += TL) {  // padding word i of level lv is at (lv + 1) E + i
+        for (uint32_t i = g; i < L::PAD; i += TL) {  // padding word i of level lv is at (lv + 1) E + i
           const uint32_t lv = i < 4u ? 0u : (i < 16u ? 1u : 2u);
           LVm[(lv + 1u) * (uint32_t)E + i] = 0;
         }
@@ -431,11 +437,16 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
           // round, so L <= 3 * (64 + 16 + 4 + 1) = 255, the length cap
           {
             // round of k = 64 (Ln = 0): S_64 at p, p + 64, p + 128 from S_16,
-            // reads up to p + 176, inside S_16's padding
+            // reads up to p + 176, inside S_16's padding (or guarded)
             const Mask* S = LVm + L::TOFF[2] + p;
-            const Mask s0 = S[0] & S[16] & S[32] & S[48];
-            const Mask s1 = S[64] & S[80] & S[96] & S[112];
-            const Mask s2 = S[128] & S[144] & S[160] & S[176];
+            Mask s0 = 0, s1 = 0, s2 = 0;  // S_64 at p, p + 64, p + 128 (0 past the chunk)
+            if (!L::GUARD64 || p + 64u <= (uint32_t)E) {
+              s0 = S[0] & S[16] & S[32] & S[48];
+              if (!L::GUARD64 || p + 128u <= (uint32_t)E) {
+                s1 = S[64] & S[80] & S[96] & S[112];
+                if (!L::GUARD64 || p + 192u <= (uint32_t)E) s2 = S[128] & S[144] & S[160] & S[176];
+              }
+            }
             const Mask t1 = surv & s0, t2 = t1 & s1, t3 = t2 & s2;
             const uint32_t n = (uint32_t)(t1 != 0) + (uint32_t)(t2 != 0) + (uint32_t)(t3 != 0);
             surv = t3 ? t3 : (t2 ? t2 : (t1 ? t1 : surv));
