@@ -251,6 +251,48 @@ __device__ __forceinline__ void copy_bytes16_r1(uint8_t* dst, const uint8_t* src
   if (t < n) dst[t] = src[t];
 }
 
+// copy_bytes16 with two blocks per lane per round.
+__device__ __forceinline__ void copy_bytes16_r2(uint8_t* dst, const uint8_t* src, uint32_t n, uint32_t l) {
+  const uint32_t h0 = (uint32_t)((16u - ((uintptr_t)dst & 15u)) & 15u);
+  const uint32_t h = h0 < n ? h0 : n;
+  if (l < h) dst[l] = src[l];
+  const uint32_t nb = (n - h) >> 4;
+  const uintptr_t s = (uintptr_t)(src + h);
+  const uint32_t sh = (uint32_t)(s & 15u);
+  const uint32_t ns = nb + (sh ? 1u : 0u);
+  const uint4* sb = (const uint4*)(s - sh);
+  uint4* db = (uint4*)(dst + h);
+  const uint32_t q = sh >> 2, r = sh & 3u;
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  auto next_of = [&](uint4 a, uint4 nx) {
+    uint4 b;
+    b.x = dpp0<kWaveShl1>(a.x);
+    b.y = dpp0<kWaveShl1>(a.y);
+    b.z = dpp0<kWaveShl1>(a.z);
+    b.w = dpp0<kWaveShl1>(a.w);
+    return l == 63u ? nx : b;
+  };
+  auto lane0 = [&](uint4 a) {
+    return make_uint4((uint32_t)__builtin_amdgcn_readlane((int)a.x, 0), (uint32_t)__builtin_amdgcn_readlane((int)a.y, 0),
+                      (uint32_t)__builtin_amdgcn_readlane((int)a.z, 0), (uint32_t)__builtin_amdgcn_readlane((int)a.w, 0));
+  };
+  auto put = [&](uint32_t k, uint4 a, uint4 b) {
+    if (k < nb) db[k] = sh ? funnel16(a, b, q, r) : a;
+  };
+#pragma unroll 1
+  for (uint32_t k0 = 0; k0 < nb; k0 += 128u) {
+    const uint32_t k = k0 + l;
+    const uint4 a0 = k < ns ? sb[k] : z;
+    const uint4 a1 = k + 64u < ns ? sb[k + 64u] : z;
+    const uint32_t kx = k0 + 128u;  // first block of the next round
+    const uint4 x = (l == 63u && sh && kx < ns) ? sb[kx] : z;
+    put(k, a0, next_of(a0, lane0(a1)));
+    put(k + 64u, a1, next_of(a1, x));
+  }
+  const uint32_t t = h + 16u * nb + l;  // fewer than 16 tail bytes
+  if (t < n) dst[t] = src[t];
+}
+
 // Zero n bytes at dst (any alignment) with one wave (this is lane l).
 __device__ __forceinline__ void zero_bytes16(uint8_t* dst, uint32_t n, uint32_t l) {
   const uint32_t h0 = (uint32_t)((16u - ((uintptr_t)dst & 15u)) & 15u);

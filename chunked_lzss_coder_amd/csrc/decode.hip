@@ -714,6 +714,7 @@ __device__ __forceinline__ void decode_group_teams(const DecP& p, const uint8_t*
       const uint32_t w0 = (g >> 6) * share;
       const uint32_t len = w0 < bc ? (bc - w0 < share ? bc - w0 : share) : 0u;
       if (e.y == 0u) zero_bytes16(dst + w0, len, lane);
+      else if constexpr (G::OVL) copy_bytes16_r2(dst + w0, pay + w0, len, lane);
       else copy_bytes16_r1(dst + w0, pay + w0, len, lane);
     } else {
       if (!decode_coded<CS, WS, false, TEAMS>(pay, lim, e.x, e.y, bc, dst, arena, sh, SplitSrc{}) && g == 0)
