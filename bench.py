@@ -162,6 +162,26 @@ def cpu_baseline(w, level, gpu_stream_bytes: bytes):
     }, identical
 
 
+def oracle_identical(w, level, gpu_stream_bytes: bytes, limit: int = 64 << 20):
+    """Oracle leg: is the GPU stream the oracle's, byte for byte?  The whole
+    stream when the workload is at most `limit` bytes; else the first whole
+    chunks worth about `limit` bytes (chunks are coded independently and
+    their payloads packed in order, so their size-table rows and payloads are
+    a prefix of the table and of the payload region).  Returns (flag, scope)."""
+    import oracle
+    oracle.build()
+    n, cs = w.n, w.chunk_size
+    take = n if n <= limit else (limit // cs) * cs
+    ref = oracle.encode(w.data[:take], cs, w.word_size, level).tobytes()
+    if take == n:
+        return ref == gpu_stream_bytes, "whole stream"
+    ns, nc = take // cs, -(-n // cs)
+    tab, pay = ref[32:32 + 8 * ns], ref[32 + 8 * ns:]
+    p0 = 32 + 8 * nc
+    same = gpu_stream_bytes[32:32 + 8 * ns] == tab and gpu_stream_bytes[p0:p0 + len(pay)] == pay
+    return same, f"size-table rows and payloads of the first {ns} chunks"
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -577,8 +597,13 @@ def main(argv=None) -> int:
         out = bufs[lv0][0]
         gpu_stream = out[:stream_bytes[lv0]].cpu().numpy().tobytes()
         cpu, identical = cpu_baseline(w, lv0, gpu_stream)
-        r0["byte_identical"] = identical
-        log(f"cpu oracle: {cpu['value']} GB/s encode ({cpu['encode_s']} s), byte_identical={identical}")
+        log(f"cpu oracle: {cpu['value']} GB/s encode ({cpu['encode_s']} s)")
+        for lv in levels:
+            out = bufs[lv][0]
+            flag, scope = oracle_identical(w, lv, out[:stream_bytes[lv]].cpu().numpy().tobytes())
+            res[lv]["byte_identical"] = bool(flag)
+            res[lv]["byte_identical_scope"] = scope
+            log(f"level {lv}: byte_identical={flag} ({scope})")
 
     ms_per_step = wall * 1e3 / max(args.steps, 1)
     line = {
