@@ -254,7 +254,7 @@ def test_many_one_wave_chunks(g, oracle_mod):
     """A stream of 33,000 chunks of 4096 bytes at word size 4 (enough that
     each chunk is decoded by one wave, its payload staged over its decoded
     bytes): the oracle's stream decodes to the input, and corrupting one
-    coded chunk's match token gives the oracle's verdict."""
+    coded chunk's match token gives the oracle's status."""
     from chunked_lzss_coder_amd import synth
     cs, ws = 4096, 4
     n = 33000 * cs - 1000  # ragged tail
