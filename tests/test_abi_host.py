@@ -203,3 +203,14 @@ def test_encode_advancing_search_rejects_bad_arguments(g):
     wsn = g.encode_workspace_size(100, 2048)
     assert lib.gpulz_encode_advancing_search(p, 100, 2048, 4, p, need, p, p, wsn - 1, None, None, None) \
         == g.ERR_CAPACITY
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    # no CPU fallback: without the built library every entry point raises
+    import chunked_lzss_coder_amd as gl
+    monkeypatch.setattr(gl, "_lib", None)
+    monkeypatch.setattr(gl, "LIB_PATH", gl.LIB_PATH + ".absent")
+    with pytest.raises(gl.GpulzError):
+        gl.lib()
+    with pytest.raises(gl.GpulzError):
+        gl.max_compressed_size(100, 2048)
