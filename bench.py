@@ -574,9 +574,14 @@ def main(argv=None) -> int:
 
     lv0 = levels[0]
     r0 = res[lv0]
+    E = cs // ws
     roof = {
         "bound": "hbm",
-        "kernel": "encode_chunks_kernel (level %d)" % lv0,
+        # the template instance as the kernel trace names it (word, elements, level,
+        # window, waves per chunk, chunks per workgroup)
+        "kernel": "encode_kernel<%d, %d, %d, 32, %d, %d>" % (ws, E, lv0, 1 if E <= 512 else E // 512,
+                                                           2 if E <= 512 else 1),
+        "decode_kernel": "chunks_kernel",
         "achieved": r0["encode_kernel_hbm_gbps"],
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
