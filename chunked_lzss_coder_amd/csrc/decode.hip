@@ -35,7 +35,8 @@ constexpr uint32_t kTileMax = 1u << 20;  // at most (offsets within a tile < 2^3
 constexpr uint32_t kMaxTiles = 64;       // tiles wanted (one tile total per lane)
 constexpr uint32_t kScanPer = 4;         // chunks per thread per scan round
 constexpr uint32_t kScanRound = kScanPer * kBlock;
-constexpr uint32_t kDecodeGrid = 8192;   // chunk-kernel workgroups at most
+constexpr uint32_t kDecodeGrid = 8192;   // chunk-kernel workgroups at most (chunks shared by waves)
+constexpr uint32_t kDecodeGridTeams = 16384;  // the same for chunks decoded by a whole workgroup
 constexpr uint32_t kMaxTilesAlloc = 4096; // split mode: stride of the three tile-total arrays
 constexpr uint32_t kOneWaveMinChunks = 2048;  // overlaid chunks: one per wave from this many chunks on
 static_assert(kTileMin % kScanRound == 0 && (uint64_t)kTileMax * 4096u <= (1ull << 32), "tile sizes");
@@ -662,7 +663,14 @@ __device__ __forceinline__ void decode_group_teams(const DecP& p, const uint8_t*
   // readlane: one load latency per 64 chunks, not one per chunk.  A payload
   // offset is its tile's offset (the earlier tiles' totals: lane t of `pre`
   // for streams of up to 64 tiles) plus its offset within the tile.
-  const uint64_t stride = (uint64_t)gridDim.x * CPW;
+  // Chunks decoded a workgroup each use the whole grid (up to one chunk per
+  // workgroup, so one chunk's serial phases overlap other workgroups', not
+  // wait in line); chunks shared by waves use at most kDecodeGrid workgroups
+  // (each wave then covers enough chunks to use its metadata batches), the
+  // rest of the grid leaves at once.
+  const uint32_t grid = (CPW > 1u && gridDim.x > kDecodeGrid) ? kDecodeGrid : gridDim.x;
+  if (blockIdx.x >= grid) return;
+  const uint64_t stride = (uint64_t)grid * CPW;
   const uint64_t c0 = (uint64_t)blockIdx.x * CPW + team;
   const uint32_t lane = lane_id();
   uint64_t pre = 0;
@@ -1151,7 +1159,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     // times over, not one per group (their launch would cost more than the
     // work for zero and raw chunks)
     uint32_t grid = (a.chunks_cap + kWaves - 1u) / kWaves;
-    if (grid > kDecodeGrid) grid = kDecodeGrid;
+    if (grid > kDecodeGridTeams) grid = kDecodeGridTeams;
     hipLaunchKernelGGL(chunks_kernel, dim3(grid), dim3(kBlock), 0, stream, a.in, a.in_bytes, a.out,
                        (const DecP*)a.params, (const uint32_t*)a.loc, (const uint64_t*)a.tile_sums,
                        (const uint32_t*)a.tile_err, a.status, a.out_bytes);

@@ -759,7 +759,6 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
   const uint32_t F = (K + 7u) / 8u;
   const uint32_t D = (uint32_t)WS * (K - M) + 2u * M;
   const bool raw = nonzero && F + D >= bc;
-  const uint32_t size = !nonzero ? 0u : (raw ? bc : F + D);
 
   // ---- 7. size-table row, payload into the chunk's staging slot --------------------
   // Flags first (bit k of the bitmap = item k is a match), then the data bytes
