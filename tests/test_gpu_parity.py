@@ -28,7 +28,7 @@ def g():
 
 
 def to_dev(a: np.ndarray):
-    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+    return torch.from_numpy(np.array(a, copy=True)).to("cuda:0")  # a writable, contiguous copy
 
 
 def gpu_encode(g, data: np.ndarray, cs: int, ws: int, level: int) -> np.ndarray:
