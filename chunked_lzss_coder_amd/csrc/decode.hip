@@ -41,6 +41,16 @@ constexpr uint32_t kMaxTilesAlloc = 4096; // split mode: stride of the three til
 constexpr uint32_t kOneWaveMinChunks = 2048;  // overlaid chunks: one per wave from this many chunks on
 static_assert(kTileMin % kScanRound == 0 && (uint64_t)kTileMax * 4096u <= (1ull << 32), "tile sizes");
 
+// Chunks per scan tile for a stream of nc chunks: about nc / kMaxTiles,
+// a whole number of scan rounds, within [kTileMin, kTileMax].
+__host__ __device__ inline uint32_t scan_tile_chunks(uint64_t nc) {
+  uint64_t T = (nc + kMaxTiles - 1u) / kMaxTiles;
+  T = (T + kTileMin - 1u) / kTileMin * kTileMin;
+  if (T < kTileMin) T = kTileMin;
+  if (T > kTileMax) T = kTileMax;
+  return (uint32_t)T;
+}
+
 __device__ __forceinline__ uint32_t ld_u32_bytes(const uint8_t* p) {
   return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
 }
@@ -81,7 +91,7 @@ struct DecP {
 };
 
 __global__ __launch_bounds__(kBlock) void scan_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes,
-                                                      uint64_t out_capacity, uint32_t chunks_cap, uint32_t T,
+                                                      uint64_t out_capacity, uint32_t chunks_cap,
                                                       DecP* __restrict__ P, uint32_t* __restrict__ loc,
                                                       uint64_t* __restrict__ tile_sum,
                                                       uint32_t* __restrict__ tile_err, uint32_t* __restrict__ status,
@@ -101,6 +111,9 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(const uint8_t* __restrict_
     else if (n > out_capacity) st = kStatusCapacity;
     else if (nc > chunks_cap) st = kStatusCorrupt;
   }
+  // Tiles are sized for the stream's own chunk count (the host only knows
+  // a bound): nc <= chunks_cap, so at most the launched workgroups are needed.
+  const uint32_t T = scan_tile_chunks(nc);
   const uint32_t ntiles = (nc + T - 1u) / T;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     P->n = n;
@@ -1104,16 +1117,19 @@ __global__ __launch_bounds__(kBlock) void serial_chunks_kernel(const uint8_t* __
 
 }  // namespace
 
-uint32_t decode_tile_chunks(uint32_t chunks_cap) {
-  uint64_t T = ((uint64_t)chunks_cap + kMaxTiles - 1u) / kMaxTiles;
-  T = (T + kTileMin - 1u) / kTileMin * kTileMin;
-  if (T < kTileMin) T = kTileMin;
-  if (T > kTileMax) T = kTileMax;
-  return (uint32_t)T;
-}
+uint32_t decode_tile_chunks(uint32_t chunks_cap) { return scan_tile_chunks(chunks_cap); }
 uint32_t decode_num_tiles(uint32_t chunks_cap) {
   const uint32_t T = decode_tile_chunks(chunks_cap);
   return chunks_cap ? (uint32_t)(((uint64_t)chunks_cap + T - 1u) / T) : 1u;
+}
+// Scan workgroups for any stream of at most chunks_cap chunks: its tiles are
+// kTileMax chunks each (then chunks_cap's tiles are too, and as many or more),
+// or there are at most kMaxTiles of them and at most one per kTileMin chunks.
+uint32_t decode_scan_groups(uint32_t chunks_cap) {
+  const uint32_t by_min = (uint32_t)(((uint64_t)chunks_cap + kTileMin - 1u) / kTileMin);
+  const uint32_t small = by_min < kMaxTiles ? by_min : kMaxTiles;
+  const uint32_t nt = decode_num_tiles(chunks_cap);
+  return nt > small ? nt : (small ? small : 1u);
 }
 uint64_t decode_params_bytes() { return sizeof(DecP); }
 
@@ -1132,10 +1148,9 @@ hipError_t launch_decode_split(const SplitDecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_decode_serial(const DecodeArgs& a, hipStream_t stream) {
-  const uint32_t T = decode_tile_chunks(a.chunks_cap);
-  const uint32_t tiles = decode_num_tiles(a.chunks_cap);
+  const uint32_t tiles = decode_scan_groups(a.chunks_cap);
   hipLaunchKernelGGL(scan_kernel, dim3(tiles), dim3(kBlock), 0, stream, a.in, a.in_bytes, a.out_capacity,
-                     a.chunks_cap, T, (DecP*)a.params, a.loc, a.tile_sums, a.tile_err, a.status, a.out_bytes);
+                     a.chunks_cap, (DecP*)a.params, a.loc, a.tile_sums, a.tile_err, a.status, a.out_bytes);
   if (a.ev_start && hipEventRecord(a.ev_start, stream) != hipSuccess) return hipErrorUnknown;
   if (a.chunks_cap > 0) {
     uint32_t grid = (a.chunks_cap + kBlock - 1u) / kBlock;
@@ -1149,10 +1164,9 @@ hipError_t launch_decode_serial(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  const uint32_t T = decode_tile_chunks(a.chunks_cap);
-  const uint32_t tiles = decode_num_tiles(a.chunks_cap);
+  const uint32_t tiles = decode_scan_groups(a.chunks_cap);
   hipLaunchKernelGGL(scan_kernel, dim3(tiles), dim3(kBlock), 0, stream, a.in, a.in_bytes, a.out_capacity,
-                     a.chunks_cap, T, (DecP*)a.params, a.loc, a.tile_sums, a.tile_err, a.status, a.out_bytes);
+                     a.chunks_cap, (DecP*)a.params, a.loc, a.tile_sums, a.tile_err, a.status, a.out_bytes);
   if (a.ev_start && hipEventRecord(a.ev_start, stream) != hipSuccess) return hipErrorUnknown;
   if (a.chunks_cap > 0) {
     // workgroups loop over chunk groups: enough of them to fill every CU a few
