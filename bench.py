@@ -10,11 +10,16 @@ GB/s of uncompressed input (whole gpulz_encode call); decode GB/s and the
 compression ratio of every level sit beside it.  ``roofline`` reports the
 dominant kernel (the chunk encode kernel) against the HBM peak, with its
 duration taken from HIP events recorded around that kernel alone, and
-``cpu_baseline`` the CPU oracle (single thread) on the same bytes.
+``cpu_baseline`` the CPU oracle (one pinned core, and all cores) on the
+same bytes.
 
 Default workload: 2D Lorenzo residual codes of a 1800x3600 field
 (25,920,000 bytes of uint32 words), chunk_size 2048, word_size 4, levels 0
-and 1.  ``--workload 4 --levels 0`` runs the 2 GiB stress stream at level 0.
+and 1.  ``stress_level0`` adds the largest level-0 run beside it: the 2 GiB
+stress stream (chunk 4096, word 4) with per-call and per-kernel encode and
+decode times and their fractions of the HBM peak (``--no-stress-row`` skips
+it).  ``--workload 4 --levels 0`` makes the stress stream the main workload.
+Every stream is compared whole with the oracle's in the CPU-baseline leg.
 """
 from __future__ import annotations
 
@@ -100,86 +105,182 @@ def measured_traffic(cs: int, ws: int, level: int, workload: str):
     return None
 
 
-def cpu_baseline(w, level, gpu_stream_bytes: bytes):
-    """Oracle leg: time the single-threaded CPU oracle on the same bytes and
-    check the GPU stream against its stream."""
+def host_cpu() -> dict:
+    """The host's CPU model and counts, as the CPU-baseline leg reports them."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
+
+
+def cpu_baseline(w, levels):
+    """Oracle leg: the plain single-threaded C oracle on the workload's bytes,
+    timed on one pinned host core (whole encodes repeated for a few seconds
+    per level), and the same oracle calls over contiguous whole-chunk ranges on
+    all usable cores (at most 16, the host share of one GPU)."""
     import numpy as np
 
     import oracle
     oracle.build()
-    n = w.n
+    n, cs, ws = w.n, w.chunk_size, w.word_size
     # bounded sample: the whole workload if it is small, else a prefix of
-    # whole chunks worth about 64 MiB (the oracle is chunk-independent)
+    # whole chunks worth about 64 MiB (chunks are coded independently)
     limit = 64 << 20
-    take = n if n <= limit else (limit // w.chunk_size) * w.chunk_size
+    take = n if n <= limit else (limit // cs) * cs
     sample = w.data[:take]
-    # repeat whole encodes of the sample until about 10 s of CPU work (at
-    # most 30 s), so the rate is not dominated by one short measurement
-    passes, t_enc = 0, 0.0
-    while passes == 0 or (t_enc < 10.0 and t_enc * (passes + 1) / passes < 30.0):
-        t0 = time.perf_counter()
-        ref = oracle.encode(sample, w.chunk_size, w.word_size, level)
-        t_enc += time.perf_counter() - t0
-        passes += 1
-    t0 = time.perf_counter()
-    back = oracle.decode(ref)
-    t_dec = time.perf_counter() - t0
-    ok_rt = bool(np.array_equal(back, sample))
-    # all cores: the same oracle call over contiguous whole-chunk ranges, one
-    # thread each (the C call releases the interpreter lock); at most 16
-    # threads, the host share of one GPU
-    from concurrent.futures import ThreadPoolExecutor
-    threads = max(1, min(16, os.cpu_count() or 1))
-    nch = -(-take // w.chunk_size)
-    per = -(-nch // threads)
-    parts = [sample[i * per * w.chunk_size:min(take, (i + 1) * per * w.chunk_size)] for i in range(threads)]
-    parts = [q for q in parts if q.size]
-    mt_passes, t_mt = 0, 0.0
-    with ThreadPoolExecutor(max_workers=len(parts)) as ex:
-        while mt_passes == 0 or (t_mt < 5.0 and mt_passes < 200):
+    cpu = host_cpu()
+    try:
+        allowed = sorted(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = []
+    threads = max(1, min(16, cpu["usable_cpus"]))
+    per_level = {}
+    for level in levels:
+        # single thread, pinned to one core for the timed passes
+        pinned = None
+        if allowed:
+            pinned = allowed[-1]
+            os.sched_setaffinity(0, {pinned})
+        try:
+            times = []
+            while len(times) < 3 or (sum(times) < 6.0 and len(times) < 200):
+                t0 = time.perf_counter()
+                ref = oracle.encode(sample, cs, ws, level)
+                times.append(time.perf_counter() - t0)
             t0 = time.perf_counter()
-            list(ex.map(lambda q: oracle.encode(q, w.chunk_size, w.word_size, level), parts))
-            t_mt += time.perf_counter() - t0
-            mt_passes += 1
-    identical = None
-    if take == n:
-        identical = bool(ref.tobytes() == gpu_stream_bytes)
+            back = oracle.decode(ref)
+            t_dec = time.perf_counter() - t0
+        finally:
+            if allowed:
+                os.sched_setaffinity(0, set(allowed))
+        ok_rt = bool(np.array_equal(back, sample))
+        # all cores: the same oracle calls over contiguous whole-chunk ranges
+        mt = []
+        while len(mt) < 3 or (sum(mt) < 3.0 and len(mt) < 200):
+            t0 = time.perf_counter()
+            oracle.encode_parallel(sample, cs, ws, level, threads=threads)
+            mt.append(time.perf_counter() - t0)
+        med, mmed = float(np.median(times)), float(np.median(mt))
+        per_level[level] = {
+            "encode_gbps": round(take / med / 1e9, 6),
+            "encode_gbps_mean": round(take * len(times) / sum(times) / 1e9, 6),
+            "decode_gbps": round(take / t_dec / 1e9, 6),
+            "passes": len(times), "encode_s": round(sum(times), 3), "pinned_cpu": pinned,
+            "round_trip": ok_rt,
+            "all_cores": {"encode_gbps": round(take / mmed / 1e9, 6), "threads": threads, "passes": len(mt)},
+        }
+    l0 = per_level[levels[0]]
     return {
-        "value": round(take * passes / t_enc / 1e9, 6),
+        "value": l0["encode_gbps"],
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"level-{level} encode of {'the whole workload' if take == n else 'the first %d bytes' % take}"
-                   f" ({take} bytes), {passes} passes, single-threaded C oracle"),
-        "decode_gbps": round(take / t_dec / 1e9, 6),
-        "encode_s": round(t_enc, 3),
-        "passes": passes,
-        "decode_s": round(t_dec, 3),
-        "round_trip": ok_rt,
-        "all_cores": {"value": round(take * mt_passes / t_mt / 1e9, 6), "unit": "GB/s", "cores": len(parts),
-                      "passes": mt_passes, "encode_s": round(t_mt, 3),
-                      "sample": "the same bytes split into contiguous whole-chunk ranges, one oracle call per thread"},
-    }, identical
+        "sample": (f"level-{levels[0]} encode of {'the whole workload' if take == n else 'the first %d bytes' % take}"
+                   f" ({take} bytes), median of {l0['passes']} whole passes, single-threaded C oracle pinned to"
+                   f" one core; all_cores: the same calls over contiguous whole-chunk ranges on {threads} threads"),
+        "host_cpu": cpu,
+        "all_cores": {"value": l0["all_cores"]["encode_gbps"], "unit": "GB/s", "cores": threads},
+        "levels": {str(k): v for k, v in per_level.items()},
+    }
 
 
-def oracle_identical(w, level, gpu_stream_bytes: bytes, limit: int = 64 << 20):
-    """Oracle leg: is the GPU stream the oracle's, byte for byte?  The whole
-    stream when the workload is at most `limit` bytes; else the first whole
-    chunks worth about `limit` bytes (chunks are coded independently and
-    their payloads packed in order, so their size-table rows and payloads are
-    a prefix of the table and of the payload region).  Returns (flag, scope)."""
+def oracle_identical(w, level, gpu_stream):
+    """Oracle leg: is the whole GPU stream (a host uint8 array) the oracle's,
+    byte for byte?  The oracle's stream is built by the single-threaded oracle
+    run on contiguous whole-chunk ranges across the host's cores (chunks are
+    coded independently).  Returns (flag, scope)."""
+    import numpy as np
+
     import oracle
     oracle.build()
-    n, cs = w.n, w.chunk_size
-    take = n if n <= limit else (limit // cs) * cs
-    ref = oracle.encode(w.data[:take], cs, w.word_size, level).tobytes()
-    if take == n:
-        return ref == gpu_stream_bytes, "whole stream"
-    ns, nc = take // cs, -(-n // cs)
-    tab, pay = ref[32:32 + 8 * ns], ref[32 + 8 * ns:]
-    p0 = 32 + 8 * nc
-    same = gpu_stream_bytes[32:32 + 8 * ns] == tab and gpu_stream_bytes[p0:p0 + len(pay)] == pay
-    return same, f"size-table rows and payloads of the first {ns} chunks"
+    ref = oracle.encode_parallel(w.data, w.chunk_size, w.word_size, level)
+    return bool(ref.size == gpu_stream.size and np.array_equal(ref, gpu_stream)), "whole stream"
+
+
+def stress_level0_row(g, ev, dev, steps: int, warmup: int):
+    """The 2 GiB stress stream (chunk 4096, word 4) at level 0, the largest
+    level-0 run: per-call and per-kernel encode and decode times, their
+    fractions of the HBM peak, the ratio and the round trip.  Returns the row,
+    the workload and a host copy of the GPU stream (for the oracle check)."""
+    import numpy as np
+    import torch
+
+    import workloads
+    t0 = time.perf_counter()
+    w = workloads.workload(4)
+    log(f"stress row: {w.name}, {w.n} bytes, generated in {time.perf_counter() - t0:.1f}s")
+    cs, ws, n = w.chunk_size, w.word_size, w.n
+    x = torch.from_numpy(w.data).to(dev)
+    cap = g.max_compressed_size(n, cs)
+    out = torch.empty(cap, dtype=torch.uint8, device=dev)
+    nb = torch.zeros(1, dtype=torch.uint64, device=dev)
+    ews = torch.empty(g.encode_workspace_size(n, cs), dtype=torch.uint8, device=dev)
+    dout = torch.empty(n, dtype=torch.uint8, device=dev)
+    dnb = torch.zeros(1, dtype=torch.uint64, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    dws = torch.empty(g.decode_workspace_size(cap), dtype=torch.uint8, device=dev)
+    g.encode_into(x, cs, ws, 0, out, nb, ews)
+    torch.cuda.synchronize()
+    sb = int(nb.item())
+    g.decode_into(out, sb, dout, dnb, st, dws)
+    torch.cuda.synchronize()
+    if sb < 32 or int(st.item()) != 0 or int(dnb.item()) != n or not torch.equal(dout, x):
+        raise RuntimeError("stress row: level-0 round trip failed")
+    hs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    calls = []
+    for i in range(warmup + steps):
+        ce, cd = ev.pair(), ev.pair()
+        ev.hip.hipEventRecord(ce[0], hs)
+        g.encode_into(x, cs, ws, 0, out, nb, ews)
+        ev.hip.hipEventRecord(ce[1], hs)
+        ev.hip.hipEventRecord(cd[0], hs)
+        g.decode_into(out, sb, dout, dnb, st, dws)
+        ev.hip.hipEventRecord(cd[1], hs)
+        if i >= warmup:
+            calls.append((ce, cd))
+    kern = []
+    for _ in range(steps):
+        ke, kd = ev.pair(), ev.pair()
+        g.encode_into(x, cs, ws, 0, out, nb, ews, events=ke)
+        g.decode_into(out, sb, dout, dnb, st, dws, events=kd)
+        kern.append((ke, kd))
+    torch.cuda.synchronize()
+    if int(nb.item()) != sb or int(st.item()) != 0 or not torch.equal(dout, x):
+        raise RuntimeError("stress row: repeated calls differ")
+    me = float(np.mean([ev.ms(c[0]) for c in calls]))
+    md = float(np.mean([ev.ms(c[1]) for c in calls]))
+    mke = float(np.mean([ev.ms(k[0]) for k in kern]))
+    mkd = float(np.mean([ev.ms(k[1]) for k in kern]))
+    algo = n + (sb - 32)  # input + size-table rows + payloads (decode: the same, read and write swapped)
+
+    def frac(ms):
+        return round(algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 5)
+    row = {
+        "workload": w.name, "bytes": n, "chunk_size": cs, "word_size": ws, "level": 0,
+        "ratio": round(n / sb, 4), "stream_bytes": sb, "algorithmic_bytes": algo,
+        "encode_ms": round(me, 4), "encode_gbps": round(n / (me * 1e-3) / 1e9, 3),
+        "encode_kernel_ms": round(mke, 4), "encode_assembly_ms": round(me - mke, 4),
+        "decode_ms": round(md, 4), "decode_gbps": round(n / (md * 1e-3) / 1e9, 3),
+        "decode_kernel_ms": round(mkd, 4),
+        "encode_frac_per_call": frac(me), "encode_frac_kernel": frac(mke),
+        "decode_frac_per_call": frac(md), "decode_frac_kernel": frac(mkd),
+        "encode_kernel_traffic": measured_traffic(cs, ws, 0, w.name),
+        "round_trip": True, "steps": steps, "warmup": warmup,
+    }
+    host_stream = out[:sb].cpu().numpy()
+    del x, out, nb, ews, dout, dnb, st, dws
+    torch.cuda.empty_cache()
+    return row, w, host_stream
 
 
 def main(argv=None) -> int:
@@ -193,6 +294,8 @@ def main(argv=None) -> int:
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (the HBM-counter reference)")
     ap.add_argument("--no-split", action="store_true", help="skip the split-mode (four ports) measurement")
+    ap.add_argument("--no-stress-row", action="store_true",
+                    help="skip the level-0 row of the 2 GiB stress stream beside the headline workload")
     ap.add_argument("--flush-reps", type=int, default=11,
                     help="repetitions of the flushed-cache and host-latency measurements (0: skip)")
     args = ap.parse_args(argv)
@@ -206,7 +309,7 @@ def main(argv=None) -> int:
     import torch
 
     import chunked_lzss_coder_amd as g
-    from chunked_lzss_coder_amd import synth
+    import workloads as synth
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -484,8 +587,9 @@ def main(argv=None) -> int:
                        "exact_kernel_speedup": round(ma_ / res[0]["encode_kernel_ms"], 2)}
         del a_out, a_nb
     # The Lorenzo-quantizer front end on the device: the workload's float
-    # field -> its u32 codes (they must equal the coder's input), kernel time
-    # and the front end's roofline (4 bytes read + 4 written per cell).
+    # field -> its u32 codes, kernel time and the front end's roofline (4 bytes
+    # read + 4 written per cell).  Its codes are checked against the oracle's
+    # by the GPU tests, not here.
     front = None
     fld = synth.field_of(args.workload)
     if fld is not None and not args.no_split:
@@ -504,18 +608,14 @@ def main(argv=None) -> int:
             if i >= args.warmup:
                 ts_.append(e_)
         torch.cuda.synchronize()
-        match = bool(torch.equal(codes.reshape(-1).view(torch.uint8), x))
         mq = float(np.mean([ev.ms(p_) for p_ in ts_]))
         cells = f32.size
         hbm = 8.0 * cells / (mq * 1e-3) / 1e9
         front = {"field": "x".join(str(d_) for d_ in f32.shape) + " float32", "abs_error_bound": eb,
                  "ms": round(mq, 4), "field_gbps": round(4.0 * cells / (mq * 1e-3) / 1e9, 3),
-                 "codes_equal_coder_input": match, "clamped": int(clamped.item()),
+                 "clamped": int(clamped.item()),
                  "roofline": {"bound": "hbm", "achieved": round(hbm, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                               "frac": round(hbm / HBM_PEAK_GBPS, 5)}}
-        if not match:
-            print("bench.py: device Lorenzo codes differ from the coder input", file=sys.stderr)
-            return 1
         del d_f, codes, clamped
     # Near-window and chunk-size sweep (the pages' ratio trade): ratio and
     # encode kernel time for windows 32 / 48 / 64, both levels, chunk sizes
@@ -546,7 +646,6 @@ def main(argv=None) -> int:
                     sweep.append({"chunk_size": cs_, "level": lv, "window": win, "ratio": round(n / sb_, 4),
                                   "encode_ms": round(me_, 4), "encode_gbps": round(n / (me_ * 1e-3) / 1e9, 3)})
             del o_, nb_, w_
-    ev.close()
     if args.calibration_copy_mib > 0:
         a_ = torch.empty(args.calibration_copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
         b_ = torch.empty_like(a_)
@@ -597,18 +696,33 @@ def main(argv=None) -> int:
         "decode_frac_input_only": round(w.n / (r0["decode_kernel_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 5),
     }
 
+    # The largest level-0 run beside the headline workload: the 2 GiB stress
+    # stream (its inputs do not fit the 256 MB last-level cache).
+    stress = None
+    stress_w = stress_stream = None
+    if not args.no_stress_row and args.workload != 4:
+        stress, stress_w, stress_stream = stress_level0_row(g, ev, dev, max(3, min(args.steps, 10)),
+                                                            max(1, min(args.warmup, 3)))
+        log(f"stress row: encode {stress['encode_ms']} ms/call ({stress['encode_kernel_ms']} kernel), "
+            f"decode {stress['decode_ms']} ms/call ({stress['decode_kernel_ms']} kernel)")
+    ev.close()
+
     cpu = None
     if not args.no_cpu_baseline:
-        out = bufs[lv0][0]
-        gpu_stream = out[:stream_bytes[lv0]].cpu().numpy().tobytes()
-        cpu, identical = cpu_baseline(w, lv0, gpu_stream)
-        log(f"cpu oracle: {cpu['value']} GB/s encode ({cpu['encode_s']} s)")
+        cpu = cpu_baseline(w, levels)
+        log(f"cpu oracle: {cpu['value']} GB/s encode, single pinned core ({cpu['host_cpu']})")
         for lv in levels:
             out = bufs[lv][0]
-            flag, scope = oracle_identical(w, lv, out[:stream_bytes[lv]].cpu().numpy().tobytes())
+            flag, scope = oracle_identical(w, lv, out[:stream_bytes[lv]].cpu().numpy())
             res[lv]["byte_identical"] = bool(flag)
             res[lv]["byte_identical_scope"] = scope
             log(f"level {lv}: byte_identical={flag} ({scope})")
+        if stress is not None:
+            flag, scope = oracle_identical(stress_w, 0, stress_stream)
+            stress["byte_identical"] = flag
+            stress["byte_identical_scope"] = scope
+            log(f"stress row: byte_identical={flag} ({scope})")
+    del stress_w, stress_stream
 
     ms_per_step = wall * 1e3 / max(args.steps, 1)
     line = {
@@ -636,6 +750,7 @@ def main(argv=None) -> int:
         "lorenzo_front_end": front,
         "window_sweep": sweep,
         "roofline": roof,
+        "stress_level0": stress,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

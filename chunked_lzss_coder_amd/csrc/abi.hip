@@ -8,6 +8,7 @@
 #include "gpulz_window.h"
 
 #include "common.h"
+#include "scan_tiles.h"
 
 using namespace gpulz;
 
@@ -45,11 +46,9 @@ DecLayoutHost dec_layout(uint64_t chunks_cap) {
   L.params = 0;
   L.loc = round_up(decode_params_bytes());
   L.tile_sums = L.loc + round_up((chunks_cap ? chunks_cap : 1) * 4u);
-  // the launch uses at most this many tiles for any chunk bound up to
-  // chunks_cap: at most 64 while tiles grow, then one per 2^20 chunks
-  const uint32_t cap32 = chunks_cap > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)chunks_cap;
-  const uint32_t nt = decode_num_tiles(cap32);
-  const uint64_t tiles = nt > 256u ? nt : 256u;
+  // a stream of at most chunks_cap chunks has at most this many scan tiles
+  // (scan_tiles.h); the launch clamps the bound to 2^32 - 1 chunks
+  const uint64_t tiles = workspace_tiles(chunks_cap > 0xFFFFFFFFull ? 0xFFFFFFFFull : chunks_cap);
   L.tile_err = L.tile_sums + round_up(tiles * 8u);
   L.total = L.tile_err + round_up(tiles * 4u) + kAlign;
   return L;
@@ -337,8 +336,10 @@ int gpulz_decode_split(const void* d_lit, uint64_t lit_bytes, const void* d_lens
   return GPULZ_OK;
 }
 
-int gpulz_stream_info(const void* h_prefix, uint64_t bytes, uint64_t* original_size, uint64_t* stream_bytes,
-                      uint32_t* chunk_size, uint32_t* word_size) {
+namespace {
+// Fields of a 32-byte header in host memory; kind = version byte wanted.
+int header_fields(const void* h_prefix, uint64_t bytes, uint32_t version, uint64_t* n_out, uint64_t* last_out,
+                  uint32_t* nc_out, uint32_t* cs_out, uint32_t* ws_out) {
   if (h_prefix == nullptr || bytes < kHeaderBytes) return GPULZ_ERR_CORRUPT;
   const uint8_t* s = (const uint8_t*)h_prefix;
   auto u32 = [&](int o) {
@@ -346,10 +347,41 @@ int gpulz_stream_info(const void* h_prefix, uint64_t bytes, uint64_t* original_s
   };
   auto u64 = [&](int o) { return (uint64_t)u32(o) | ((uint64_t)u32(o + 4) << 32); };
   const uint32_t ws = s[5], cs = u32(8), nc = u32(12);
-  const uint64_t n = u64(16), pb = u64(24);
-  if (u32(0) != kMagic || s[4] != kVersion || s[6] != 0 || s[7] != 0) return GPULZ_ERR_CORRUPT;
+  const uint64_t n = u64(16);
+  if (u32(0) != kMagic || s[4] != version || s[6] != 0 || s[7] != 0) return GPULZ_ERR_CORRUPT;
   if (!word_size_ok(ws) || !chunk_size_ok(cs)) return GPULZ_ERR_CORRUPT;
-  if (num_chunks_of(n, cs) != nc || pb > n) return GPULZ_ERR_CORRUPT;
+  if (num_chunks_of(n, cs) != nc) return GPULZ_ERR_CORRUPT;
+  *n_out = n;
+  *last_out = u64(24);
+  *nc_out = nc;
+  *cs_out = cs;
+  *ws_out = ws;
+  return GPULZ_OK;
+}
+}  // namespace
+
+int gpulz_split_info(const void* h_prefix, uint64_t bytes, uint64_t* original_size, uint64_t* meta_bytes,
+                     uint32_t* chunk_size, uint32_t* word_size) {
+  uint64_t n, nflag;
+  uint32_t nc, cs, ws;
+  const int rc = header_fields(h_prefix, bytes, kSplitVersion, &n, &nflag, &nc, &cs, &ws);
+  if (rc != GPULZ_OK) return rc;
+  // at most one flag byte per 8 items, at most chunk_size / word_size items per chunk
+  if (nflag > (uint64_t)nc * ((cs / ws + 7u) / 8u)) return GPULZ_ERR_CORRUPT;
+  if (original_size) *original_size = n;
+  if (meta_bytes) *meta_bytes = (uint64_t)kHeaderBytes + (uint64_t)kEntryBytes * nc + nflag;
+  if (chunk_size) *chunk_size = cs;
+  if (word_size) *word_size = ws;
+  return GPULZ_OK;
+}
+
+int gpulz_stream_info(const void* h_prefix, uint64_t bytes, uint64_t* original_size, uint64_t* stream_bytes,
+                      uint32_t* chunk_size, uint32_t* word_size) {
+  uint64_t n, pb;
+  uint32_t nc, cs, ws;
+  const int rc = header_fields(h_prefix, bytes, kVersion, &n, &pb, &nc, &cs, &ws);
+  if (rc != GPULZ_OK) return rc;
+  if (pb > n) return GPULZ_ERR_CORRUPT;
   if (original_size) *original_size = n;
   if (stream_bytes) *stream_bytes = (uint64_t)kHeaderBytes + (uint64_t)kEntryBytes * nc + pb;
   if (chunk_size) *chunk_size = cs;

@@ -26,8 +26,6 @@ constexpr uint32_t kHashSize = 1u << kHashBits;
 // ---- launch geometry ----------------------------------------------------
 constexpr int kBlock = 256;           // threads per workgroup (4 wave64)
 constexpr int kWaves = kBlock / 64;
-constexpr uint32_t kTile = 1024;      // chunks per size-scan tile
-constexpr uint32_t kMaxGrid = 1u << 20;
 
 // Status codes mirrored from the public header.
 constexpr uint32_t kStatusOk = 0u;
@@ -341,7 +339,7 @@ struct DecodeArgs {
   uint32_t* status;
   void* params;         // device-resident stream parameters
   uint32_t* loc;        // chunks_cap payload offsets within their scan tile
-  uint64_t* tile_sums;  // one per scan tile (decode_num_tiles)
+  uint64_t* tile_sums;  // one per scan tile (workspace_tiles slots)
   uint32_t* tile_err;   // one per scan tile
   uint32_t chunks_cap;  // host bound on num_chunks
   hipEvent_t ev_start;  // optional, recorded around the chunk decode kernel

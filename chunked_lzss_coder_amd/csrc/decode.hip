@@ -4,7 +4,8 @@
 // host (the GPULZStage page's own inverse reads the header with blocking
 // copies before it can launch; this one can be captured).
 //
-// scan_kernel (<= 256 workgroups, one per tile of T chunks): checks the
+// scan_kernel (one workgroup per tile of T chunks, T sized on the device from
+//   the header's chunk count; scan_tiles.h states the bounds): checks the
 //   header, writes the parameters, the initial status and length; validates
 //   every size-table row against its chunk's real bytes, writes each chunk's
 //   payload offset within its tile, the tile's total and an error flag.
@@ -26,13 +27,11 @@
 //   Errors only ever raise the status (and zero the length), so the kernel
 //   order makes the first write of the status the header kernel's.
 #include "common.h"
+#include "scan_tiles.h"
 
 namespace gpulz {
 namespace {
 
-constexpr uint32_t kTileMin = 1024;     // chunks per scan tile: at least,
-constexpr uint32_t kTileMax = 1u << 20;  // at most (offsets within a tile < 2^32)
-constexpr uint32_t kMaxTiles = 64;       // tiles wanted (one tile total per lane)
 constexpr uint32_t kScanPer = 4;         // chunks per thread per scan round
 constexpr uint32_t kScanRound = kScanPer * kBlock;
 constexpr uint32_t kDecodeGrid = 8192;   // chunk-kernel workgroups at most (chunks shared by waves)
@@ -40,16 +39,6 @@ constexpr uint32_t kDecodeGridTeams = 16384;  // the same for chunks decoded by 
 constexpr uint32_t kMaxTilesAlloc = 4096; // split mode: stride of the three tile-total arrays
 constexpr uint32_t kOneWaveMinChunks = 2048;  // overlaid chunks: one per wave from this many chunks on
 static_assert(kTileMin % kScanRound == 0 && (uint64_t)kTileMax * 4096u <= (1ull << 32), "tile sizes");
-
-// Chunks per scan tile for a stream of nc chunks: about nc / kMaxTiles,
-// a whole number of scan rounds, within [kTileMin, kTileMax].
-__host__ __device__ inline uint32_t scan_tile_chunks(uint64_t nc) {
-  uint64_t T = (nc + kMaxTiles - 1u) / kMaxTiles;
-  T = (T + kTileMin - 1u) / kTileMin * kTileMin;
-  if (T < kTileMin) T = kTileMin;
-  if (T > kTileMax) T = kTileMax;
-  return (uint32_t)T;
-}
 
 __device__ __forceinline__ uint32_t ld_u32_bytes(const uint8_t* p) {
   return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
@@ -1118,19 +1107,7 @@ __global__ __launch_bounds__(kBlock) void serial_chunks_kernel(const uint8_t* __
 }  // namespace
 
 uint32_t decode_tile_chunks(uint32_t chunks_cap) { return scan_tile_chunks(chunks_cap); }
-uint32_t decode_num_tiles(uint32_t chunks_cap) {
-  const uint32_t T = decode_tile_chunks(chunks_cap);
-  return chunks_cap ? (uint32_t)(((uint64_t)chunks_cap + T - 1u) / T) : 1u;
-}
-// Scan workgroups for any stream of at most chunks_cap chunks: its tiles are
-// kTileMax chunks each (then chunks_cap's tiles are too, and as many or more),
-// or there are at most kMaxTiles of them and at most one per kTileMin chunks.
-uint32_t decode_scan_groups(uint32_t chunks_cap) {
-  const uint32_t by_min = (uint32_t)(((uint64_t)chunks_cap + kTileMin - 1u) / kTileMin);
-  const uint32_t small = by_min < kMaxTiles ? by_min : kMaxTiles;
-  const uint32_t nt = decode_num_tiles(chunks_cap);
-  return nt > small ? nt : (small ? small : 1u);
-}
+uint32_t decode_num_tiles(uint32_t chunks_cap) { return chunks_cap ? scan_tiles(chunks_cap) : 1u; }
 uint64_t decode_params_bytes() { return sizeof(DecP); }
 
 hipError_t launch_decode_split(const SplitDecodeArgs& a, hipStream_t stream) {
@@ -1148,7 +1125,7 @@ hipError_t launch_decode_split(const SplitDecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_decode_serial(const DecodeArgs& a, hipStream_t stream) {
-  const uint32_t tiles = decode_scan_groups(a.chunks_cap);
+  const uint32_t tiles = scan_groups(a.chunks_cap);
   hipLaunchKernelGGL(scan_kernel, dim3(tiles), dim3(kBlock), 0, stream, a.in, a.in_bytes, a.out_capacity,
                      a.chunks_cap, (DecP*)a.params, a.loc, a.tile_sums, a.tile_err, a.status, a.out_bytes);
   if (a.ev_start && hipEventRecord(a.ev_start, stream) != hipSuccess) return hipErrorUnknown;
@@ -1164,7 +1141,7 @@ hipError_t launch_decode_serial(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  const uint32_t tiles = decode_scan_groups(a.chunks_cap);
+  const uint32_t tiles = scan_groups(a.chunks_cap);
   hipLaunchKernelGGL(scan_kernel, dim3(tiles), dim3(kBlock), 0, stream, a.in, a.in_bytes, a.out_capacity,
                      a.chunks_cap, (DecP*)a.params, a.loc, a.tile_sums, a.tile_err, a.status, a.out_bytes);
   if (a.ev_start && hipEventRecord(a.ev_start, stream) != hipSuccess) return hipErrorUnknown;

@@ -91,7 +91,10 @@ GPULZ_API uint64_t gpulz_decode_workspace_size(uint64_t in_bytes);
  *     else GPULZ_ERR_CAPACITY and nothing is enqueued.  Bytes of d_out past
  *     the stream's length are left untouched.
  *   d_out_bytes: device u64 that receives the stream length once the stream
- *     reaches the end of this call's work.
+ *     reaches the end of this call's work.  0 means the call failed on the
+ *     device (the assembly's bounded wait for an earlier tile's offset gave
+ *     up; never expected): the contents of d_out are then undefined.  A
+ *     valid stream is at least 32 bytes long.
  *   d_workspace / workspace_bytes: at least gpulz_encode_workspace_size();
  *     any alignment; its contents on entry do not matter and are clobbered.
  * Output bytes do not depend on workspace contents, stream, or run. */

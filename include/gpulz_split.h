@@ -73,6 +73,15 @@ GPULZ_API int gpulz_decode_split(const void* d_lit, uint64_t lit_bytes, const vo
                                  uint64_t out_capacity, uint64_t* d_out_bytes, uint32_t* d_status, void* d_workspace,
                                  uint64_t workspace_bytes, hipStream_t stream);
 
+/* Host-side read of a meta port's header (no device access): from the first
+ * `bytes` (>= 32) bytes of a meta port in host memory, return its original
+ * size, the meta port's length (header, rows and flag bytes), chunk_size and
+ * word_size.  GPULZ_ERR_CORRUPT if they are not a valid split-mode header
+ * (magic, version 2, reserved bytes, supported sizes, chunk count matching
+ * the original size); any output pointer may be NULL. */
+GPULZ_API int gpulz_split_info(const void* h_prefix, uint64_t bytes, uint64_t* original_size,
+                               uint64_t* meta_bytes, uint32_t* chunk_size, uint32_t* word_size);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,6 +20,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gpulz_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# A separately built copy (the sanitizer test builds one with ASan/UBSan) may
+# be named here; it is loaded instead of liboracle.so and never rebuilt.
+_LIB_OVERRIDE = os.environ.get("GPULZ_ORACLE_LIB")
 _lib = None
 
 OK, EINVAL, ECAP, ECORRUPT = 0, -1, -2, -3
@@ -45,9 +48,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
-        build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
     u8p = ctypes.c_void_p
     lib.oracle_max_stream_size.argtypes = [ctypes.c_uint64, ctypes.c_uint32]
     lib.oracle_max_stream_size.restype = ctypes.c_uint64
@@ -278,3 +284,84 @@ def lorenzo_quant(field, eb: float) -> tuple[np.ndarray, int]:
     codes = np.empty(f.shape, dtype=np.uint32)
     clamped = _load().oracle_lorenzo_quant(_ptr(f), dims[2], dims[1], dims[0], float(eb), _ptr(codes))
     return codes, int(clamped)
+
+
+# ---- whole streams on several host threads -----------------------------------
+# Chunks are coded independently (GPULZStage page, introduction: every chunk is
+# compressed on its own), so the oracle run over contiguous whole-chunk ranges
+# of the input, one call per range, yields the size-table rows and payloads of
+# exactly those chunks; concatenated in range order they are the rows and
+# payloads of the whole buffer.  Only the header's whole-buffer fields (chunk
+# count, original size, payload or flag-byte total) are rewritten.  The
+# per-range calls are the plain single-threaded oracle; the C calls release
+# the interpreter lock, so the ranges run side by side.
+
+def _ranges(n: int, chunk_size: int, parts: int) -> list[tuple[int, int]]:
+    nch = -(-n // chunk_size)
+    parts = max(1, min(parts, nch))
+    per = -(-nch // parts)
+    out = []
+    for i in range(parts):
+        c0, c1 = i * per, min(nch, (i + 1) * per)
+        if c0 < c1:
+            out.append((c0 * chunk_size, min(n, c1 * chunk_size)))
+    return out
+
+
+def _map_ranges(fn, a: np.ndarray, chunk_size: int, threads: int):
+    from concurrent.futures import ThreadPoolExecutor
+    rngs = _ranges(a.size, chunk_size, threads)
+    with ThreadPoolExecutor(max_workers=max(1, len(rngs))) as ex:
+        return list(ex.map(lambda r: fn(a[r[0]:r[1]]), rngs)), rngs
+
+
+def encode_parallel(data, chunk_size: int, word_size: int, level: int, threads: int | None = None,
+                    window: int = 32) -> np.ndarray:
+    """The stream encode() returns, built from the oracle run on `threads`
+    contiguous whole-chunk ranges at once (default: the host's CPUs, at most
+    16)."""
+    a = _bytes(data)
+    threads = threads or max(1, min(16, os.cpu_count() or 1))
+    if a.size <= chunk_size or threads == 1:
+        return encode(a, chunk_size, word_size, level, window)
+    parts, rngs = _map_ranges(lambda q: encode(q, chunk_size, word_size, level, window), a, chunk_size, threads)
+    nch = -(-a.size // chunk_size)
+    tables, pays = [], []
+    for (lo, hi), s in zip(rngs, parts):
+        k = -(-(hi - lo) // chunk_size)
+        tables.append(s[HEADER_BYTES:HEADER_BYTES + ENTRY_BYTES * k])
+        pays.append(s[HEADER_BYTES + ENTRY_BYTES * k:])
+    payload = sum(int(p.size) for p in pays)
+    head = parts[0][:HEADER_BYTES].copy()
+    head[12:16] = np.frombuffer(np.uint32(nch).astype("<u4").tobytes(), dtype=np.uint8)
+    head[16:24] = np.frombuffer(np.uint64(a.size).astype("<u8").tobytes(), dtype=np.uint8)
+    head[24:32] = np.frombuffer(np.uint64(payload).astype("<u8").tobytes(), dtype=np.uint8)
+    return np.concatenate([head, *tables, *pays])
+
+
+def encode_split_parallel(data, chunk_size: int, word_size: int, level: int, threads: int | None = None):
+    """The four ports encode_split() returns, built from the oracle run on
+    `threads` contiguous whole-chunk ranges at once.  Ports concatenate in
+    range order; meta = header | every range's rows | every range's flag
+    bytes, with the header's chunk count, size and flag-byte total rewritten."""
+    a = _bytes(data)
+    threads = threads or max(1, min(16, os.cpu_count() or 1))
+    if a.size <= chunk_size or threads == 1:
+        return encode_split(a, chunk_size, word_size, level)
+    parts, rngs = _map_ranges(lambda q: encode_split(q, chunk_size, word_size, level), a, chunk_size, threads)
+    nch = -(-a.size // chunk_size)
+    rows, flags = [], []
+    for (lo, hi), (_, _, _, m) in zip(rngs, parts):
+        k = -(-(hi - lo) // chunk_size)
+        rows.append(m[HEADER_BYTES:HEADER_BYTES + ENTRY_BYTES * k])
+        flags.append(m[HEADER_BYTES + ENTRY_BYTES * k:])
+    nflag = sum(int(f.size) for f in flags)
+    head = parts[0][3][:HEADER_BYTES].copy()
+    head[12:16] = np.frombuffer(np.uint32(nch).astype("<u4").tobytes(), dtype=np.uint8)
+    head[16:24] = np.frombuffer(np.uint64(a.size).astype("<u8").tobytes(), dtype=np.uint8)
+    head[24:32] = np.frombuffer(np.uint64(nflag).astype("<u8").tobytes(), dtype=np.uint8)
+    lit = np.concatenate([p[0] for p in parts])
+    lens = np.concatenate([p[1] for p in parts])
+    offs = np.concatenate([p[2] for p in parts])
+    meta = np.concatenate([head, *rows, *flags])
+    return lit, lens, offs, meta

@@ -37,7 +37,7 @@ def test_header_declares_the_entry_points():
                                          "gpulz_encode_split", "gpulz_decode_split_workspace_size",
                                          "gpulz_decode_split", "gpulz_decode_one_thread_per_chunk",
                                          "gpulz_lorenzo_quant", "gpulz_encode_window",
-                                         "gpulz_encode_advancing_search"])
+                                         "gpulz_encode_advancing_search", "gpulz_split_info"])
 
 
 def test_library_exports_every_declared_symbol(g):
@@ -77,6 +77,29 @@ def test_stream_info_matches_oracle_streams(g, oracle_mod):
         bad = s[:32].copy()
         bad[0] ^= 1
         assert g.stream_info(bad.tobytes()) is None
+
+
+def test_split_info_matches_oracle_meta(g, oracle_mod):
+    rng = np.random.default_rng(1)
+    for cs, ws, n in [(2048, 4, 5000), (1024, 1, 0), (4096, 2, 9000), (2048, 4, 40 * 2048)]:
+        a = rng.integers(0, 4, size=n, dtype=np.uint8)
+        meta = oracle_mod.encode_split(a, cs, ws, 1)[3]
+        assert g.split_info(meta[:32].tobytes()) == (n, meta.size, cs, ws)
+        assert g.split_info(meta[:31].tobytes()) is None
+        # a one-stream header is not a meta port, and vice versa
+        s = oracle_mod.encode(a, cs, ws, 0)
+        assert g.split_info(s[:32].tobytes()) is None
+        assert g.stream_info(meta[:32].tobytes()) is None
+        for i, v in ((0, 1), (6, 1), (12, 1)):
+            bad = meta[:32].copy()
+            bad[i] ^= v
+            assert g.split_info(bad.tobytes()) is None, i
+        # more flag bytes than the chunks can hold
+        bad = meta[:32].copy()
+        nc = -(-n // cs)
+        too_many = nc * ((cs // ws + 7) // 8) + 1
+        bad[24:32] = np.frombuffer(np.uint64(too_many).astype("<u8").tobytes(), dtype=np.uint8)
+        assert g.split_info(bad.tobytes()) is None
 
 
 def _call_encode(g, ptr_in, n, cs, ws, level, ptr_out, cap, ptr_nb, ptr_ws, wsb):

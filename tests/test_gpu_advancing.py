@@ -96,7 +96,7 @@ def test_constant_run_hand_stream(g, oracle_mod):
 
 
 def test_workload_1800x3600(g, oracle_mod):
-    from chunked_lzss_coder_amd import synth
+    import workloads as synth
     w = synth.workload(1)
     data = np.ascontiguousarray(w.data)
     out, nb = gpu_encode_adv(g, data, w.chunk_size, w.word_size)

@@ -55,7 +55,7 @@ def test_serial_decode_matches(g, oracle_mod, cs, ws):
 
 
 def test_serial_decode_workload(g, oracle_mod):
-    from chunked_lzss_coder_amd import synth
+    import workloads as synth
     w = synth.workload(1)
     s = oracle_mod.encode(w.data, w.chunk_size, w.word_size, 0).tobytes()
     st, nb, out = serial_decode(g, s, w.n)

@@ -73,7 +73,7 @@ def test_constant_and_zero_patches(g, oracle_mod):
 
 @pytest.mark.parametrize("shape", [(1800, 3600), (100, 256, 256)])
 def test_full_size_fields(g, oracle_mod, shape):
-    from chunked_lzss_coder_amd import synth
+    import workloads as synth
     rng = np.random.default_rng(11)
     f = synth._sinusoid_field(rng, shape).astype(np.float32)
     f[synth._zero_patches(rng, shape, 0.3)] = 0.0
@@ -83,7 +83,7 @@ def test_full_size_fields(g, oracle_mod, shape):
 
 def test_quantizer_feeds_the_coder(g, oracle_mod):
     # device codes -> device encode must equal oracle codes -> oracle encode
-    from chunked_lzss_coder_amd import synth
+    import workloads as synth
     rng = np.random.default_rng(12)
     f = synth._sinusoid_field(rng, (300, 700)).astype(np.float32)
     eb = 1e-4 * float(f.max() - f.min())

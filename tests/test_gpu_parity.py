@@ -3,7 +3,8 @@
 Streams must be byte-identical to the oracle's and every decode bit-exact.
 Covers the hand-worked streams, all (chunk_size, word_size, level) pairs on
 ragged inputs, the five workloads (full size for the field workloads and the
-byte mix; sampled chunks plus a full round trip for the 2 GiB stress stream),
+byte mix; the 2 GiB stress stream whole, against the oracle run on chunk
+ranges across the host's cores),
 corrupted streams, capacity errors, unaligned buffers, poisoned workspace.
 """
 from __future__ import annotations
@@ -90,7 +91,7 @@ def test_random_ragged_inputs(g, oracle_mod, cs, ws, level):
 
 @pytest.fixture(scope="module")
 def workloads():
-    from chunked_lzss_coder_amd import synth
+    import workloads as synth
     cache = {}
 
     def get(idx):
@@ -113,33 +114,26 @@ def test_workload_full_stream(g, oracle_mod, workloads, idx, level):
 
 
 @pytest.mark.parametrize("level", [1, 0])
-def test_stress_2gib_sampled(g, oracle_mod, workloads, level):
-    """2 GiB stress stream at its full size: every size-table entry of a sample
-    of chunks and its payload bytes equal the oracle's; the table is
-    consistent; the GPU decode reproduces all 2 GiB."""
+def test_stress_2gib_whole_stream(g, oracle_mod, workloads, level):
+    """2 GiB stress stream at its full size: the whole GPU stream (header,
+    every size-table row, every payload byte) equals the oracle's, which is
+    built from the single-threaded oracle run on contiguous whole-chunk ranges
+    across the host's cores; the GPU decode reproduces all 2 GiB."""
     w = workloads(4)
     cs, ws = w.chunk_size, w.word_size
+    print(f"stress 2 GiB level {level}: GPU encode", flush=True)
     x = to_dev(w.data)
     out, nb = g.encode(x, cs, ws, level)
     torch.cuda.synchronize()
     total = int(nb.item())
-    chunks = -(-w.n // cs)
-    hdr = out[:32].cpu().numpy()
-    assert g.stream_info(hdr.tobytes()) == (w.n, total, cs, ws)
-    table = out[32:32 + 8 * chunks].cpu().numpy().view("<u4").reshape(chunks, 2).astype(np.int64)
-    f, d = table[:, 0], table[:, 1]
-    sizes = np.where(f > 0, f + d, np.where(d & 0x80000000, d & 0x7FFFFFFF, 0))
-    offs = np.concatenate([[0], np.cumsum(sizes)])
-    assert 32 + 8 * chunks + offs[-1] == total
-    rng = np.random.default_rng(99 + level)
-    sample = np.unique(np.concatenate([np.arange(64), rng.integers(0, chunks, size=3000), [chunks - 1]]))
-    base = 32 + 8 * chunks
-    for c in sample:
-        chunk = w.data[c * cs: min((c + 1) * cs, w.n)]
-        ef, ed, pay = oracle_mod.encode_chunk(chunk, cs, ws, level)
-        assert (int(f[c]), int(d[c])) == (ef, ed), c
-        lo = base + int(offs[c])
-        assert out[lo:lo + len(pay)].cpu().numpy().tobytes() == pay, c
+    assert total > 0
+    got = out[:total].cpu().numpy()
+    print(f"stress 2 GiB level {level}: oracle on host threads", flush=True)
+    ref = oracle_mod.encode_parallel(w.data, cs, ws, level)
+    assert got.size == ref.size
+    assert np.array_equal(got, ref)
+    del got, ref
+    print(f"stress 2 GiB level {level}: GPU decode", flush=True)
     dec, db, st = g.decode(out[:total], out_capacity=w.n)
     torch.cuda.synchronize()
     assert int(st.item()) == 0 and int(db.item()) == w.n
@@ -147,7 +141,7 @@ def test_stress_2gib_sampled(g, oracle_mod, workloads, level):
 
 
 def test_decode_oracle_streams_all_levels(g, oracle_mod):
-    from chunked_lzss_coder_amd import synth
+    import workloads as synth
     w = synth.workload(0)
     for level in (0, 1):
         s = oracle_mod.encode(w.data, w.chunk_size, w.word_size, level)
@@ -156,7 +150,7 @@ def test_decode_oracle_streams_all_levels(g, oracle_mod):
 
 
 def test_deterministic_with_poisoned_workspace(g):
-    from chunked_lzss_coder_amd import synth
+    import workloads as synth
     w = synth.workload(0)
     x = to_dev(w.data)
     ref = None
@@ -255,7 +249,7 @@ def test_many_one_wave_chunks(g, oracle_mod):
     each chunk is decoded by one wave, its payload staged over its decoded
     bytes): the oracle's stream decodes to the input, and corrupting one
     coded chunk's match token gives the oracle's status."""
-    from chunked_lzss_coder_amd import synth
+    import workloads as synth
     cs, ws = 4096, 4
     n = 33000 * cs - 1000  # ragged tail
     w = synth.workload(4, scale_bytes=n + 1000)

@@ -87,7 +87,7 @@ def run(g, hip, data: np.ndarray, cs, ws, level):
 
 @pytest.mark.parametrize("level", [0, 1])
 def test_timed_workload_1800x3600(g, hip, oracle_mod, level):
-    from chunked_lzss_coder_amd import synth
+    import workloads as synth
     w = synth.workload(1)
     data = np.ascontiguousarray(w.data)
     got = run(g, hip, data, w.chunk_size, w.word_size, level)

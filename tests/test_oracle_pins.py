@@ -371,7 +371,7 @@ def test_zero_chunks_cost_only_their_entry(oracle_mod):
 
 
 def test_cross_level_streams_decode_identically(oracle_mod):
-    from chunked_lzss_coder_amd import synth
+    import workloads as synth
     w = synth.workload(0)
     s0 = oracle_mod.encode(w.data, w.chunk_size, w.word_size, 0)
     s1 = oracle_mod.encode(w.data, w.chunk_size, w.word_size, 1)
