@@ -21,7 +21,8 @@ SYMBOLS = ("gpulz_max_compressed_size", "gpulz_encode_workspace_size", "gpulz_de
            "gpulz_encode", "gpulz_decode", "gpulz_stream_info", "gpulz_encode_timed", "gpulz_decode_timed",
            "gpulz_split_bounds", "gpulz_encode_split_workspace_size", "gpulz_encode_split",
            "gpulz_decode_split_workspace_size", "gpulz_decode_split", "gpulz_decode_one_thread_per_chunk",
-           "gpulz_lorenzo_quant", "gpulz_encode_window", "gpulz_encode_advancing_search", "gpulz_split_info")
+           "gpulz_lorenzo_quant", "gpulz_encode_window", "gpulz_encode_advancing_search", "gpulz_split_info",
+           "gpulz_decode_noalloc")
 
 _lib = None
 
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
     L.gpulz_lorenzo_quant.restype = ctypes.c_int
     L.gpulz_split_info.argtypes = L.gpulz_stream_info.argtypes
     L.gpulz_split_info.restype = ctypes.c_int
+    L.gpulz_decode_noalloc.argtypes = [vp, u64, vp, u64, vp, vp, vp]
+    L.gpulz_decode_noalloc.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -203,6 +206,22 @@ def decode_into(d_stream, in_bytes: int, out, out_bytes, status, workspace, stre
             _check(lib().gpulz_decode(*args), "gpulz_decode")
         else:
             _check(lib().gpulz_decode_timed(*args, events[0], events[1]), "gpulz_decode_timed")
+
+
+DECODE_NOALLOC_MAX_CHUNKS = 1 << 22
+
+
+def decode_noalloc_into(d_stream, in_bytes: int, out, out_bytes, status, stream=None) -> None:
+    """Enqueue gpulz_decode_noalloc: decode_into without a workspace (the
+    library's static device array serves as one; calls whose work overlaps on
+    one GPU race).  Raises GpulzError if the call's chunk bound exceeds
+    DECODE_NOALLOC_MAX_CHUNKS."""
+    with _on(stream):
+        s = _u8_view(d_stream)
+        if in_bytes > s.numel():
+            raise GpulzError("in_bytes exceeds the stream buffer")
+        _check(lib().gpulz_decode_noalloc(_ptr(s), in_bytes, _ptr(out), out.numel(), _ptr(out_bytes), _ptr(status),
+                                          _stream(stream)), "gpulz_decode_noalloc")
 
 
 def decode_one_thread_per_chunk_into(d_stream, in_bytes: int, out, out_bytes, status, workspace, stream=None,

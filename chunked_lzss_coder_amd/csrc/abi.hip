@@ -7,6 +7,8 @@
 #include "gpulz_baseline.h"
 #include "gpulz_window.h"
 
+#include <mutex>
+
 #include "common.h"
 #include "scan_tiles.h"
 
@@ -199,20 +201,22 @@ int gpulz_decode_one_thread_per_chunk(const void* d_in, uint64_t in_bytes, void*
 }  // extern "C"
 
 namespace {
-int decode_common(const void* d_in, uint64_t in_bytes, void* d_out, uint64_t out_capacity, uint64_t* d_out_bytes,
-                  uint32_t* d_status, void* d_workspace, uint64_t workspace_bytes, hipStream_t stream,
-                  hipEvent_t ev_start, hipEvent_t ev_stop, bool serial) {
-  if (d_in == nullptr || d_out_bytes == nullptr || d_status == nullptr || d_workspace == nullptr)
-    return GPULZ_ERR_INVALID_ARG;
-  if (out_capacity > 0 && d_out == nullptr) return GPULZ_ERR_INVALID_ARG;
-  if (in_bytes < kHeaderBytes) return GPULZ_ERR_CORRUPT;
+// Chunk bound of a decode call: the stream's table cannot hold more rows than
+// (in_bytes - 32) / 8, and the output no more chunks than one per 1024 bytes
+// (the smallest chunk size).
+uint64_t dec_call_chunks(uint64_t in_bytes, uint64_t out_capacity) {
   uint64_t cap = dec_chunks_bound(in_bytes);
   const uint64_t by_out = num_chunks_of(out_capacity, 1024u);
   if (by_out < cap) cap = by_out;
   if (cap > 0xFFFFFFFFull) cap = 0xFFFFFFFFull;
-  const DecLayoutHost L = dec_layout(dec_chunks_bound(in_bytes));
-  if (workspace_bytes < L.total) return GPULZ_ERR_CAPACITY;
-  uint8_t* ws = align_up(d_workspace);
+  return cap;
+}
+
+// Enqueue the decode kernels with the workspace laid out by L from ws (a
+// kAlign-aligned address with L.total - kAlign bytes behind it).
+int decode_launch(const void* d_in, uint64_t in_bytes, void* d_out, uint64_t out_capacity, uint64_t* d_out_bytes,
+                  uint32_t* d_status, uint8_t* ws, const DecLayoutHost& L, uint64_t cap, hipStream_t stream,
+                  hipEvent_t ev_start, hipEvent_t ev_stop, bool serial) {
   DecodeArgs da;
   da.in = (const uint8_t*)d_in;
   da.in_bytes = in_bytes;
@@ -230,6 +234,49 @@ int decode_common(const void* d_in, uint64_t in_bytes, void* d_out, uint64_t out
   if ((serial ? launch_decode_serial(da, stream) : launch_decode(da, stream)) != hipSuccess) return GPULZ_ERR_HIP;
   return GPULZ_OK;
 }
+
+int decode_common(const void* d_in, uint64_t in_bytes, void* d_out, uint64_t out_capacity, uint64_t* d_out_bytes,
+                  uint32_t* d_status, void* d_workspace, uint64_t workspace_bytes, hipStream_t stream,
+                  hipEvent_t ev_start, hipEvent_t ev_stop, bool serial) {
+  if (d_in == nullptr || d_out_bytes == nullptr || d_status == nullptr || d_workspace == nullptr)
+    return GPULZ_ERR_INVALID_ARG;
+  if (out_capacity > 0 && d_out == nullptr) return GPULZ_ERR_INVALID_ARG;
+  if (in_bytes < kHeaderBytes) return GPULZ_ERR_CORRUPT;
+  const uint64_t cap = dec_call_chunks(in_bytes, out_capacity);
+  // sized by the stream bound alone, as gpulz_decode_workspace_size is
+  const DecLayoutHost L = dec_layout(dec_chunks_bound(in_bytes));
+  if (workspace_bytes < L.total) return GPULZ_ERR_CAPACITY;
+  return decode_launch(d_in, in_bytes, d_out, out_capacity, d_out_bytes, d_status, align_up(d_workspace), L, cap,
+                       stream, ev_start, ev_stop, serial);
+}
+
+// ---- decode without allocation: the workspace in a static device array ----
+// The decode workspace (stream parameters, per-chunk offsets within scan
+// tiles, tile totals and error flags) lives in `scratch`, one copy per GPU,
+// held from the library's first use on that GPU to the end of the process.
+// Every part of it is written by the scan kernel before the chunk kernel
+// reads it, so nothing needs clearing between calls.  In host code `scratch`
+// only names the symbol: its device address comes from hipGetSymbolAddress,
+// taken once per device with that device current and kept in scratch_ptr.
+constexpr uint64_t kNoAllocMaxChunks = GPULZ_DECODE_NOALLOC_MAX_CHUNKS;
+constexpr uint64_t kScratchBytes = kNoAllocMaxChunks * 4u + (64u << 10);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(uint8_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GPULZ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return GPULZ_ERR_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = (uint8_t*)scratch_ptr[dev];
+  return GPULZ_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -238,6 +285,25 @@ int gpulz_decode(const void* d_in, uint64_t in_bytes, void* d_out, uint64_t out_
                  uint32_t* d_status, void* d_workspace, uint64_t workspace_bytes, hipStream_t stream) {
   return gpulz_decode_timed(d_in, in_bytes, d_out, out_capacity, d_out_bytes, d_status, d_workspace,
                             workspace_bytes, stream, nullptr, nullptr);
+}
+
+int gpulz_decode_noalloc(const void* d_in, uint64_t in_bytes, void* d_out, uint64_t out_capacity,
+                         uint64_t* d_out_bytes, uint32_t* d_status, hipStream_t stream) {
+  if (d_in == nullptr || d_out_bytes == nullptr || d_status == nullptr) return GPULZ_ERR_INVALID_ARG;
+  if (out_capacity > 0 && d_out == nullptr) return GPULZ_ERR_INVALID_ARG;
+  if (in_bytes < kHeaderBytes) return GPULZ_ERR_CORRUPT;
+  const uint64_t cap = dec_call_chunks(in_bytes, out_capacity);
+  if (cap > kNoAllocMaxChunks) return GPULZ_ERR_CAPACITY;
+  // the scan and chunk kernels never index past chunk `cap - 1` (a stream
+  // declaring more chunks is rejected on the device), so the layout of the
+  // call's own bound suffices
+  const DecLayoutHost L = dec_layout(cap);
+  if (L.total > kScratchBytes) return GPULZ_ERR_CAPACITY;
+  uint8_t* ws = nullptr;
+  const int rc = scratch_of_current_device(&ws);
+  if (rc != GPULZ_OK) return rc;
+  return decode_launch(d_in, in_bytes, d_out, out_capacity, d_out_bytes, d_status, align_up(ws), L, cap, stream,
+                       nullptr, nullptr, false);
 }
 
 int gpulz_split_bounds(uint64_t n_bytes, uint32_t chunk_size, uint32_t word_size, uint64_t* lit_cap,

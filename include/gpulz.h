@@ -118,6 +118,31 @@ GPULZ_API int gpulz_decode(const void* d_in, uint64_t in_bytes, void* d_out, uin
                  uint64_t* d_out_bytes, uint32_t* d_status, void* d_workspace,
                  uint64_t workspace_bytes, hipStream_t stream);
 
+/* Largest chunk bound gpulz_decode_noalloc accepts (see there). */
+#define GPULZ_DECODE_NOALLOC_MAX_CHUNKS (1ull << 22)
+
+/* gpulz_decode without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments and
+ * results as gpulz_decode minus d_workspace / workspace_bytes; the
+ * workspace is a static device array of the library (about 16 MiB, one per
+ * GPU, held from the first call on that GPU until the process ends).
+ *   Size limit: the call's chunk bound, min((in_bytes - 32) / 8,
+ *     ceil(out_capacity / 1024)), must not exceed
+ *     GPULZ_DECODE_NOALLOC_MAX_CHUNKS (4,194,304: e.g. any output of up to
+ *     4 GiB), else GPULZ_ERR_CAPACITY and nothing is enqueued.  Pass
+ *     out_capacity = the stream's original size (gpulz_stream_info) to keep
+ *     the bound tight.
+ *   Concurrency: every call on one GPU uses that GPU's one array, so calls
+ *     whose work overlaps on one GPU (on different streams, or from several
+ *     host threads without ordering) race and give undefined results; calls
+ *     ordered on one stream are safe.  Nothing in the array needs to survive
+ *     from one call to the next.
+ *   Errors: as gpulz_decode; GPULZ_ERR_HIP also if the array's device
+ *     address cannot be obtained. */
+GPULZ_API int gpulz_decode_noalloc(const void* d_in, uint64_t in_bytes, void* d_out, uint64_t out_capacity,
+                                   uint64_t* d_out_bytes, uint32_t* d_status, hipStream_t stream);
+
 /* Host-side header read (no device access): from the first `bytes` (>= 32)
  * bytes of a stream in host memory, return its original size, total stream
  * length, chunk_size and word_size.  GPULZ_ERR_CORRUPT if the header is not

@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
                                          "gpulz_encode_split", "gpulz_decode_split_workspace_size",
                                          "gpulz_decode_split", "gpulz_decode_one_thread_per_chunk",
                                          "gpulz_lorenzo_quant", "gpulz_encode_window",
-                                         "gpulz_encode_advancing_search", "gpulz_split_info"])
+                                         "gpulz_encode_advancing_search", "gpulz_split_info",
+                                         "gpulz_decode_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(g):
@@ -135,6 +136,25 @@ def test_decode_rejects_bad_arguments_before_launch(g):
     assert dec(p, 31, p, big, p, p, p, big, None) == g.ERR_CORRUPT
     need = g.decode_workspace_size(1000)
     assert dec(p, 1000, p, big, p, p, p, need - 1, None) == g.ERR_CAPACITY
+
+
+def test_decode_noalloc_rejects_bad_arguments_before_launch(g):
+    # every call below fails a host check before the device is touched
+    p = ctypes.c_void_p(0x1000)
+    dec = g.lib().gpulz_decode_noalloc
+    big = 1 << 40
+    assert dec(None, 100, p, big, p, p, None) == g.ERR_INVALID_ARG
+    assert dec(p, 100, p, big, None, p, None) == g.ERR_INVALID_ARG
+    assert dec(p, 100, p, big, p, None, None) == g.ERR_INVALID_ARG
+    assert dec(p, 100, None, 10, p, p, None) == g.ERR_INVALID_ARG
+    assert dec(p, 31, p, big, p, p, None) == g.ERR_CORRUPT
+    mx = g.DECODE_NOALLOC_MAX_CHUNKS
+    # chunk bound = min((in_bytes - 32) / 8, ceil(out_capacity / 1024)) above the limit
+    assert dec(p, 32 + 8 * (mx + 1), p, 1024 * (mx + 1), p, p, None) == g.ERR_CAPACITY
+    assert dec(p, big, p, big, p, p, None) == g.ERR_CAPACITY
+    hdr = open(os.path.join(ROOT, "include", "gpulz.h")).read()
+    assert re.search(r"#define GPULZ_DECODE_NOALLOC_MAX_CHUNKS \(1ull << 22\)", hdr)
+    assert mx == 1 << 22
 
 
 def test_product_package_does_not_import_the_oracle():
