@@ -78,6 +78,64 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
   return v;
 }
 
+// The short descent's mark for a position whose longest match is 16 or
+// longer (its exact length is found only if the parse starts an item there),
+// and the segment-exit flag that sends the parse to such a position.
+constexpr uint32_t kLongMark = 0xFFu;
+constexpr uint32_t kLongExit = 0x8000u;
+
+// DPP lane move whose out-of-row or masked-off lanes read all ones (the
+// identity of AND).
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_ones(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)0xFFFFFFFF, (int)v, CTRL, ROWS, 0xF, false);
+}
+
+// Inclusive AND scan over the 64 lanes (lane i: AND of lanes 0..i).
+__device__ __forceinline__ uint32_t wave_incl_and(uint32_t v) {
+  v &= dpp_ones<kRowShr1>(v);
+  v &= dpp_ones<kRowShr2>(v);
+  v &= dpp_ones<kRowShr4>(v);
+  v &= dpp_ones<kRowShr8>(v);
+  v &= dpp_ones<kRowBcast15, 0xA>(v);
+  v &= dpp_ones<kRowBcast31, 0xC>(v);
+  return v;
+}
+
+// Exact capped longest match at position r (uniform; every lane of the wave
+// takes part), GPULZStage page, exact longest-match search and long-match
+// paragraphs: L = the largest k <= min(255, E - r) such that some offset
+// matches at all of r .. r + k - 1, i.e. the AND of omask over [r, r + k) is
+// not empty; O = the smallest offset left in that AND.  One round: lane j
+// takes positions r + 4j .. r + 4j + 3 (256 >= 255), ANDs them in order,
+// and an exclusive AND scan over the lanes supplies what comes before; the
+// running ANDs only shrink, so the non-empty ones are a prefix and L is
+// their count.  Returns L | O << 8.
+__device__ __forceinline__ uint32_t long_match(const uint32_t* S1, uint32_t r, uint32_t E) {
+  const uint32_t lane = lane_id();
+  const uint32_t lim = (E - r) < kMaxLen ? (E - r) : kMaxLen;
+  const uint32_t i0 = 4u * lane;
+  const uint32_t m0 = i0 < lim ? S1[r + i0] : 0u;
+  const uint32_t m1 = i0 + 1u < lim ? S1[r + i0 + 1u] : 0u;
+  const uint32_t m2 = i0 + 2u < lim ? S1[r + i0 + 2u] : 0u;
+  const uint32_t m3 = i0 + 3u < lim ? S1[r + i0 + 3u] : 0u;
+  const uint32_t a1 = m0 & m1, a2 = a1 & m2, a3 = a2 & m3;
+  // AND of every earlier lane's four (all ones for lane 0)
+  const uint32_t incl = wave_incl_and(a3);
+  const uint32_t ex = lane ? dpp_ones<kWaveShr1>(incl) : ~0u;
+  const uint32_t p0 = ex & m0, p1 = ex & a1, p2 = ex & a2, p3 = ex & a3;
+  const uint32_t cnt = (uint32_t)(p0 != 0u) + (uint32_t)(p1 != 0u) + (uint32_t)(p2 != 0u) + (uint32_t)(p3 != 0u);
+  // the first lane whose four are not all non-empty ends the run
+  const uint64_t part = __ballot(cnt < 4u);
+  const uint32_t jl = part ? (uint32_t)__builtin_ctzll(part) : 63u;
+  const uint32_t L = 4u * jl + (uint32_t)__builtin_amdgcn_readlane((int)cnt, (int)jl);
+  // survivors at position L - 1: lane (L - 1) / 4, running AND (L - 1) % 4
+  const uint32_t k = (L - 1u) & 3u;
+  const uint32_t pk = k == 0u ? p0 : (k == 1u ? p1 : (k == 2u ? p2 : p3));
+  const uint32_t fin = (uint32_t)__builtin_amdgcn_readlane((int)pk, (int)((L - 1u) >> 2));
+  return L | (((uint32_t)__builtin_ctz(fin) + 1u) << 8);
+}
+
 // Decoupled look-back over the chunks' published payload sizes (one wave).
 // Each flag is one 64-bit word {state:2, value:62}, written with one atomic
 // store, so a reader never sees a state without its value.  Nothing else is
@@ -200,10 +258,30 @@ struct Lay {
   static constexpr uint32_t SEARCH = MW * (3u * E + PAD);
   static constexpr bool XL = LEVEL == 1 && E >= 2048;                // level 1, X reloaded
   static constexpr uint32_t XW = LEVEL == 1 && !XL ? (uint32_t)E : 0u;  // words of a separate X
+  // Level 0 with the 32-offset window and chunks of up to 1024 elements
+  // (LAZY): the descent finds lengths below 16 at every position and marks
+  // longer ones; the exact length of a long match is found only where the
+  // parse starts an item (most positions inside long matches are never item
+  // starts).  Regions, in words:
+  //   S_1 [0, E) + 16 zero words (the long-match scan and the short descent
+  //       read S_1; the payload staging overlays it once the parse is done)
+  //   S_4 [E + 16, 2E + 16) + 16 zero words, then LO (the same words)
+  //   XQ  [2E + 32, 3E + 32) segment exits | ISB | LMB | FLG (E/32 each)
+  static constexpr bool LAZY = LEVEL == 0 && W == 32 && E <= 1024;
+  static constexpr uint32_t LZ_T4 = E + 16u;
+  static constexpr uint32_t LZ_XQ = 2u * E + 32u;
+  static constexpr uint32_t LZ_ISB = 3u * E + 32u;
+  static constexpr uint32_t LZ_R = 3u * E + 32u + 3u * (E / 32u);
+  static_assert(!LAZY || CS / 4u + 4u <= E + 16u, "payload staging fits over S_1");
   static constexpr uint32_t R =
-      (cmax(cmax(SEARCH, LEVEL ? (XL ? 2u : 1u) * E + kHashSize : 0u), RP) + 3u) & ~3u;
+      LAZY ? ((LZ_R + 3u) & ~3u)
+           : (cmax(cmax(SEARCH, LEVEL ? (XL ? 2u : 1u) * E + kHashSize : 0u), RP) + 3u) & ~3u;
   static constexpr uint32_t MISC = 2u * (E / 64u + 1u) + 8u;
-  static constexpr uint32_t TOTAL = (XW + R + MISC + 3u) & ~3u;  // words per chunk, 16-byte multiple
+  // 32 zero words ahead of X (32-offset window): every lane of the offset-mask
+  // pass loads its 32 + 8 words with the same 16-byte loads, the first lanes'
+  // window running into the zeros (the bits they give are masked off)
+  static constexpr uint32_t XPAD = W == 32 ? 32u : 0u;
+  static constexpr uint32_t TOTAL = (XPAD + XW + R + MISC + 3u) & ~3u;  // words per chunk, 16-byte multiple
 };
 
 template <int WS, int E, int LEVEL, int W, int WPC, int CPW>
@@ -227,19 +305,19 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
   const uint32_t team = threadIdx.x / TL;
   const uint32_t g = threadIdx.x % TL;  // lane within the team
   const uint32_t lane = lane_id();
-  uint32_t* X = lds_all + team * L::TOTAL;
+  uint32_t* X = lds_all + team * L::TOTAL + L::XPAD;
   uint32_t* LV = X + L::XW;  // X and S_1 share their words unless X has its own region
   // level 1: the words for the candidate checks (its own region, or loaded
   // again behind the hash table)
   uint32_t* XL = L::XL ? LV + E + kHashSize : X;
   Mask* LVm = (Mask*)LV;  // the search tables
-  uint32_t* LO = LV;
-  uint32_t* XQ = LV + E;
+  uint32_t* LO = L::LAZY ? LV + L::LZ_T4 : LV;
+  uint32_t* XQ = L::LAZY ? LV + L::LZ_XQ : LV + E;
   uint32_t* T = LV + E;
-  uint32_t* ISB = LV + 2u * E;
+  uint32_t* ISB = L::LAZY ? LV + L::LZ_ISB : LV + 2u * E;
   uint32_t* LMB = ISB + E / 32u;
   uint32_t* FLG = LMB + E / 32u;
-  uint8_t* STG = (uint8_t*)(FLG + E / 32u);
+  uint8_t* STG = L::LAZY ? (uint8_t*)LV : (uint8_t*)(FLG + E / 32u);
   uint32_t* MISC = LV + L::R;
   uint32_t* KB = MISC;                   // items before 64-position word w
   uint32_t* MB = MISC + (E / 64u + 1u);  // matches before word w
@@ -261,6 +339,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
   };
 
   // ---- 1. load + zero vote ---------------------------------------------------------
+  for (uint32_t i = g; i < L::XPAD; i += TL) X[(int)i - (int)L::XPAD] = 0u;
   uint32_t any = 0;
   if (bc == CS && (((uintptr_t)src) & 15u) == 0) {
     const uint4* s4 = (const uint4*)src;
@@ -316,7 +395,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
       for (uint32_t ps = 0; ps < NPASS; ++ps) {
         const uint32_t p0 = (ps * TL + g) * PPASS;
         uint32_t w[32 + PPASS];
-        if (p0 >= 32u) {
+        if (L::XPAD != 0u || p0 >= 32u) {
 #pragma unroll
           for (uint32_t i = 0; i < (32 + PPASS) / 4; ++i) {
             const uint4 v = *(const uint4*)(X + p0 - 32u + 4u * i);
@@ -339,8 +418,14 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
           uint32_t m = 0;
           match_bits16(m, &w[q], w[32 + q]);
           match_bits16(m, &w[q + 16], w[32 + q]);
-          const uint32_t p = p0 + q;
-          om[q] = p >= 32u ? m : (m & ((1u << p) - 1u));
+          om[q] = m;
+        }
+        if (p0 < 32u) {  // offsets reach back to the chunk start at most: bits o - 1 < p
+#pragma unroll
+          for (uint32_t q = 0; q < PPASS; ++q) {
+            const uint32_t p = p0 + q;
+            if (p < 32u) om[q] &= (1u << p) - 1u;
+          }
         }
         if constexpr (W > 32) {
           // offsets 33..W into bits 32..W-1, from the W - 32 + PPASS words
@@ -402,7 +487,49 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
     if (LEVEL == 0 && !near) {
       K = (uint32_t)E;
     } else {
-      if (near) {
+      if (L::LAZY && near) {
+        // ---- 3 (short form). S_4 and a two-round descent for lengths below 16 ---------
+        // S_4[p] = AND of S_1 over [p, p + 4) (0 past the chunk).  At each
+        // position: t_j = AND of S_1 over [p, p + 4j) for j = 1..4 (nested
+        // sets); t_4 not empty means L >= 16 and the position gets the long
+        // mark.  Otherwise a = the number of non-empty t_1..t_3, then up to
+        // three single steps from p + 4a: L = 4a + b < 16 exactly, O = the
+        // smallest offset left.  S_1 and S_4 are followed by 16 zero words,
+        // so no read needs a bounds check.
+        uint32_t* S1 = LV;
+        uint32_t* S4 = LV + L::LZ_T4;
+        for (uint32_t i = g; i < 32u; i += TL) {
+          if (i < 16u) S1[E + i] = 0u;
+          else S4[E + i - 16u] = 0u;
+        }
+#pragma unroll
+        for (uint32_t i = 0; i < PPL; ++i) {
+          const uint32_t p = g + i * TL;
+          uint32_t v = 0;
+          if (p + 4u <= (uint32_t)E) v = S1[p] & S1[p + 1] & S1[p + 2] & S1[p + 3];
+          S4[p] = v;
+        }
+        team_sync<WPC>();
+        uint32_t lo[PPL];
+#pragma unroll
+        for (uint32_t i = 0; i < PPL; ++i) {
+          const uint32_t p = g + i * TL;
+          const uint32_t* T4 = S4 + p;
+          const uint32_t t1 = T4[0], t2 = t1 & T4[4], t3 = t2 & T4[8], t4 = t3 & T4[12];
+          const uint32_t a = (uint32_t)(t1 != 0u) + (uint32_t)(t2 != 0u) + (uint32_t)(t3 != 0u);
+          const uint32_t sa = t3 ? t3 : (t2 ? t2 : (t1 ? t1 : ~0u));
+          const uint32_t* T1 = S1 + p + 4u * a;
+          const uint32_t u1 = sa & T1[0], u2 = u1 & T1[1], u3 = u2 & T1[2];
+          const uint32_t b = (uint32_t)(u1 != 0u) + (uint32_t)(u2 != 0u) + (uint32_t)(u3 != 0u);
+          const uint32_t fin = u3 ? u3 : (u2 ? u2 : (u1 ? u1 : sa));
+          const uint32_t Ls = 4u * a + b;
+          lo[i] = t4 ? kLongMark : (Ls ? (Ls | (((uint32_t)__builtin_ctz(fin) + 1u) << 8)) : 0u);
+        }
+        team_sync<WPC>();
+#pragma unroll
+        for (uint32_t i = 0; i < PPL; ++i) LO[g + i * TL] = lo[i];  // over S_4
+        team_sync<WPC>();
+      } else if (near) {
         // ---- 3. base-4 doubling table S_4, S_16 and a 4-round descent -----------------
         // S_k[p] = AND of omask over [p, p+k) when p + k <= E, else 0; every
         // table is followed by zeros, so descent reads past the chunk need no
@@ -595,6 +722,9 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
                 e = ex[r];
                 m = (1u << q) | im[r];
               }
+            // a long match starts here: its length is found when the parse
+            // gets here, so the exit names this position
+            if (L::LAZY && l8[q] == kLongMark) e = (p0 + (uint32_t)q) | kLongExit;
             ex[q] = e;
             im[q] = m;
           }
@@ -619,16 +749,32 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             xqr[i] = XQ[p];
             lmw[i] = __ballot((LO[p] & 0xFFu) >= MM);
           }
+          // The walk only records where it enters each segment (one scalar
+          // bit per hop); each segment's item starts are then read from its
+          // exit table by the lanes of the segment, all words at once.  A
+          // long-match exit (flagged, so past every word bound) leaves the
+          // inner walk to have the match's length found.
           uint32_t P = 0;
 #pragma unroll
           for (uint32_t i = 0; i < NR; ++i) {
-            uint64_t acc = 0;
-            while (P < 64u * (i + 1u)) {
-              const uint32_t xq = __builtin_amdgcn_readlane(xqr[i], P & 63u);
-              acc |= (uint64_t)(xq >> 16) << (P & 56u);
-              P = xq & 0xFFFFu;
+            uint64_t ent = 0;
+            while (true) {
+              while (P < 64u * (i + 1u)) {
+                ent |= 1ull << (P & 63u);
+                P = __builtin_amdgcn_readlane(xqr[i], P & 63u) & 0xFFFFu;
+              }
+              if (!(L::LAZY && (P & kLongExit))) break;
+              const uint32_t r = P & ~kLongExit;  // a long match starts at r
+              const uint32_t v = long_match(LV, r, (uint32_t)E);
+              if (lane == 0u) LO[r] = v;
+              P = r + ((v & 0xFFu) ? (v & 0xFFu) : 1u);  // L >= 16 here; the select only guards progress
             }
-            isw[i] = acc;
+            // lane j: segment j >> 3 of the word, entered at most once
+            const uint32_t sb = lane & 56u;
+            const uint32_t se = (uint32_t)(ent >> sb) & 0xFFu;
+            const uint32_t q0 = se ? (uint32_t)__builtin_ctz(se) : 0u;
+            const uint32_t xe = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((sb + q0) << 2), (int)xqr[i]);
+            isw[i] = __ballot(se != 0u && ((xe >> (16u + (lane & 7u))) & 1u));
           }
           // ---- 6. counts -------------------------------------------------------------------
 #pragma unroll
@@ -652,12 +798,24 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
               for (uint32_t i = 0; i < NR; ++i) {
                 const uint32_t xqr = xq_next;
                 if (i + 1u < NR) xq_next = XQ[64u * (i + 1u) + lane];
-                uint64_t acc = 0;
-                while (P < 64u * (i + 1u)) {
-                  const uint32_t xq = __builtin_amdgcn_readlane(xqr, P & 63u);
-                  acc |= (uint64_t)(xq >> 16) << (P & 56u);
-                  P = xq & 0xFFFFu;
+                // entries only, as in the one-wave walk
+                uint64_t ent = 0;
+                while (true) {
+                  while (P < 64u * (i + 1u)) {
+                    ent |= 1ull << (P & 63u);
+                    P = __builtin_amdgcn_readlane(xqr, P & 63u) & 0xFFFFu;
+                  }
+                  if (!(L::LAZY && (P & kLongExit))) break;
+                  const uint32_t r = P & ~kLongExit;  // a long match starts at r
+                  const uint32_t v = long_match(LV, r, (uint32_t)E);
+                  if (lane == 0u) LO[r] = v;
+                  P = r + ((v & 0xFFu) ? (v & 0xFFu) : 1u);  // L >= 16 here; the select only guards progress
                 }
+                const uint32_t sb = lane & 56u;
+                const uint32_t se = (uint32_t)(ent >> sb) & 0xFFu;
+                const uint32_t q0 = se ? (uint32_t)__builtin_ctz(se) : 0u;
+                const uint32_t xe = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((sb + q0) << 2), (int)xqr);
+                const uint64_t acc = __ballot(se != 0u && ((xe >> (16u + (lane & 7u))) & 1u));
                 if (lane == 0u) IS64w[i] = acc;
               }
             }
@@ -763,7 +921,11 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
   // ---- 7. size-table row, payload into the chunk's staging slot --------------------
   // Flags first (bit k of the bitmap = item k is a match), then the data bytes
   // right after them, so the slot holds the payload exactly as it will appear
-  // in the stream; the compaction kernel moves it to its final offset.
+  // in the stream; the compaction kernel moves it to its final offset.  In
+  // LDS the data bytes start on a 4-byte boundary DB and the flag bytes end
+  // there (the payload is STG[DB - F, DB + D)), so literals and match tokens
+  // go in with 16-bit writes (word sizes 2 and 4); the copy to the slot
+  // realigns by DB - F bytes.
   uint32_t* STG32 = (uint32_t*)STG;
   uint32_t* slot = (uint32_t*)(staging + base);
   if (nonzero && !raw) {
@@ -775,35 +937,40 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
       const uint32_t p = WPC == 1 ? 64u * i + lane : g + i * TL;
       xv[i] = L::XW ? X[p] : word_at(p);
     }
-    for (uint32_t i = g; i < (F + 3u) / 4u; i += TL) STG32[i] = 0u;
+    const uint32_t DB = (F + 3u) & ~3u;
+    const uint32_t S0 = DB - F;  // payload byte 0 is STG byte S0
+    for (uint32_t i = g; i < DB / 4u; i += TL) STG32[i] = 0u;
     team_sync<WPC>();
-    if constexpr (WPC == 1) {
-#pragma unroll
-      for (uint32_t i = 0; i < NR; ++i) {
-        const uint64_t is = isw[i], ms = is & lmw[i];
-        if ((ms >> lane) & 1ull) {
-          const uint32_t k = kb[i] + mbcnt64(is);
-          atomicOr(&STG32[k >> 5], 1u << (k & 31u));
+    // item k: flag bit 8 S0 + k of STG; data bytes at DB + WS (k - m) + 2 m
+    // (m = matches before it)
+    auto put_item = [&](bool match, uint32_t k, uint32_t m, uint32_t lo_v, uint32_t x) {
+      const uint32_t off = DB + (uint32_t)WS * (k - m) + 2u * m;
+      if (match) {
+        const uint32_t fb = 8u * S0 + k;
+        atomicOr(&STG32[fb >> 5], 1u << (fb & 31u));
+        if (WS >= 2) {
+          *(uint16_t*)(STG + off) = (uint16_t)lo_v;
+        } else {
+          STG[off] = (uint8_t)lo_v;
+          STG[off + 1] = (uint8_t)(lo_v >> 8);
         }
+      } else if (WS == 4) {
+        *(uint16_t*)(STG + off) = (uint16_t)x;
+        *(uint16_t*)(STG + off + 2) = (uint16_t)(x >> 16);
+      } else if (WS == 2) {
+        *(uint16_t*)(STG + off) = (uint16_t)x;
+      } else {
+        STG[off] = (uint8_t)x;
       }
-      team_sync<WPC>();
+    };
+    if constexpr (WPC == 1) {
 #pragma unroll
       for (uint32_t i = 0; i < NR; ++i) {
         const uint32_t p = 64u * i + lane;
         const uint64_t is = isw[i], ms = is & lmw[i];
         if (!((is >> lane) & 1ull)) continue;
-        const uint32_t k = kb[i] + mbcnt64(is);
-        const uint32_t m = mb[i] + mbcnt64(ms);
-        const uint32_t off = F + (uint32_t)WS * (k - m) + 2u * m;
-        if ((ms >> lane) & 1ull) {
-          const uint32_t v = LO[p];
-          STG[off] = (uint8_t)v;
-          STG[off + 1] = (uint8_t)(v >> 8);
-        } else {
-          const uint32_t v = xv[i];
-#pragma unroll
-          for (int b = 0; b < WS; ++b) STG[off + b] = (uint8_t)(v >> (8 * b));
-        }
+        const bool mt = (ms >> lane) & 1ull;
+        put_item(mt, kb[i] + mbcnt64(is), mb[i] + mbcnt64(ms), mt ? LO[p] : 0u, xv[i]);
       }
     } else {
       const uint64_t* IS64 = (const uint64_t*)ISB;
@@ -814,36 +981,19 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
         const uint32_t wi = p >> 6;
         const uint64_t is = IS64[wi], ms = is & LM64[wi];
         const uint64_t bit = 1ull << (p & 63u);
-        if (ms & bit) {
-          const uint32_t k = KB[wi] + (uint32_t)__builtin_popcountll(is & (bit - 1ull));
-          atomicOr(&STG32[k >> 5], 1u << (k & 31u));
-        }
-      }
-      team_sync<WPC>();
-#pragma unroll
-      for (uint32_t i = 0; i < PPL; ++i) {
-        const uint32_t p = g + i * TL;
-        const uint32_t wi = p >> 6;
-        const uint64_t is = IS64[wi], ms = is & LM64[wi];
-        const uint64_t bit = 1ull << (p & 63u);
         if (!(is & bit)) continue;
         const uint64_t below = bit - 1ull;
-        const uint32_t k = KB[wi] + (uint32_t)__builtin_popcountll(is & below);
-        const uint32_t m = MB[wi] + (uint32_t)__builtin_popcountll(ms & below);
-        const uint32_t off = F + (uint32_t)WS * (k - m) + 2u * m;
-        if (ms & bit) {
-          const uint32_t v = LO[p];
-          STG[off] = (uint8_t)v;
-          STG[off + 1] = (uint8_t)(v >> 8);
-        } else {
-          const uint32_t v = xv[i];
-#pragma unroll
-          for (int b = 0; b < WS; ++b) STG[off + b] = (uint8_t)(v >> (8 * b));
-        }
+        const bool mt = (ms & bit) != 0ull;
+        put_item(mt, KB[wi] + (uint32_t)__builtin_popcountll(is & below),
+                 MB[wi] + (uint32_t)__builtin_popcountll(ms & below), mt ? LO[p] : 0u, xv[i]);
       }
     }
     team_sync<WPC>();
-    for (uint32_t i = g; i < (F + D + 3u) / 4u; i += TL) slot[i] = STG32[i];
+    const uint32_t nd = (F + D + 3u) / 4u;
+    for (uint32_t i = g; i < nd; i += TL) {
+      const uint32_t a = STG32[i], b = STG32[i + 1];
+      slot[i] = S0 ? __builtin_amdgcn_alignbyte(b, a, S0) : a;
+    }
   }
   if (g == 0) {
     const uint2 ent = !nonzero ? make_uint2(0u, 0u) : (raw ? make_uint2(0u, kRawBit | bc) : make_uint2(F, D));
