@@ -265,18 +265,26 @@ struct Lay {
   // starts).  Regions, in words:
   //   S_1 [0, E) + 16 zero words (the long-match scan and the short descent
   //       read S_1; the payload staging overlays it once the parse is done)
-  //   S_4 [E + 16, 2E + 16) + 16 zero words, then LO (the same words)
-  //   XQ  [2E + 32, 3E + 32) segment exits | ISB | LMB | FLG (E/32 each)
+  //   S_4 [E + 16, 2E + 16) + 12 zero words; after the descent the same words
+  //       hold LOX: (L | O << 8) in the low half, and from the segment pass
+  //       on, the position's segment exit in the high half
+  //   IM  [2E + 28, 2E + 28 + E/4) the item-start bits of the segment walk
+  //       from each position, a byte each
+  //   ISB | LMB (E/32 each, teams of several waves only)
+  // Teams of one wave keep the item bits and counts in registers and need no
+  // further words, so a two-chunk workgroup of 512-element chunks takes
+  // under 10 KB of LDS.
   static constexpr bool LAZY = LEVEL == 0 && W == 32 && E <= 1024;
+  static constexpr uint32_t WPC_ = E <= 512 ? 1u : (uint32_t)E / 512u;  // waves per chunk (launch_one)
   static constexpr uint32_t LZ_T4 = E + 16u;
-  static constexpr uint32_t LZ_XQ = 2u * E + 32u;
-  static constexpr uint32_t LZ_ISB = 3u * E + 32u;
-  static constexpr uint32_t LZ_R = 3u * E + 32u + 3u * (E / 32u);
+  static constexpr uint32_t LZ_IM = 2u * E + 28u;
+  static constexpr uint32_t LZ_ISB = LZ_IM + E / 4u;
+  static constexpr uint32_t LZ_R = LZ_ISB + (WPC_ > 1u ? 2u * (E / 32u) : 0u);
   static_assert(!LAZY || CS / 4u + 4u <= E + 16u, "payload staging fits over S_1");
   static constexpr uint32_t R =
       LAZY ? ((LZ_R + 3u) & ~3u)
            : (cmax(cmax(SEARCH, LEVEL ? (XL ? 2u : 1u) * E + kHashSize : 0u), RP) + 3u) & ~3u;
-  static constexpr uint32_t MISC = 2u * (E / 64u + 1u) + 8u;
+  static constexpr uint32_t MISC = (LAZY && WPC_ == 1u) ? 0u : 2u * (E / 64u + 1u) + 8u;
   // 32 zero words ahead of X (32-offset window): every lane of the offset-mask
   // pass loads its 32 + 8 words with the same 16-byte loads, the first lanes'
   // window running into the zeros (the bits they give are masked off)
@@ -311,13 +319,20 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
   // again behind the hash table)
   uint32_t* XL = L::XL ? LV + E + kHashSize : X;
   Mask* LVm = (Mask*)LV;  // the search tables
-  uint32_t* LO = L::LAZY ? LV + L::LZ_T4 : LV;
-  uint32_t* XQ = L::LAZY ? LV + L::LZ_XQ : LV + E;
+  uint32_t* LO = L::LAZY ? LV + L::LZ_T4 : LV;  // LAZY: LOX
+  uint32_t* XQ = LV + E;                         // not LAZY: exit | item-start bits << 16
+  uint8_t* IM = (uint8_t*)(LV + L::LZ_IM);       // LAZY: item-start bits
   uint32_t* T = LV + E;
   uint32_t* ISB = L::LAZY ? LV + L::LZ_ISB : LV + 2u * E;
   uint32_t* LMB = ISB + E / 32u;
   uint32_t* FLG = LMB + E / 32u;
   uint8_t* STG = L::LAZY ? (uint8_t*)LV : (uint8_t*)(FLG + E / 32u);
+  // segment exit of position p and the item-start bits of the walk from it
+  // (exit | bits << 16)
+  auto xq_at = [&](uint32_t p) -> uint32_t {
+    if constexpr (L::LAZY) return (LO[p] >> 16) | ((uint32_t)IM[p] << 16);
+    else return XQ[p];
+  };
   uint32_t* MISC = LV + L::R;
   uint32_t* KB = MISC;                   // items before 64-position word w
   uint32_t* MB = MISC + (E / 64u + 1u);  // matches before word w
@@ -498,7 +513,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
         // so no read needs a bounds check.
         uint32_t* S1 = LV;
         uint32_t* S4 = LV + L::LZ_T4;
-        for (uint32_t i = g; i < 32u; i += TL) {
+        for (uint32_t i = g; i < 28u; i += TL) {
           if (i < 16u) S1[E + i] = 0u;
           else S4[E + i - 16u] = 0u;
         }
@@ -728,10 +743,20 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             ex[q] = e;
             im[q] = m;
           }
-          *(uint4*)(XQ + p0) = make_uint4(ex[0] | (im[0] << 16), ex[1] | (im[1] << 16), ex[2] | (im[2] << 16),
-                                          ex[3] | (im[3] << 16));
-          *(uint4*)(XQ + p0 + 4) = make_uint4(ex[4] | (im[4] << 16), ex[5] | (im[5] << 16),
-                                              ex[6] | (im[6] << 16), ex[7] | (im[7] << 16));
+          if constexpr (L::LAZY) {
+            // the exit beside (L, O), the bits in their own bytes
+            *(uint4*)(LO + p0) = make_uint4((l8[0] & 0xFFFFu) | (ex[0] << 16), (l8[1] & 0xFFFFu) | (ex[1] << 16),
+                                            (l8[2] & 0xFFFFu) | (ex[2] << 16), (l8[3] & 0xFFFFu) | (ex[3] << 16));
+            *(uint4*)(LO + p0 + 4) = make_uint4((l8[4] & 0xFFFFu) | (ex[4] << 16), (l8[5] & 0xFFFFu) | (ex[5] << 16),
+                                                (l8[6] & 0xFFFFu) | (ex[6] << 16), (l8[7] & 0xFFFFu) | (ex[7] << 16));
+            *(uint2*)(IM + p0) = make_uint2(im[0] | (im[1] << 8) | (im[2] << 16) | (im[3] << 24),
+                                            im[4] | (im[5] << 8) | (im[6] << 16) | (im[7] << 24));
+          } else {
+            *(uint4*)(XQ + p0) = make_uint4(ex[0] | (im[0] << 16), ex[1] | (im[1] << 16), ex[2] | (im[2] << 16),
+                                            ex[3] | (im[3] << 16));
+            *(uint4*)(XQ + p0 + 4) = make_uint4(ex[4] | (im[4] << 16), ex[5] | (im[5] << 16),
+                                                ex[6] | (im[6] << 16), ex[7] | (im[7] << 16));
+          }
           if (WPC > 1) {
             ((uint8_t*)LMB)[sg] = (uint8_t)lmb;
             ((uint8_t*)ISB)[sg] = 0;
@@ -746,7 +771,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
 #pragma unroll
           for (uint32_t i = 0; i < NR; ++i) {
             const uint32_t p = 64u * i + lane;
-            xqr[i] = XQ[p];
+            xqr[i] = xq_at(p);
             lmw[i] = __ballot((LO[p] & 0xFFu) >= MM);
           }
           // The walk only records where it enters each segment (one scalar
@@ -766,7 +791,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
               if (!(L::LAZY && (P & kLongExit))) break;
               const uint32_t r = P & ~kLongExit;  // a long match starts at r
               const uint32_t v = long_match(LV, r, (uint32_t)E);
-              if (lane == 0u) LO[r] = v;
+              if (lane == 0u) *(uint16_t*)(LO + r) = (uint16_t)v;  // (L, O); the exit half stays
               P = r + ((v & 0xFFu) ? (v & 0xFFu) : 1u);  // L >= 16 here; the select only guards progress
             }
             // lane j: segment j >> 3 of the word, entered at most once
@@ -793,11 +818,11 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             if (g < 64u) {
               uint64_t* IS64w = (uint64_t*)ISB;
               uint32_t P = 0;
-              uint32_t xq_next = XQ[lane];
+              uint32_t xq_next = xq_at(lane);
 #pragma unroll 1
               for (uint32_t i = 0; i < NR; ++i) {
                 const uint32_t xqr = xq_next;
-                if (i + 1u < NR) xq_next = XQ[64u * (i + 1u) + lane];
+                if (i + 1u < NR) xq_next = xq_at(64u * (i + 1u) + lane);
                 // entries only, as in the one-wave walk
                 uint64_t ent = 0;
                 while (true) {
@@ -808,7 +833,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
                   if (!(L::LAZY && (P & kLongExit))) break;
                   const uint32_t r = P & ~kLongExit;  // a long match starts at r
                   const uint32_t v = long_match(LV, r, (uint32_t)E);
-                  if (lane == 0u) LO[r] = v;
+                  if (lane == 0u) *(uint16_t*)(LO + r) = (uint16_t)v;  // (L, O); the exit half stays
                   P = r + ((v & 0xFFu) ? (v & 0xFFu) : 1u);  // L >= 16 here; the select only guards progress
                 }
                 const uint32_t sb = lane & 56u;
@@ -964,17 +989,22 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
       }
     };
     if constexpr (WPC == 1) {
+      uint32_t lov[NR];  // every position's (L, O), loaded before any item is placed
+#pragma unroll
+      for (uint32_t i = 0; i < NR; ++i) lov[i] = LO[64u * i + lane];
 #pragma unroll
       for (uint32_t i = 0; i < NR; ++i) {
-        const uint32_t p = 64u * i + lane;
         const uint64_t is = isw[i], ms = is & lmw[i];
         if (!((is >> lane) & 1ull)) continue;
         const bool mt = (ms >> lane) & 1ull;
-        put_item(mt, kb[i] + mbcnt64(is), mb[i] + mbcnt64(ms), mt ? LO[p] : 0u, xv[i]);
+        put_item(mt, kb[i] + mbcnt64(is), mb[i] + mbcnt64(ms), lov[i], xv[i]);
       }
     } else {
       const uint64_t* IS64 = (const uint64_t*)ISB;
       const uint64_t* LM64 = (const uint64_t*)LMB;
+      uint32_t lov[PPL];  // every position's (L, O), loaded before any item is placed
+#pragma unroll
+      for (uint32_t i = 0; i < PPL; ++i) lov[i] = LO[g + i * TL];
 #pragma unroll
       for (uint32_t i = 0; i < PPL; ++i) {
         const uint32_t p = g + i * TL;
@@ -985,7 +1015,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
         const uint64_t below = bit - 1ull;
         const bool mt = (ms & bit) != 0ull;
         put_item(mt, KB[wi] + (uint32_t)__builtin_popcountll(is & below),
-                 MB[wi] + (uint32_t)__builtin_popcountll(ms & below), mt ? LO[p] : 0u, xv[i]);
+                 MB[wi] + (uint32_t)__builtin_popcountll(ms & below), lov[i], xv[i]);
       }
     }
     team_sync<WPC>();
