@@ -281,9 +281,13 @@ struct Lay {
   static constexpr uint32_t LZ_ISB = LZ_IM + E / 4u;
   static constexpr uint32_t LZ_R = LZ_ISB + (WPC_ > 1u ? 2u * (E / 32u) : 0u);
   static_assert(!LAZY || CS / 4u + 4u <= E + 16u, "payload staging fits over S_1");
+  // level 1 with chunks of up to 512 elements: 16-bit buckets (positions + 1
+  // fit), half the table's LDS, so half again as many chunks per CU
+  static constexpr bool HT16 = LEVEL == 1 && E <= 512;
+  static constexpr uint32_t TW_ = HT16 ? kHashSize / 2u : kHashSize;  // table words
   static constexpr uint32_t R =
       LAZY ? ((LZ_R + 3u) & ~3u)
-           : (cmax(cmax(SEARCH, LEVEL ? (XL ? 2u : 1u) * E + kHashSize : 0u), RP) + 3u) & ~3u;
+           : (cmax(cmax(SEARCH, LEVEL ? (XL ? 2u : 1u) * E + TW_ : 0u), RP) + 3u) & ~3u;
   static constexpr uint32_t MISC = (LAZY && WPC_ == 1u) ? 0u : 2u * (E / 64u + 1u) + 8u;
   // 32 zero words ahead of X (32-offset window): every lane of the offset-mask
   // pass loads its 32 + 8 words with the same 16-byte loads, the first lanes'
@@ -317,7 +321,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
   uint32_t* LV = X + L::XW;  // X and S_1 share their words unless X has its own region
   // level 1: the words for the candidate checks (its own region, or loaded
   // again behind the hash table)
-  uint32_t* XL = L::XL ? LV + E + kHashSize : X;
+  uint32_t* XL = L::XL ? LV + E + L::TW_ : X;
   Mask* LVm = (Mask*)LV;  // the search tables
   uint32_t* LO = L::LAZY ? LV + L::LZ_T4 : LV;  // LAZY: LOX
   uint32_t* XQ = LV + E;                         // not LAZY: exit | item-start bits << 16
@@ -624,7 +628,8 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
       bool matched = true;
       if (LEVEL == 1) {
         bool hit = false;
-        for (uint32_t i = g; i < kHashSize; i += TL) T[i] = 0u;
+        uint16_t* T16 = (uint16_t*)T;
+        for (uint32_t i = g; i < L::TW_; i += TL) T[i] = 0u;
         if constexpr (L::XL) {
 #pragma unroll
           for (uint32_t i = 0; i < PPL; ++i) XL[g + i * TL] = xr[i];
@@ -651,7 +656,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             uint32_t o = 0, Lnear = 0, lim = 0;
             bool need = false;
             if (ins) {
-              const uint32_t v = T[bk];
+              const uint32_t v = L::HT16 ? (uint32_t)T16[bk] : T[bk];
               o = p - (v - 1u);  // entries come from earlier sub-blocks: o >= 1
               lim = (uint32_t)E - p < kMaxLen ? (uint32_t)E - p : kMaxLen;
               Lnear = LO[p] & 0xFFu;
@@ -705,8 +710,24 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             }
           }
           team_sync<WPC>();
-          if (ins) atomicMax(&T[bk], p + 1u);
-          team_sync<WPC>();
+          if constexpr (L::HT16) {
+            // every insert of this sub-block is larger than anything stored
+            // before, so the bucket must end with the largest of them: plain
+            // 16-bit stores, then whoever still sees a smaller value stores
+            // again until nobody does (the same result as atomicMax)
+            if (ins) T16[bk] = (uint16_t)(p + 1u);
+            team_sync<WPC>();
+            while (true) {
+              const bool lose = ins && (uint32_t)T16[bk] < p + 1u;
+              const bool again = WPC == 1 ? __ballot(lose) != 0ull : __syncthreads_or(lose);
+              if (!again) break;
+              if (lose) T16[bk] = (uint16_t)(p + 1u);
+              team_sync<WPC>();
+            }
+          } else {
+            if (ins) atomicMax(&T[bk], p + 1u);
+            team_sync<WPC>();
+          }
         }
         if (WPC == 1) matched = near || __ballot(hit) != 0ull;
         else matched = near || __syncthreads_or(hit);
