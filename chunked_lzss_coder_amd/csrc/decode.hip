@@ -364,10 +364,11 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
   const uint32_t nit = k0 < NI ? (NI - k0 < R ? NI - k0 : R) : 0u;
   uint32_t fb = 0;  // this lane's flag bits, item k0 in bit 0
   if (nit) {
-    const uint32_t b0 = k0 >> 3;
-#pragma unroll
-    for (uint32_t b = 0; b < 4u; ++b)
-      if (b0 + b < F) fb |= (uint32_t)FL[b0 + b] << (8u * b);
+    // flag bytes k0 / 8 .. + 3 from the two aligned LDS dwords holding them
+    // (bytes past the F flag bytes land in bits past nit, masked off)
+    const uint32_t fa = (uint32_t)(FL - PB) + (k0 >> 3);
+    const uint32_t* fw = (const uint32_t*)(PB + (fa & ~3u));
+    fb = __builtin_amdgcn_alignbyte(fw[1], fw[0], fa & 3u);
     fb = (fb >> (k0 & 7u)) & ((1u << nit) - 1u);
   }
   uint32_t mt_total;
@@ -654,7 +655,8 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
 template <uint32_t CS, uint32_t WS, bool TEAMS>
 __device__ __forceinline__ void decode_group_teams(const DecP& p, const uint8_t* in, const uint8_t* lim, uint8_t* out,
                                                    const uint32_t* loc, const uint64_t* tile_sum, uint32_t* status,
-                                                   uint64_t* out_bytes, uint8_t* arena_all, uint32_t* sh) {
+                                                   uint64_t* out_bytes, uint8_t* arena_all, uint32_t* sh,
+                                                   uint64_t pre) {
   using G = Geo<CS, WS, TEAMS>;
   constexpr uint32_t TL = G::TL;
   constexpr uint32_t CPW = kWaves / G::TW;  // chunks per workgroup
@@ -675,17 +677,12 @@ __device__ __forceinline__ void decode_group_teams(const DecP& p, const uint8_t*
   const uint64_t stride = (uint64_t)grid * CPW;
   const uint64_t c0 = (uint64_t)blockIdx.x * CPW + team;
   const uint32_t lane = lane_id();
-  uint64_t pre = 0;
-  if (p.ntiles <= 64u) {
-    const uint64_t v = lane < p.ntiles ? tile_sum[lane] : 0ull;
-    pre = wave_incl_add64(v) - v;
-  }
   uint2 me = make_uint2(0u, 0u);
   uint64_t moff = 0;
   auto batch = [&](uint64_t k0) {
     const uint64_t cc = c0 + (k0 + lane) * stride;
     const bool live = cc < p.nc;
-    const uint32_t t = live ? (uint32_t)(cc / p.T) : 0u;
+    const uint32_t t = live ? (uint32_t)(cc >> __builtin_ctz(p.T)) : 0u;
     const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((t & 63u) << 2), (int)(uint32_t)pre);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((t & 63u) << 2), (int)(uint32_t)(pre >> 32));
     uint64_t tp = (uint64_t)lo | ((uint64_t)hi << 32);
@@ -737,26 +734,26 @@ __device__ __forceinline__ void decode_group_teams(const DecP& p, const uint8_t*
 template <uint32_t CS, uint32_t WS>
 __device__ __forceinline__ void decode_group(const DecP& p, const uint8_t* in, const uint8_t* lim, uint8_t* out,
                              const uint32_t* loc, const uint64_t* tile_sum, uint32_t* status, uint64_t* out_bytes,
-                             uint8_t* arena_all, uint32_t* sh) {
+                             uint8_t* arena_all, uint32_t* sh, uint64_t pre) {
   // Chunks that fit one slot only with the payload over the values go one
   // per wave when there are enough of them to keep every CU busy; a small
   // stream decodes faster with a workgroup per chunk.
   if constexpr (Geo<CS, WS>::OVL) {
     if (p.nc >= kOneWaveMinChunks) {
-      decode_group_teams<CS, WS, false>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena_all, sh);
+      decode_group_teams<CS, WS, false>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena_all, sh, pre);
       return;
     }
   }
-  decode_group_teams<CS, WS, true>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena_all, sh);
+  decode_group_teams<CS, WS, true>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena_all, sh, pre);
 }
 
 template <uint32_t CS>
 __device__ __forceinline__ void decode_by_ws(const DecP& p, const uint8_t* in, const uint8_t* lim, uint8_t* out,
                              const uint32_t* loc, const uint64_t* tile_sum, uint32_t* status, uint64_t* out_bytes,
-                             uint8_t* arena, uint32_t* sh) {
-  if (p.ws == 4u) decode_group<CS, 4>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh);
-  else if (p.ws == 2u) decode_group<CS, 2>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh);
-  else decode_group<CS, 1>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh);
+                             uint8_t* arena, uint32_t* sh, uint64_t pre) {
+  if (p.ws == 4u) decode_group<CS, 4>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh, pre);
+  else if (p.ws == 2u) decode_group<CS, 2>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh, pre);
+  else decode_group<CS, 1>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh, pre);
 }
 
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(7))) void chunks_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes,
@@ -768,8 +765,18 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(7))) voi
                                                         uint64_t* __restrict__ out_bytes) {
   __shared__ __attribute__((aligned(16))) uint8_t arena[kArena];
   __shared__ uint32_t sh[2 * kWaves];
+  // the first 64 tile totals (the workspace holds at least that many slots),
+  // loaded before the parameters so that the two loads overlap
+  const uint64_t ts_lane = tile_sum[lane_id()];
   const DecP p = *P;
   if (p.status != kStatusOk) return;
+  // lane t: the payload bytes of the tiles before tile t (streams of up to
+  // 64 tiles; larger ones add the totals per chunk)
+  uint64_t pre = 0;
+  if (p.ntiles <= 64u) {
+    const uint64_t v = lane_id() < p.ntiles ? ts_lane : 0ull;
+    pre = wave_incl_add64(v) - v;
+  }
   if (blockIdx.x == 0 && threadIdx.x < 64u) {
     // stream-wide checks: the tile totals must add up to the header's payload
     // size and no row may be invalid
@@ -785,9 +792,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(7))) voi
   }
   const uint8_t* lim = in + in_bytes;
   // the header kernel accepted cs and ws, so they are among these
-  if (p.cs == 1024u) decode_by_ws<1024>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh);
-  else if (p.cs == 2048u) decode_by_ws<2048>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh);
-  else decode_by_ws<4096>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh);
+  if (p.cs == 1024u) decode_by_ws<1024>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh, pre);
+  else if (p.cs == 2048u) decode_by_ws<2048>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh, pre);
+  else decode_by_ws<4096>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh, pre);
 }
 
 // ---- split mode ------------------------------------------------------------------
@@ -915,7 +922,7 @@ __device__ __forceinline__ void decode_group_split(const DecP& p, const SplitDec
     uint32_t fz, lz, mz;
     if (!split_sizes(e, bc, CS, WS, &fz, &lz, &mz)) continue;  // reported by the scan kernel
     // offsets: earlier tiles' totals + offsets within the tile, for each port
-    const uint32_t t = (uint32_t)(c / p.T);
+    const uint32_t t = (uint32_t)(c >> __builtin_ctz(p.T));
     uint64_t pre[3];
 #pragma unroll
     for (uint32_t q = 0; q < 3u; ++q) {
@@ -1022,7 +1029,7 @@ __global__ __launch_bounds__(kBlock) void serial_chunks_kernel(const uint8_t* __
     const uint32_t bc = (uint32_t)((p.n - start) < cs ? (p.n - start) : cs);
     if (!row_ok(e, bc)) continue;  // reported by the scan kernel
     const uint32_t size = entry_payload(e.x, e.y);
-    const uint32_t t = (uint32_t)(c / p.T);
+    const uint32_t t = (uint32_t)(c >> __builtin_ctz(p.T));
     uint64_t off = loc[c];
     for (uint32_t i = 0; i < t; ++i) off += tile_sum[i];
     if (off + size > p.pb) continue;  // reported by the tile-total check

@@ -18,13 +18,12 @@ constexpr uint32_t kTileMax = 1u << 20;  // at most (offsets within a tile < 2^3
 constexpr uint32_t kMaxTiles = 64;       // tiles wanted (one tile total per lane)
 constexpr uint32_t kWorkspaceTilesMin = 256;
 
-// Chunks per scan tile for a stream of nc chunks: about nc / kMaxTiles, a
-// multiple of kTileMin, within [kTileMin, kTileMax].
+// Chunks per scan tile for a stream of nc chunks: the smallest power of two
+// from kTileMin up to kTileMax with nc <= kMaxTiles * T (kTileMax if none), so
+// a chunk's tile is its index shifted right.
 __host__ __device__ inline uint32_t scan_tile_chunks(uint64_t nc) {
-  uint64_t T = (nc + kMaxTiles - 1u) / kMaxTiles;
-  T = (T + kTileMin - 1u) / kTileMin * kTileMin;
-  if (T < kTileMin) T = kTileMin;
-  if (T > kTileMax) T = kTileMax;
+  uint64_t T = kTileMin;
+  while (T < kTileMax && T * kMaxTiles < nc) T <<= 1;
   return (uint32_t)T;
 }
 

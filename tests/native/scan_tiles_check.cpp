@@ -18,7 +18,8 @@ static void check(uint64_t nc, uint64_t cap) {
   const uint32_t t = scan_tiles(nc), g = scan_groups(cap), w = workspace_tiles(cap);
   const uint32_t T = scan_tile_chunks(nc);
   const bool tiles_cover = (uint64_t)t * T >= nc && (t == 0 || (uint64_t)(t - 1) * T < nc);
-  if (t > g || t > w || g == 0 || !tiles_cover || T % kTileMin != 0 || T < kTileMin || T > kTileMax) {
+  if (t > g || t > w || g == 0 || !tiles_cover || T % kTileMin != 0 || T < kTileMin || T > kTileMax ||
+      (T & (T - 1u)) != 0 || (T < kTileMax && (uint64_t)T * kMaxTiles < nc)) {
     if (bad < 20) std::printf("nc=%llu cap=%llu tiles=%u groups=%u slots=%u T=%u\n", (unsigned long long)nc,
                               (unsigned long long)cap, t, g, w, T);
     ++bad;
