@@ -270,16 +270,15 @@ struct Lay {
   //       on, the position's segment exit in the high half
   //   IM  [2E + 28, 2E + 28 + E/4) the item-start bits of the segment walk
   //       from each position, a byte each
-  //   ISB | LMB (E/32 each, teams of several waves only)
-  // Teams of one wave keep the item bits and counts in registers and need no
-  // further words, so a two-chunk workgroup of 512-element chunks takes
-  // under 10 KB of LDS.
+  //   ISB | LMB (E/32 each) the item-start and match bits of each segment,
+  //       a byte each
+  // so a two-chunk workgroup of 512-element chunks takes under 10 KB of LDS.
   static constexpr bool LAZY = LEVEL == 0 && W == 32 && E <= 1024;
   static constexpr uint32_t WPC_ = E <= 512 ? 1u : (uint32_t)E / 512u;  // waves per chunk (launch_one)
   static constexpr uint32_t LZ_T4 = E + 16u;
   static constexpr uint32_t LZ_IM = 2u * E + 28u;
   static constexpr uint32_t LZ_ISB = LZ_IM + E / 4u;
-  static constexpr uint32_t LZ_R = LZ_ISB + (WPC_ > 1u ? 2u * (E / 32u) : 0u);
+  static constexpr uint32_t LZ_R = LZ_ISB + 2u * (E / 32u);
   static_assert(!LAZY || CS / 4u + 4u <= E + 16u, "payload staging fits over S_1");
   // level 1 with chunks of up to 512 elements: 16-bit buckets (positions + 1
   // fit), half the table's LDS, so half again as many chunks per CU
@@ -402,8 +401,9 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
   }
 
   uint32_t K = 0, M = 0;
-  uint64_t isw[WPC == 1 ? NR : 1], lmw[WPC == 1 ? NR : 1];  // item / match-capable bits (one wave)
-  uint32_t kb[WPC == 1 ? NR : 1], mb[WPC == 1 ? NR : 1];
+  // segment g's item-start and match bits, and the items (low half) and
+  // matches (high half) of the segments before it
+  uint32_t it8 = 0, mt8 = 0, kex = 0;
   if (nonzero) {
     // ---- 2. omask: 8 consecutive positions per lane, window in registers -------------
     Mask any_om = 0;  // OR of this lane's masks
@@ -778,10 +778,8 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             *(uint4*)(XQ + p0 + 4) = make_uint4(ex[4] | (im[4] << 16), ex[5] | (im[5] << 16),
                                                 ex[6] | (im[6] << 16), ex[7] | (im[7] << 16));
           }
-          if (WPC > 1) {
-            ((uint8_t*)LMB)[sg] = (uint8_t)lmb;
-            ((uint8_t*)ISB)[sg] = 0;
-          }
+          ((uint8_t*)LMB)[sg] = (uint8_t)lmb;
+          if (WPC > 1) ((uint8_t*)ISB)[sg] = 0;
         }
         team_sync<WPC>();
         // (b) hops: the parse's real entry into every segment it passes through
@@ -793,7 +791,6 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
           for (uint32_t i = 0; i < NR; ++i) {
             const uint32_t p = 64u * i + lane;
             xqr[i] = xq_at(p);
-            lmw[i] = __ballot((LO[p] & 0xFFu) >= MM);
           }
           // The walk only records where it enters each segment (one scalar
           // bit per hop); each segment's item starts are then read from its
@@ -820,16 +817,10 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             const uint32_t se = (uint32_t)(ent >> sb) & 0xFFu;
             const uint32_t q0 = se ? (uint32_t)__builtin_ctz(se) : 0u;
             const uint32_t xe = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((sb + q0) << 2), (int)xqr[i]);
-            isw[i] = __ballot(se != 0u && ((xe >> (16u + (lane & 7u))) & 1u));
+            // the segment's item-start bits: those of its walk from the entry
+            if ((lane & 7u) == 0u) ((uint8_t*)ISB)[8u * i + (lane >> 3)] = se ? (uint8_t)(xe >> 16) : (uint8_t)0;
           }
-          // ---- 6. counts -------------------------------------------------------------------
-#pragma unroll
-          for (uint32_t i = 0; i < NR; ++i) {
-            kb[i] = K;
-            mb[i] = M;
-            K += (uint32_t)__builtin_popcountll(isw[i]);
-            M += (uint32_t)__builtin_popcountll(isw[i] & lmw[i]);
-          }
+          wave_sync();
         } else {
           if constexpr (WPC < 4) {
             // two waves: the first wave hops word by word (the other's chunk
@@ -925,38 +916,35 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             }
             team_sync<WPC>();
           }
-          // ---- 6. counts (first wave) --------------------------------------------------------
-          const uint64_t* IS64 = (const uint64_t*)ISB;
-          const uint64_t* LM64 = (const uint64_t*)LMB;
-          if (g < 64u) {
-            uint32_t kc = 0, mc = 0;
-            if (g < NR) {
-              const uint64_t is = IS64[g];
-              kc = __builtin_popcountll(is);
-              mc = __builtin_popcountll(is & LM64[g]);
-            }
-            uint32_t ki = kc, mi = mc;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-              const uint32_t a = __shfl_up(ki, d, 64), b = __shfl_up(mi, d, 64);
-              if (lane >= (uint32_t)d) {
-                ki += a;
-                mi += b;
-              }
-            }
-            if (g < NR) {
-              KB[g] = ki - kc;
-              MB[g] = mi - mc;
-            }
-            if (g == NR - 1u) {
-              SC[1] = ki;
-              SC[2] = mi;
-            }
-          }
-          team_sync<WPC>();
-          K = SC[1];
-          M = SC[2];
         }
+        // ---- 6. counts: lane g takes segment g (there are never more
+        // segments than lanes); one packed scan gives the items and matches
+        // of the segments before it and the chunk's totals
+        static_assert(L::NSEG <= TL, "a segment per lane");
+        it8 = g < L::NSEG ? (uint32_t)((const uint8_t*)ISB)[g] : 0u;
+        mt8 = g < L::NSEG ? (uint32_t)((const uint8_t*)LMB)[g] & it8 : 0u;
+        const uint32_t cnt = (uint32_t)__builtin_popcount(it8) | ((uint32_t)__builtin_popcount(mt8) << 16);
+        const uint32_t inc = wave_incl_add(cnt);
+        uint32_t tot;
+        if constexpr (WPC == 1) {
+          tot = lane63(inc);
+          kex = inc - cnt;
+        } else {
+          const uint32_t wv = g >> 6;
+          if (lane == 63u) KB[wv] = inc;
+          team_sync<WPC>();
+          uint32_t pre = 0;
+          tot = 0;
+#pragma unroll
+          for (uint32_t w = 0; w < (uint32_t)WPC; ++w) {
+            const uint32_t t = KB[w];
+            pre += w < wv ? t : 0u;
+            tot += t;
+          }
+          kex = pre + inc - cnt;
+        }
+        K = tot & 0xFFFFu;
+        M = tot >> 16;
       }  // some match
     }  // near match, or level 1
   }  // nonzero
@@ -975,69 +963,82 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
   uint32_t* STG32 = (uint32_t*)STG;
   uint32_t* slot = (uint32_t*)(staging + base);
   if (nonzero && !raw) {
-    // this lane's literal words: from X's own region, else from the input
-    // (loaded here so the loads overlap the flag bitmap's construction)
-    uint32_t xv[PPL];
-#pragma unroll
-    for (uint32_t i = 0; i < PPL; ++i) {
-      const uint32_t p = WPC == 1 ? 64u * i + lane : g + i * TL;
-      xv[i] = L::XW ? X[p] : word_at(p);
-    }
+    // Lane g places the items of segment g (positions 8g .. 8g + 7): they are
+    // items kex.lo .. of the chunk and their data bytes are consecutive.  The
+    // segment's (L, O) and literal words are loaded before the flag words are
+    // cleared, so the loads overlap.
     const uint32_t DB = (F + 3u) & ~3u;
     const uint32_t S0 = DB - F;  // payload byte 0 is STG byte S0
+    const uint32_t p0 = 8u * g;
+    uint32_t lo8[8], xw[8];
+#pragma unroll
+    for (uint32_t q = 0; q < 8u; ++q) lo8[q] = xw[q] = 0u;
+    if (g < L::NSEG) {
+      const uint4 a = *(const uint4*)(LO + p0), b = *(const uint4*)(LO + p0 + 4u);
+      lo8[0] = a.x, lo8[1] = a.y, lo8[2] = a.z, lo8[3] = a.w, lo8[4] = b.x, lo8[5] = b.y, lo8[6] = b.z, lo8[7] = b.w;
+      if constexpr (L::XW != 0u) {  // the words in their own region
+        const uint4 u = *(const uint4*)(X + p0), v = *(const uint4*)(X + p0 + 4u);
+        xw[0] = u.x, xw[1] = u.y, xw[2] = u.z, xw[3] = u.w, xw[4] = v.x, xw[5] = v.y, xw[6] = v.z, xw[7] = v.w;
+      } else if (bc == CS && (((uintptr_t)src) & 15u) == 0u) {  // from the input, 8 WS bytes at once
+        if constexpr (WS == 4) {
+          const uint4 u = ((const uint4*)src)[2u * g], v = ((const uint4*)src)[2u * g + 1u];
+          xw[0] = u.x, xw[1] = u.y, xw[2] = u.z, xw[3] = u.w, xw[4] = v.x, xw[5] = v.y, xw[6] = v.z, xw[7] = v.w;
+        } else if constexpr (WS == 2) {
+          const uint4 u = ((const uint4*)src)[g];
+          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (uint32_t j = 0; j < 4u; ++j) {
+            xw[2u * j] = w4[j] & 0xFFFFu;
+            xw[2u * j + 1u] = w4[j] >> 16;
+          }
+        } else {
+          const uint2 u = ((const uint2*)src)[g];
+#pragma unroll
+          for (uint32_t j = 0; j < 4u; ++j) {
+            xw[j] = (u.x >> (8u * j)) & 0xFFu;
+            xw[4u + j] = (u.y >> (8u * j)) & 0xFFu;
+          }
+        }
+      } else {
+#pragma unroll
+        for (uint32_t q = 0; q < 8u; ++q) xw[q] = word_at(p0 + q);
+      }
+    }
     for (uint32_t i = g; i < DB / 4u; i += TL) STG32[i] = 0u;
     team_sync<WPC>();
     // item k: flag bit 8 S0 + k of STG; data bytes at DB + WS (k - m) + 2 m
     // (m = matches before it)
-    auto put_item = [&](bool match, uint32_t k, uint32_t m, uint32_t lo_v, uint32_t x) {
+    const uint32_t k0 = kex & 0xFFFFu;
+    uint32_t k = k0, m = kex >> 16, fl = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < 8u; ++q) {
+      if (!((it8 >> q) & 1u)) continue;
+      const bool mt = (mt8 >> q) & 1u;
       const uint32_t off = DB + (uint32_t)WS * (k - m) + 2u * m;
-      if (match) {
-        const uint32_t fb = 8u * S0 + k;
-        atomicOr(&STG32[fb >> 5], 1u << (fb & 31u));
+      if (mt) {
+        fl |= 1u << (k - k0);
         if (WS >= 2) {
-          *(uint16_t*)(STG + off) = (uint16_t)lo_v;
+          *(uint16_t*)(STG + off) = (uint16_t)lo8[q];
         } else {
-          STG[off] = (uint8_t)lo_v;
-          STG[off + 1] = (uint8_t)(lo_v >> 8);
+          STG[off] = (uint8_t)lo8[q];
+          STG[off + 1] = (uint8_t)(lo8[q] >> 8);
         }
       } else if (WS == 4) {
-        *(uint16_t*)(STG + off) = (uint16_t)x;
-        *(uint16_t*)(STG + off + 2) = (uint16_t)(x >> 16);
+        *(uint16_t*)(STG + off) = (uint16_t)xw[q];
+        *(uint16_t*)(STG + off + 2) = (uint16_t)(xw[q] >> 16);
       } else if (WS == 2) {
-        *(uint16_t*)(STG + off) = (uint16_t)x;
+        *(uint16_t*)(STG + off) = (uint16_t)xw[q];
       } else {
-        STG[off] = (uint8_t)x;
+        STG[off] = (uint8_t)xw[q];
       }
-    };
-    if constexpr (WPC == 1) {
-      uint32_t lov[NR];  // every position's (L, O), loaded before any item is placed
-#pragma unroll
-      for (uint32_t i = 0; i < NR; ++i) lov[i] = LO[64u * i + lane];
-#pragma unroll
-      for (uint32_t i = 0; i < NR; ++i) {
-        const uint64_t is = isw[i], ms = is & lmw[i];
-        if (!((is >> lane) & 1ull)) continue;
-        const bool mt = (ms >> lane) & 1ull;
-        put_item(mt, kb[i] + mbcnt64(is), mb[i] + mbcnt64(ms), lov[i], xv[i]);
-      }
-    } else {
-      const uint64_t* IS64 = (const uint64_t*)ISB;
-      const uint64_t* LM64 = (const uint64_t*)LMB;
-      uint32_t lov[PPL];  // every position's (L, O), loaded before any item is placed
-#pragma unroll
-      for (uint32_t i = 0; i < PPL; ++i) lov[i] = LO[g + i * TL];
-#pragma unroll
-      for (uint32_t i = 0; i < PPL; ++i) {
-        const uint32_t p = g + i * TL;
-        const uint32_t wi = p >> 6;
-        const uint64_t is = IS64[wi], ms = is & LM64[wi];
-        const uint64_t bit = 1ull << (p & 63u);
-        if (!(is & bit)) continue;
-        const uint64_t below = bit - 1ull;
-        const bool mt = (ms & bit) != 0ull;
-        put_item(mt, KB[wi] + (uint32_t)__builtin_popcountll(is & below),
-                 MB[wi] + (uint32_t)__builtin_popcountll(ms & below), lov[i], xv[i]);
-      }
+      ++k;
+      m += mt ? 1u : 0u;
+    }
+    // the segment's flag bits (at most 8, in item order) into the bitmap
+    if (fl) {
+      const uint32_t fb = 8u * S0 + k0, sh = fb & 31u;
+      atomicOr(&STG32[fb >> 5], fl << sh);
+      if (sh > 24u && (fl >> (32u - sh)) != 0u) atomicOr(&STG32[(fb >> 5) + 1u], fl >> (32u - sh));
     }
     team_sync<WPC>();
     const uint32_t nd = (F + D + 3u) / 4u;
