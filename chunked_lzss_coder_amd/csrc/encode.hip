@@ -1007,32 +1007,35 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
     for (uint32_t i = g; i < DB / 4u; i += TL) STG32[i] = 0u;
     team_sync<WPC>();
     // item k: flag bit 8 S0 + k of STG; data bytes at DB + WS (k - m) + 2 m
-    // (m = matches before it)
-    const uint32_t k0 = kex & 0xFFFFu;
-    uint32_t k = k0, m = kex >> 16, fl = 0;
+    // (m = matches before it).  The segment's items are consecutive, so its
+    // data pointer and item count just advance.
+    const uint32_t k0 = kex & 0xFFFFu, m0 = kex >> 16;
+    uint8_t* dp = STG + DB + (uint32_t)WS * (k0 - m0) + 2u * m0;
+    uint32_t j = 0, fl = 0;
 #pragma unroll
     for (uint32_t q = 0; q < 8u; ++q) {
       if (!((it8 >> q) & 1u)) continue;
-      const bool mt = (mt8 >> q) & 1u;
-      const uint32_t off = DB + (uint32_t)WS * (k - m) + 2u * m;
-      if (mt) {
-        fl |= 1u << (k - k0);
+      if ((mt8 >> q) & 1u) {
+        fl |= 1u << j;
         if (WS >= 2) {
-          *(uint16_t*)(STG + off) = (uint16_t)lo8[q];
+          *(uint16_t*)dp = (uint16_t)lo8[q];
         } else {
-          STG[off] = (uint8_t)lo8[q];
-          STG[off + 1] = (uint8_t)(lo8[q] >> 8);
+          dp[0] = (uint8_t)lo8[q];
+          dp[1] = (uint8_t)(lo8[q] >> 8);
         }
-      } else if (WS == 4) {
-        *(uint16_t*)(STG + off) = (uint16_t)xw[q];
-        *(uint16_t*)(STG + off + 2) = (uint16_t)(xw[q] >> 16);
-      } else if (WS == 2) {
-        *(uint16_t*)(STG + off) = (uint16_t)xw[q];
+        dp += 2;
       } else {
-        STG[off] = (uint8_t)xw[q];
+        if (WS == 4) {
+          *(uint16_t*)dp = (uint16_t)xw[q];
+          *(uint16_t*)(dp + 2) = (uint16_t)(xw[q] >> 16);
+        } else if (WS == 2) {
+          *(uint16_t*)dp = (uint16_t)xw[q];
+        } else {
+          dp[0] = (uint8_t)xw[q];
+        }
+        dp += WS;
       }
-      ++k;
-      m += mt ? 1u : 0u;
+      ++j;
     }
     // the segment's flag bits (at most 8, in item order) into the bitmap
     if (fl) {
