@@ -276,10 +276,6 @@ struct SplitSrc {
   const uint8_t* lit;    // its K - M literal words
   const uint8_t* lens;   // its M match lengths
   const uint8_t* offs;   // its M match offsets
-  const uint8_t* meta_lim;
-  const uint8_t* lit_lim;
-  const uint8_t* lens_lim;
-  const uint8_t* offs_lim;
   uint32_t K, M;
 };
 
@@ -331,10 +327,39 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
   const uint32_t NL = SPLIT ? sp.K - sp.M : 0u;  // split: literal words
   if constexpr (SPLIT) {
     const uint32_t lo = (F + 3u) & ~3u, mo = (lo + WS * NL + 3u) & ~3u, oo = (mo + sp.M + 3u) & ~3u;
-    stage(0u, sp.flags, F, sp.meta_lim);
-    stage(lo, sp.lit, WS * NL, sp.lit_lim);
-    stage(mo, sp.lens, sp.M, sp.lens_lim);
-    stage(oo, sp.offs, sp.M, sp.offs_lim);
+    // the four regions in one pass, so their loads are in flight together:
+    // dword i of PB belongs to the region whose dword range holds it (the
+    // gaps between regions get zeros); a region's reads stop at its own
+    // last byte (aligned dwords holding a byte of it, so no read leaves the
+    // pages its bytes lie in)
+    const uint32_t d1 = lo >> 2, d2 = mo >> 2, d3 = oo >> 2;
+    const uint32_t e0 = (F + 3u) >> 2, e1 = d1 + ((WS * NL + 3u) >> 2), e2 = d2 + ((sp.M + 3u) >> 2),
+                   e3 = d3 + ((sp.M + 3u) >> 2);
+#pragma unroll 1
+    for (uint32_t i0 = 0; i0 < e3; i0 += 4u * TL) {
+      uint32_t v[4];
+#pragma unroll
+      for (uint32_t r = 0; r < 4u; ++r) {
+        const uint32_t i = i0 + g + r * TL;
+        const uint8_t* src = nullptr;
+        uint32_t len = 0, b = 0;
+        if (i < e0) {
+          src = sp.flags, len = F, b = i;
+        } else if (i >= d1 && i < e1) {
+          src = sp.lit, len = WS * NL, b = i - d1;
+        } else if (i >= d2 && i < e2) {
+          src = sp.lens, len = sp.M, b = i - d2;
+        } else if (i >= d3 && i < e3) {
+          src = sp.offs, len = sp.M, b = i - d3;
+        }
+        v[r] = src ? load4_unaligned(src + 4u * b, src + len) : 0u;
+      }
+#pragma unroll
+      for (uint32_t r = 0; r < 4u; ++r) {
+        const uint32_t i = i0 + g + r * TL;
+        if (i < e3) ((uint32_t*)PB)[i] = v[r];
+      }
+    }
     FL = PB;
     LITB = PB + lo;
     LENB = PB + mo;
@@ -913,44 +938,65 @@ __device__ __forceinline__ void decode_group_split(const DecP& p, const SplitDec
   const uint32_t team = threadIdx.x / TL, g = threadIdx.x % TL, lane = lane_id();
   uint8_t* arena = arena_all + team * (G::TW * kSlot);
   const uint8_t* flags = a.meta + p.base;
-  const uint8_t* meta_lim = a.meta + a.meta_bytes;
   const uint64_t stride = (uint64_t)gridDim.x * CPW;
-  for (uint64_t c = (uint64_t)blockIdx.x * CPW + team; c < p.nc; c += stride) {
-    const uint2 e = read_row(a.meta, c);
+  const uint64_t c0 = (uint64_t)blockIdx.x * CPW + team;
+  // The metadata of 64 of the team's chunks (entry and the three port
+  // offsets) is loaded at once, one chunk per lane, and handed out by
+  // readlane, as in the one-stream decode.  A port offset is the bytes of
+  // that port in the earlier tiles plus the offset within the tile.
+  uint2 me = make_uint2(0u, 0u);
+  uint64_t mo[3] = {0ull, 0ull, 0ull};
+  auto batch = [&](uint64_t k0) {
+    const uint64_t cc = c0 + (k0 + lane) * stride;
+    const bool live = cc < p.nc;
+    const uint32_t t = live ? (uint32_t)(cc >> __builtin_ctz(p.T)) : 0u;
+    me = live ? read_row(a.meta, cc) : make_uint2(0u, 0u);
+#pragma unroll
+    for (uint32_t q = 0; q < 3u; ++q) {
+      const uint64_t* ts = tile_sum + (uint64_t)q * kMaxTilesAlloc;
+      uint64_t tp = 0;
+      if (p.ntiles <= 64u) {  // lane i: the tiles before tile i, handed to each chunk's lane
+        const uint64_t v = lane < p.ntiles ? ts[lane] : 0ull;
+        const uint64_t pr = wave_incl_add64(v) - v;
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((t & 63u) << 2), (int)(uint32_t)pr);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((t & 63u) << 2), (int)(uint32_t)(pr >> 32));
+        tp = (uint64_t)lo | ((uint64_t)hi << 32);
+      } else if (live) {  // huge streams only: this lane adds the earlier tiles itself
+        for (uint32_t i = 0; i < t; ++i) tp += ts[i];
+      }
+      mo[q] = live ? tp + loc[(uint64_t)q * a.chunks_cap + cc] : 0ull;
+    }
+  };
+  for (uint64_t k = 0;; ++k) {
+    const uint64_t c = c0 + k * stride;
+    if (c >= p.nc) break;
+    if ((k & 63u) == 0u) batch(k);
+    const int j = (int)(k & 63u);
+    const uint2 e = make_uint2((uint32_t)__builtin_amdgcn_readlane((int)me.x, j),
+                               (uint32_t)__builtin_amdgcn_readlane((int)me.y, j));
+    uint64_t pre[3];
+#pragma unroll
+    for (uint32_t q = 0; q < 3u; ++q)
+      pre[q] = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mo[q], j) |
+               ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mo[q] >> 32), j) << 32);
     const uint64_t start = c * CS;
     const uint32_t bc = (uint32_t)((p.n - start) < CS ? (p.n - start) : CS);
     uint32_t fz, lz, mz;
     if (!split_sizes(e, bc, CS, WS, &fz, &lz, &mz)) continue;  // reported by the scan kernel
-    // offsets: earlier tiles' totals + offsets within the tile, for each port
-    const uint32_t t = (uint32_t)(c >> __builtin_ctz(p.T));
-    uint64_t pre[3];
-#pragma unroll
-    for (uint32_t q = 0; q < 3u; ++q) {
-      uint64_t s = 0;
-      for (uint32_t i = lane; i < t; i += 64u) s += tile_sum[(uint64_t)q * kMaxTilesAlloc + i];
-      pre[q] = lane63_64(wave_incl_add64(s)) + loc[(uint64_t)q * a.chunks_cap + c];
-    }
     // sizes inconsistent with the ports: reported by workgroup 0 below
     if (pre[0] + fz > p.pb || pre[1] + lz > a.lit_bytes || pre[2] + mz > a.tok_bytes) continue;
     uint8_t* dst = a.out + start;
     if (e.x == 0u) {
-      const bool zero = e.y == 0u;
-      const bool al = (((uintptr_t)dst) & 3u) == 0;
-      const uint8_t* src = a.lit + pre[1];
-      const uint8_t* lim = a.lit + a.lit_bytes;
-      const uint32_t nw = (bc + 3u) / 4u;
-      for (uint32_t i = g; i < nw; i += TL) {
-        const uint32_t v = zero ? 0u : load4_unaligned(src + 4u * i, lim);
-        if (al && 4u * i + 4u <= bc) {
-          *(uint32_t*)(dst + 4u * i) = v;
-        } else {
-          for (uint32_t b = 0; b < 4u; ++b)
-            if (4u * i + b < bc) dst[4u * i + b] = (uint8_t)(v >> (8u * b));
-        }
-      }
+      // zero or raw chunk: each wave of the team fills or copies its share
+      // (whole 16-byte blocks but the last), one block per lane per round
+      constexpr uint32_t TW = G::TW;
+      const uint32_t share = ((bc + 16u * TW - 1u) / (16u * TW)) * 16u;
+      const uint32_t w0 = (g >> 6) * share;
+      const uint32_t len = w0 < bc ? (bc - w0 < share ? bc - w0 : share) : 0u;
+      if (e.y == 0u) zero_bytes16(dst + w0, len, lane);
+      else copy_bytes16_r1(dst + w0, a.lit + pre[1] + w0, len, lane);
     } else {
-      const SplitSrc sp{flags + pre[0], a.lit + pre[1], a.lens + pre[2], a.offs + pre[2], meta_lim,
-                        a.lit + a.lit_bytes, a.lens + a.tok_bytes, a.offs + a.tok_bytes, e.x, e.y};
+      const SplitSrc sp{flags + pre[0], a.lit + pre[1], a.lens + pre[2], a.offs + pre[2], e.x, e.y};
       if (!decode_coded<CS, WS, true>(nullptr, nullptr, 0u, 0u, bc, dst, arena, sh, sp) && g == 0)
         raise_status(a.status, a.out_bytes, kStatusCorrupt);
     }
