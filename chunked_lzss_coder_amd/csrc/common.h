@@ -345,8 +345,6 @@ struct DecodeArgs {
   hipEvent_t ev_start;  // optional, recorded around the chunk decode kernel
   hipEvent_t ev_stop;
 };
-uint32_t decode_tile_chunks(uint32_t chunks_cap);
-uint32_t decode_num_tiles(uint32_t chunks_cap);
 uint64_t decode_params_bytes();
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_serial(const DecodeArgs& a, hipStream_t stream);

@@ -851,7 +851,7 @@ __device__ __forceinline__ bool split_sizes(uint2 e, uint32_t bc, uint32_t cs, u
 // Header and entry checks of a split stream, per tile of T chunks: each
 // chunk's three offsets within its tile, the tile's three totals.
 __global__ __launch_bounds__(kBlock) void split_scan_kernel(const uint8_t* __restrict__ meta, uint64_t meta_bytes,
-                                                            uint64_t out_capacity, uint32_t chunks_cap, uint32_t T,
+                                                            uint64_t out_capacity, uint32_t chunks_cap,
                                                             DecP* __restrict__ P, uint32_t* __restrict__ loc,
                                                             uint64_t* __restrict__ tile_sum,
                                                             uint32_t* __restrict__ tile_err,
@@ -872,6 +872,9 @@ __global__ __launch_bounds__(kBlock) void split_scan_kernel(const uint8_t* __res
     else if (n > out_capacity) st = kStatusCapacity;
     else if (nc > chunks_cap) st = kStatusCorrupt;
   }
+  // tiles sized for the stream's own chunk count, as in the one-stream scan
+  // (the launch covers them: nc <= chunks_cap)
+  const uint32_t T = scan_tile_chunks(nc);
   const uint32_t ntiles = (nc + T - 1u) / T;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     P->n = n;
@@ -1159,16 +1162,13 @@ __global__ __launch_bounds__(kBlock) void serial_chunks_kernel(const uint8_t* __
 
 }  // namespace
 
-uint32_t decode_tile_chunks(uint32_t chunks_cap) { return scan_tile_chunks(chunks_cap); }
-uint32_t decode_num_tiles(uint32_t chunks_cap) { return chunks_cap ? scan_tiles(chunks_cap) : 1u; }
 uint64_t decode_params_bytes() { return sizeof(DecP); }
 
 hipError_t launch_decode_split(const SplitDecodeArgs& a, hipStream_t stream) {
-  const uint32_t T = decode_tile_chunks(a.chunks_cap);
-  const uint32_t tiles = decode_num_tiles(a.chunks_cap);
+  const uint32_t tiles = scan_groups(a.chunks_cap);
   if (tiles > kMaxTilesAlloc) return hipErrorInvalidValue;
   hipLaunchKernelGGL(split_scan_kernel, dim3(tiles), dim3(kBlock), 0, stream, a.meta, a.meta_bytes, a.out_capacity,
-                     a.chunks_cap, T, (DecP*)a.params, a.loc, a.tile_sums, a.tile_err, a.status, a.out_bytes);
+                     a.chunks_cap, (DecP*)a.params, a.loc, a.tile_sums, a.tile_err, a.status, a.out_bytes);
   if (a.chunks_cap > 0) {
     uint32_t grid = (a.chunks_cap + kWaves - 1u) / kWaves;
     if (grid > kDecodeGrid) grid = kDecodeGrid;
