@@ -26,6 +26,8 @@
 //        decoded to zeros.
 //   Errors only ever raise the status (and zero the length), so the kernel
 //   order makes the first write of the status the header kernel's.
+#include <type_traits>
+
 #include "common.h"
 #include "scan_tiles.h"
 
@@ -431,39 +433,8 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
     else if constexpr (WS == 2) return (uint32_t)*(const uint16_t*)w;
     else return (uint32_t)*w;
   };
-  uint32_t rec[G::OVL ? G::RMAX : 1u];  // OVL: this lane's item records
-  uint32_t sum = 0;
-  {
-    uint32_t cur = c0, m = m0;
-    if constexpr (G::OVL) {
-#pragma unroll
-      for (uint32_t r = 0; r < G::RMAX; ++r) {
-        rec[r] = 0u;
-        if (r < nit) {
-          const bool mt = (fb >> r) & 1u;
-          rec[r] = item_rec(cur, m, mt);
-          sum += mt ? (rec[r] & 0xFFu) : item_len(cur, m, false);
-          advance(cur, m, mt);
-        }
-      }
-    } else {
-#pragma unroll 4
-      for (uint32_t r = 0; r < G::RMAX; ++r) {
-        if (r < nit) {
-          const bool mt = (fb >> r) & 1u;
-          sum += item_len(cur, m, mt);
-          advance(cur, m, mt);
-        }
-      }
-    }
-  }
-  uint32_t len_total;
-  uint32_t op = tx.scan(sum, &len_total);
-  // split mode: the flag bits past the last item must be 0 (read here, before
-  // OVL values may land on the flag bytes)
-  const bool pad = SPLIT && (sp.K & 7u) != 0u && (FL[F - 1u] >> (sp.K & 7u)) != 0u;
-  // OVL: every lane's payload reads are issued before any value store below
-  if constexpr (G::OVL) wave_sync();
+  uint32_t len_total = 0, op = 0;
+  bool pad = false;
   uint32_t K = 0, MK = 0, bad = 0, ends = 0;
   // place one item starting at element op
   auto place = [&](uint32_t len, bool mt, uint32_t rc) {
@@ -486,26 +457,71 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
     }
     op += len;
   };
-  {
-    uint32_t cur = c0, m = m0;
-    if constexpr (G::OVL) {
+  // split mode: the flag bits past the last item must be 0 (read before OVL
+  // values may land on the flag bytes)
+  auto pad_bits = [&]() { return SPLIT && (sp.K & 7u) != 0u && (FL[F - 1u] >> (sp.K & 7u)) != 0u; };
+  if constexpr (G::OVL) {
+    // Every lane reads all its items into registers (unrolled, so the
+    // records stay registers) before any value lands on the payload bytes.
+    // The walk is instantiated for 4, 8 and RMAX items per lane and the
+    // wave takes the smallest that holds R (a wave uniform), so a chunk with
+    // few items per lane does not step through RMAX masked slots.
+    auto walk = [&](auto nr) {
+      constexpr uint32_t NR = decltype(nr)::value;
+      uint32_t rec[NR];
+      uint32_t sum = 0, cur = c0, m = m0;
 #pragma unroll
-      for (uint32_t r = 0; r < G::RMAX; ++r) {
+      for (uint32_t r = 0; r < NR; ++r) {
+        rec[r] = 0u;
+        if (r < nit) {
+          const bool mt = (fb >> r) & 1u;
+          rec[r] = item_rec(cur, m, mt);
+          sum += mt ? (rec[r] & 0xFFu) : item_len(cur, m, false);
+          advance(cur, m, mt);
+        }
+      }
+      op = tx.scan(sum, &len_total);
+      pad = pad_bits();
+      wave_sync();
+      cur = c0;
+      m = m0;
+#pragma unroll
+      for (uint32_t r = 0; r < NR; ++r) {
         if (r < nit) {
           const bool mt = (fb >> r) & 1u;
           place(mt ? (rec[r] & 0xFFu) : item_len(cur, m, false), mt, rec[r]);
           advance(cur, m, mt);
         }
       }
-    } else {
-#pragma unroll 4
-      for (uint32_t r = 0; r < G::RMAX; ++r) {
+    };
+    static_assert(G::RMAX > 8u, "three walk sizes");
+    if (R <= 4u) walk(std::integral_constant<uint32_t, 4u>{});
+    else if (R <= 8u) walk(std::integral_constant<uint32_t, 8u>{});
+    else walk(std::integral_constant<uint32_t, G::RMAX>{});
+  } else {
+    // R (<= RMAX) bounds every lane's items
+    uint32_t sum = 0;
+    {
+      uint32_t cur = c0, m = m0;
+#pragma unroll 2
+      for (uint32_t r = 0; r < R; ++r) {
         if (r < nit) {
           const bool mt = (fb >> r) & 1u;
-          const uint32_t rc = item_rec(cur, m, mt);
-          place(mt ? (rc & 0xFFu) : item_len(cur, m, false), mt, rc);
+          sum += item_len(cur, m, mt);
           advance(cur, m, mt);
         }
+      }
+    }
+    op = tx.scan(sum, &len_total);
+    pad = pad_bits();
+    uint32_t cur = c0, m = m0;
+#pragma unroll 2
+    for (uint32_t r = 0; r < R; ++r) {
+      if (r < nit) {
+        const bool mt = (fb >> r) & 1u;
+        const uint32_t rc = item_rec(cur, m, mt);
+        place(mt ? (rc & 0xFFu) : item_len(cur, m, false), mt, rc);
+        advance(cur, m, mt);
       }
     }
   }
