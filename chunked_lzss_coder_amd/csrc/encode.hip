@@ -637,8 +637,24 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
         team_sync<WPC>();  // T (and a reloaded XL) overlay dead table levels
         constexpr uint32_t SB = E / kSubBlocks;
         static_assert(SB <= TL, "one position per lane per sub-block");
+        // The next sub-block's key words and near lengths are loaded while
+        // this one runs: the walk writes neither (it writes only the table and
+        // the current sub-block's (L, O)).
+        uint32_t nx0 = 0, nx1 = 0, nlo = 0;
+        if (g < SB) {
+          nx0 = XL[g];
+          nx1 = XL[g + 1u];
+          nlo = LO[g];
+        }
 #pragma unroll 1
         for (uint32_t s = 0; s < kSubBlocks; ++s) {
+          const uint32_t x0 = nx0, x1 = nx1, lo_p = nlo;
+          if (s + 1u < kSubBlocks && g < SB) {
+            const uint32_t pn = (s + 1u) * SB + g;
+            nx0 = XL[pn];
+            nx1 = XL[pn + 1u];  // past the chunk only at pn = E - 1 (no key there; still inside LDS)
+            nlo = LO[pn];
+          }
           // One position per lane (consecutive lanes, consecutive positions).
           // A candidate replaces the near match only if its run is strictly
           // longer, so it must match at p + Lnear, and Lnear must leave room.
@@ -651,25 +667,39 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
           // bucket is kept for the insert below.
           const uint32_t p = s * SB + g;
           const bool ins = g < SB && p + 1 < (uint32_t)E;
-          const uint32_t bk = ins ? bucket_of(XL[p], XL[p + 1]) : 0u;
+          const uint32_t bk = ins ? bucket_of(x0, x1) : 0u;
           if (g < SB) {
             uint32_t o = 0, Lnear = 0, lim = 0;
             bool need = false;
+            uint32_t r = 0;
+            bool open = false;
             if (ins) {
               const uint32_t v = L::HT16 ? (uint32_t)T16[bk] : T[bk];
               o = p - (v - 1u);  // entries come from earlier sub-blocks: o >= 1
               lim = (uint32_t)E - p < kMaxLen ? (uint32_t)E - p : kMaxLen;
-              Lnear = LO[p] & 0xFFu;
-              need = v != 0u && o <= kMaxFar && Lnear < lim && XL[p + Lnear] == XL[p + Lnear - o];
-            }
-            uint32_t r = 0;
-            bool open = need;
-            if (open) {
-              uint32_t stop = 0;
+              Lnear = lo_p & 0xFFu;
+              if (v != 0u && o <= kMaxFar && Lnear < lim) {
+                // One batch of loads: the word at p + Lnear (the candidate
+                // must match there to be longer) and the first 8 word pairs.
+                // Words past the chunk's end (p + 7 < E + 8) still lie in the
+                // team's LDS, since the word region is followed by other
+                // regions, and their bits are set by j >= lim anyway.
+                const uint32_t xa = XL[p + Lnear], xb = XL[p + Lnear - o];
+                uint32_t wa[8], wb[8];
 #pragma unroll
-              for (uint32_t j = 0; j < 8u; ++j) stop |= (uint32_t)(j >= lim || XL[p + j] != XL[p + j - o]) << j;
-              r = stop ? (uint32_t)__builtin_ctz(stop) : 8u;
-              open = stop == 0u;
+                for (uint32_t j = 0; j < 8u; ++j) {
+                  wa[j] = XL[p + j];
+                  wb[j] = XL[p + j - o];
+                }
+                need = xa == xb;
+                if (need) {
+                  uint32_t stop = 0;
+#pragma unroll
+                  for (uint32_t j = 0; j < 8u; ++j) stop |= (uint32_t)((j >= lim) | (wa[j] != wb[j])) << j;
+                  r = stop ? (uint32_t)__builtin_ctz(stop) : 8u;
+                  open = stop == 0u;
+                }
+              }
             }
             const uint64_t openm = __ballot(open);
             if (openm) {  // long runs (lim > 8 for every open lane)
