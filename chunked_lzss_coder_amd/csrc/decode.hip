@@ -282,11 +282,11 @@ struct SplitSrc {
 };
 
 // Decode one coded chunk.  One stream: pay is its payload (F flag bytes, D
-// data bytes), lim the end of the readable input.  Split mode: sp locates
-// its items in the ports (pay, lim, F, D unused).  bc: the chunk's real
+// data bytes).  Split mode: sp locates its items in the ports (pay, F, D
+// unused).  bc: the chunk's real
 // bytes, written to dst.  Returns false on a rule violation.
 template <uint32_t CS, uint32_t WS, bool SPLIT = false, bool TEAMS = false>
-__device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* lim, uint32_t F, uint32_t D, uint32_t bc,
+__device__ __forceinline__ bool decode_coded(const uint8_t* pay, uint32_t F, uint32_t D, uint32_t bc,
                              uint8_t* dst, uint8_t* arena, uint32_t* sh, const SplitSrc& sp) {
   using G = Geo<CS, WS, TEAMS>;
   constexpr uint32_t E = G::E, TW = G::TW, TL = G::TL, J = G::J, NB = G::NB;
@@ -302,22 +302,35 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
   // every live item covers at least one element: at most E items, so at most
   // (E + 7) / 8 flag bytes
   if (F > (E + 7u) / 8u) return false;
-  // stage len bytes from src into PB at byte offset at (4-byte aligned), four
-  // loads per lane in flight before their LDS stores
-  auto stage = [&](uint32_t at, const uint8_t* src, uint32_t len, const uint8_t* srclim) {
-    const uint32_t nd = (len + 3u) / 4u;
+  // stage len bytes from src into PB (dword i = source bytes 4i..4i+3): the
+  // aligned source dwords holding a byte of [src, src + len) are read (no
+  // read leaves the pages those bytes lie in), each dword realigned with the
+  // one after it; up to four loads per lane in flight before their stores
+  auto stage = [&](const uint8_t* src, uint32_t len) {
+    const uint32_t sh = (uint32_t)((uintptr_t)src & 3u);
+    const uint32_t* A = (const uint32_t*)(src - sh);
+    const uint32_t nA = (sh + len + 3u) >> 2;  // aligned dwords holding a byte of the span
+    const uint32_t nd = (len + 3u) >> 2;
+    uint32_t* P32 = (uint32_t*)PB;
+    if (nd <= TL) {  // one dword per lane
+      const uint32_t a = g < nA ? A[g] : 0u;
+      const uint32_t b = (sh != 0u && g + 1u < nA) ? A[g + 1u] : 0u;
+      if (g < nd) P32[g] = __builtin_amdgcn_alignbyte(b, a, sh);
+      return;
+    }
 #pragma unroll 1
     for (uint32_t i0 = 0; i0 < nd; i0 += 4u * TL) {
-      uint32_t v[4];
+      uint32_t a[4], b[4];
 #pragma unroll
       for (uint32_t r = 0; r < 4u; ++r) {
         const uint32_t i = i0 + g + r * TL;
-        v[r] = i < nd ? load4_unaligned(src + 4u * i, srclim) : 0u;
+        a[r] = i < nA ? A[i] : 0u;
+        b[r] = (sh != 0u && i + 1u < nA) ? A[i + 1u] : 0u;
       }
 #pragma unroll
       for (uint32_t r = 0; r < 4u; ++r) {
         const uint32_t i = i0 + g + r * TL;
-        if (i < nd) ((uint32_t*)(PB + at))[i] = v[r];
+        if (i < nd) P32[i] = __builtin_amdgcn_alignbyte(b[r], a[r], sh);
       }
     }
   };
@@ -331,9 +344,8 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
     const uint32_t lo = (F + 3u) & ~3u, mo = (lo + WS * NL + 3u) & ~3u, oo = (mo + sp.M + 3u) & ~3u;
     // the four regions in one pass, so their loads are in flight together:
     // dword i of PB belongs to the region whose dword range holds it (the
-    // gaps between regions get zeros); a region's reads stop at its own
-    // last byte (aligned dwords holding a byte of it, so no read leaves the
-    // pages its bytes lie in)
+    // gaps between regions get zeros); only aligned dwords holding a byte of
+    // the region are read, so no read leaves the pages its bytes lie in
     const uint32_t d1 = lo >> 2, d2 = mo >> 2, d3 = oo >> 2;
     const uint32_t e0 = (F + 3u) >> 2, e1 = d1 + ((WS * NL + 3u) >> 2), e2 = d2 + ((sp.M + 3u) >> 2),
                    e3 = d3 + ((sp.M + 3u) >> 2);
@@ -354,7 +366,17 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
         } else if (i >= d3 && i < e3) {
           src = sp.offs, len = sp.M, b = i - d3;
         }
-        v[r] = src ? load4_unaligned(src + 4u * b, src + len) : 0u;
+        // the aligned dwords holding bytes 4b .. 4b + 3 (only those holding
+        // a byte of the region), realigned
+        uint32_t lo = 0, hi = 0, sh = 0;
+        if (src) {
+          sh = (uint32_t)((uintptr_t)src & 3u);
+          const uint32_t* A = (const uint32_t*)(src - sh);
+          const uint32_t nA = (sh + len + 3u) >> 2;
+          lo = A[b];
+          if (sh != 0u && b + 1u < nA) hi = A[b + 1u];
+        }
+        v[r] = __builtin_amdgcn_alignbyte(hi, lo, sh);
       }
 #pragma unroll
       for (uint32_t r = 0; r < 4u; ++r) {
@@ -369,7 +391,7 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
     PD = PB;
   } else {
     const uint32_t s0 = (4u - (F & 3u)) & 3u;
-    stage(0u, pay - s0, s0 + F + D, lim);
+    stage(pay - s0, s0 + F + D);
     FL = PB + s0;
     PD = PB + s0 + F;
     LITB = LENB = OFFB = PD;
@@ -694,7 +716,7 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, const uint8_t* 
 }
 
 template <uint32_t CS, uint32_t WS, bool TEAMS>
-__device__ __forceinline__ void decode_group_teams(const DecP& p, const uint8_t* in, const uint8_t* lim, uint8_t* out,
+__device__ __forceinline__ void decode_group_teams(const DecP& p, const uint8_t* in, uint8_t* out,
                                                    const uint32_t* loc, const uint64_t* tile_sum, uint32_t* status,
                                                    uint64_t* out_bytes, uint8_t* arena_all, uint32_t* sh,
                                                    uint64_t pre) {
@@ -765,7 +787,7 @@ __device__ __forceinline__ void decode_group_teams(const DecP& p, const uint8_t*
       else if constexpr (G::OVL) copy_bytes16_r2(dst + w0, pay + w0, len, lane);
       else copy_bytes16_r1(dst + w0, pay + w0, len, lane);
     } else {
-      if (!decode_coded<CS, WS, false, TEAMS>(pay, lim, e.x, e.y, bc, dst, arena, sh, SplitSrc{}) && g == 0)
+      if (!decode_coded<CS, WS, false, TEAMS>(pay, e.x, e.y, bc, dst, arena, sh, SplitSrc{}) && g == 0)
         raise_status(status, out_bytes, kStatusCorrupt);
     }
     team_sync<G::TW>();
@@ -773,7 +795,7 @@ __device__ __forceinline__ void decode_group_teams(const DecP& p, const uint8_t*
 }
 
 template <uint32_t CS, uint32_t WS>
-__device__ __forceinline__ void decode_group(const DecP& p, const uint8_t* in, const uint8_t* lim, uint8_t* out,
+__device__ __forceinline__ void decode_group(const DecP& p, const uint8_t* in, uint8_t* out,
                              const uint32_t* loc, const uint64_t* tile_sum, uint32_t* status, uint64_t* out_bytes,
                              uint8_t* arena_all, uint32_t* sh, uint64_t pre) {
   // Chunks that fit one slot only with the payload over the values go one
@@ -781,20 +803,20 @@ __device__ __forceinline__ void decode_group(const DecP& p, const uint8_t* in, c
   // stream decodes faster with a workgroup per chunk.
   if constexpr (Geo<CS, WS>::OVL) {
     if (p.nc >= kOneWaveMinChunks) {
-      decode_group_teams<CS, WS, false>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena_all, sh, pre);
+      decode_group_teams<CS, WS, false>(p, in, out, loc, tile_sum, status, out_bytes, arena_all, sh, pre);
       return;
     }
   }
-  decode_group_teams<CS, WS, true>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena_all, sh, pre);
+  decode_group_teams<CS, WS, true>(p, in, out, loc, tile_sum, status, out_bytes, arena_all, sh, pre);
 }
 
 template <uint32_t CS>
-__device__ __forceinline__ void decode_by_ws(const DecP& p, const uint8_t* in, const uint8_t* lim, uint8_t* out,
+__device__ __forceinline__ void decode_by_ws(const DecP& p, const uint8_t* in, uint8_t* out,
                              const uint32_t* loc, const uint64_t* tile_sum, uint32_t* status, uint64_t* out_bytes,
                              uint8_t* arena, uint32_t* sh, uint64_t pre) {
-  if (p.ws == 4u) decode_group<CS, 4>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh, pre);
-  else if (p.ws == 2u) decode_group<CS, 2>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh, pre);
-  else decode_group<CS, 1>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh, pre);
+  if (p.ws == 4u) decode_group<CS, 4>(p, in, out, loc, tile_sum, status, out_bytes, arena, sh, pre);
+  else if (p.ws == 2u) decode_group<CS, 2>(p, in, out, loc, tile_sum, status, out_bytes, arena, sh, pre);
+  else decode_group<CS, 1>(p, in, out, loc, tile_sum, status, out_bytes, arena, sh, pre);
 }
 
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(7))) void chunks_kernel(const uint8_t* __restrict__ in, uint64_t in_bytes,
@@ -831,11 +853,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(7))) voi
     err = lane63(wave_incl_add(err));
     if (lane_id() == 0 && (s != p.pb || err)) raise_status(status, out_bytes, kStatusCorrupt);
   }
-  const uint8_t* lim = in + in_bytes;
   // the header kernel accepted cs and ws, so they are among these
-  if (p.cs == 1024u) decode_by_ws<1024>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh, pre);
-  else if (p.cs == 2048u) decode_by_ws<2048>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh, pre);
-  else decode_by_ws<4096>(p, in, lim, out, loc, tile_sum, status, out_bytes, arena, sh, pre);
+  if (p.cs == 1024u) decode_by_ws<1024>(p, in, out, loc, tile_sum, status, out_bytes, arena, sh, pre);
+  else if (p.cs == 2048u) decode_by_ws<2048>(p, in, out, loc, tile_sum, status, out_bytes, arena, sh, pre);
+  else decode_by_ws<4096>(p, in, out, loc, tile_sum, status, out_bytes, arena, sh, pre);
 }
 
 // ---- split mode ------------------------------------------------------------------
@@ -1016,7 +1037,7 @@ __device__ __forceinline__ void decode_group_split(const DecP& p, const SplitDec
       else copy_bytes16_r1(dst + w0, a.lit + pre[1] + w0, len, lane);
     } else {
       const SplitSrc sp{flags + pre[0], a.lit + pre[1], a.lens + pre[2], a.offs + pre[2], e.x, e.y};
-      if (!decode_coded<CS, WS, true>(nullptr, nullptr, 0u, 0u, bc, dst, arena, sh, sp) && g == 0)
+      if (!decode_coded<CS, WS, true>(nullptr, 0u, 0u, bc, dst, arena, sh, sp) && g == 0)
         raise_status(a.status, a.out_bytes, kStatusCorrupt);
     }
     team_sync<G::TW>();
