@@ -1416,8 +1416,9 @@ __global__ __launch_bounds__(kBlock) void split_compact_kernel(
 }
 
 // Upstream-style baseline search (GPULZStage page, exact longest-match search
-// paragraph: upstream advances its window pointer on every step of the
-// search and settles for shorter matches).  Read as: the pointer w walks the
+// paragraph, which describes upstream's search as one whose candidate pointer
+// moves forward with each comparison, so that it ends up with shorter
+// matches than the exact search).  Read as: the pointer w walks the
 // 32 words before p, one comparison per step of x[w] against x[p + len], the
 // word the partial match started at w - len needs next; equal grows it,
 // unequal drops it and spends w; the longest partial match seen is the

@@ -9,10 +9,10 @@
  * that decode, built the same way as gpulz_decode otherwise (device-side
  * header and size-table scan), so the two can be timed side by side.
  *
- * Encode: the page says upstream advances its window pointer on every step
- * of the match search, so a match it extends uses up the candidate starts
- * behind it, and that the exact search is both cheaper and strictly better
- * compressing (exact longest-match search paragraph).
+ * Encode: per the page, upstream's match search moves its candidate pointer
+ * forward with each comparison, so starts passed while a match is extended
+ * are never tried; the exact search costs less and compresses better (exact
+ * longest-match search paragraph).
  * gpulz_encode_advancing_search is the level-0 coder with that search in
  * place of the exact one, read as: for position p the pointer w walks the 32
  * elements before p (not before the chunk start), one comparison per step of

@@ -1,9 +1,9 @@
 """Pins of the oracle's upstream-style advancing-window search (CPU only).
 
-The GPULZStage page says upstream moves its window pointer on every step of
-the search, so a match being extended passes over candidate starts it never
-tries, and it settles for shorter matches than the exact search finds
-(exact longest-match search paragraph).  The oracle's reading: the pointer w
+Per the GPULZStage page (exact longest-match search paragraph), upstream's
+search moves its candidate pointer forward with each comparison, so while a
+match is being extended the starts it passes are never tried, and its
+matches come out shorter than the exact search's.  The oracle's reading: the pointer w
 walks the 32 elements before p, one comparison per step of x[w] against the
 element the partial match needs next; a mismatch drops the partial match and
 spends that w; the longest partial match seen wins (the first on ties).
