@@ -357,6 +357,9 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
   };
 
   // ---- 1. load + zero vote ---------------------------------------------------------
+  // PRE: level 0, 32-offset window, word size 4, one mask pass per chunk (the
+  // offset-mask pass below tries a cheaper test first)
+  constexpr bool PRE = L::LAZY && WS == 4 && E / ((E == 256 ? 4u : 8u) * TL) == 1u;
   for (uint32_t i = g; i < L::XPAD; i += TL) X[(int)i - (int)L::XPAD] = 0u;
   uint32_t any = 0;
   if (bc == CS && (((uintptr_t)src) & 15u) == 0) {
@@ -431,13 +434,39 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
           }
         }
         Mask om[PPASS];
-#pragma unroll
-        for (uint32_t q = 0; q < PPASS; ++q) {
-          // offsets 32..17, then 16..1: bit o-1 compares w[32+q] with w[32+q-o]
+        // offsets 32..17, then 16..1: bit o-1 compares w[32+q] with w[32+q-o]
+        auto mask_of = [&](uint32_t q) -> uint32_t {
           uint32_t m = 0;
           match_bits16(m, &w[q], w[32 + q]);
           match_bits16(m, &w[q + 16], w[32 + q]);
-          om[q] = m;
+          return m;
+        };
+        if constexpr (PRE) {
+          // Each lane's last position first.  If none of them has a near
+          // match, the other positions are first tested by compares alone
+          // (one instruction each, their lane masks OR-ed in scalar registers,
+          // eight accumulators so the ORs form no chain); a chunk where that
+          // finds nothing either is raw, and its masks are all zero.  Words
+          // ahead of the chunk read as zeros there, which can only report a
+          // match that is not there (then the masks are computed).
+          constexpr uint32_t QS = PPASS - 1u;
+          om[QS] = mask_of(QS);
+          if (p0 + QS < 32u) om[QS] &= (1u << (p0 + QS)) - 1u;
+          bool full = WPC == 1 ? __ballot(om[QS] != 0u) != 0ull : __syncthreads_or(om[QS] != 0u);
+          if (!full) {
+            uint64_t ha[8] = {0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull, 0ull};
+#pragma unroll
+            for (uint32_t q = 0; q < QS; ++q)
+#pragma unroll
+              for (uint32_t o = 1; o <= 32u; ++o) ha[o & 7u] |= __ballot(w[32 + q - o] == w[32 + q]);
+            const uint64_t h = (ha[0] | ha[1]) | (ha[2] | ha[3]) | (ha[4] | ha[5]) | (ha[6] | ha[7]);
+            full = WPC == 1 ? h != 0ull : __syncthreads_or(h != 0ull);
+          }
+#pragma unroll
+          for (uint32_t q = 0; q < QS; ++q) om[q] = full ? mask_of(q) : 0u;
+        } else {
+#pragma unroll
+          for (uint32_t q = 0; q < PPASS; ++q) om[q] = mask_of(q);
         }
         if (p0 < 32u) {  // offsets reach back to the chunk start at most: bits o - 1 < p
 #pragma unroll
