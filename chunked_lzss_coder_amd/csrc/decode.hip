@@ -10,15 +10,17 @@
 //   every size-table row against its chunk's real bytes, writes each chunk's
 //   payload offset within its tile, the tile's total and an error flag.
 //   No workgroup waits on another.
-// chunks_kernel (one wave per chunk; four waves per chunk when a chunk has
-//   more than 1024 elements): the chunk's payload offset is its tile's offset
-//   (sum of earlier tile totals) plus its offset in the tile; then
+// chunks_kernel (one wave per chunk; the four waves of a workgroup per
+//   chunk when a chunk has more than 1024 elements, or has 1024 and the
+//   stream fewer than 2048 chunks): the chunk's payload offset is its tile's
+//   offset (sum of earlier tile totals) plus its offset in the tile; then
 //     zero row -> zero fill; raw row -> copy; otherwise, per the
 //     block-parallel decode paragraph of the GPULZStage page:
-//     a. items 64 at a time: an item's token position follows from the
-//        number of matches before it (flag popcounts), its output length is
-//        1 or the token's length; a wave scan of the lengths gives every
-//        item's output position; every token rule is checked;
+//     a. the payload is staged in LDS; lane g walks items [gR, gR + R) (R =
+//        items per lane): an item's data offset follows from the matches
+//        before it (flag popcounts, one team scan), its output length is 1
+//        or the token's length, and a second team scan of the lengths gives
+//        every item's output position; every token rule is checked;
 //     b. each element of a match item points into the data before the item,
 //        start - O + (q - start) mod O, always < start; pointer jumping
 //        resolves chains in at most log2(items)+1 rounds with early exit;

@@ -10,25 +10,32 @@
 //   2. omask[p], bit o-1 = (x[p] == x[p-o]), o = 1..32 [exact-search
 //      paragraph]: each lane holds 8 consecutive positions and the 32 words
 //      before them in registers, so the 256 comparisons per lane read LDS once;
-//      no bit set anywhere -> at level 0 the chunk is raw, steps 3-6 skipped;
-//   3. a base-4 doubling table S_k[p] = AND of omask over [p, p+k) for
+//      no bit set anywhere -> at level 0 the chunk is raw, steps 3-6 skipped
+//      (word size 4: a chunk whose sampled positions have no match is first
+//      tested by compares alone, and skips the masks if that finds none);
+//   3. level 0, window 32, up to 1024 elements: S_4 and a short descent give
+//      the exact (L, O) below 16 and mark longer matches, whose exact length
+//      is found only where the parse starts an item (step 5).  Otherwise a
+//      base-4 doubling table S_k[p] = AND of omask over [p, p+k) for
 //      k = 1, 4, 16 (S_64 read as the AND of four S_16 entries, not stored),
-//      and a 4-round descent per position (up to three
-//      steps of k per round, so L <= 255) giving the exact longest run of any
-//      offset, capped at 255, and the smallest offset reaching it
-//      [exact-search and long-match paragraphs];
+//      and a 4-round descent per position (up to three steps of k per round,
+//      so L <= 255).  Either way: the exact longest run of any offset, capped
+//      at 255, and the smallest offset reaching it [exact-search and
+//      long-match paragraphs];
 //   4. level 1: 2048-bucket table of position+1 per sub-block, lookups and
-//      atomicMax inserts separated by barriers [hashed-table paragraphs];
+//      max inserts separated by barriers [hashed-table paragraphs];
 //   5. greedy parse [provenance paragraph], in parallel: every 8-position
 //      segment computes, for each entry position, where the parse leaves the
 //      segment and which positions start items; a short chain of hops over
 //      segments then fixes the real entry of each segment;
-//   6. item counts from popcounts (two item sizes only) -> flag bytes F and
-//      data bytes D; raw when F + D >= real bytes [raw-fallback paragraph];
+//   6. counts: lane g takes segment g; one packed scan of its items and
+//      matches (two item sizes only) -> flag bytes F and data bytes D; raw
+//      when F + D >= real bytes [raw-fallback paragraph];
 //   7. the size-table row goes straight into the stream; a coded payload
-//      (flag bitmap, then data bytes) is built in LDS and written to the
-//      chunk's fixed-stride staging slot.  A raw chunk's payload is its input
-//      bytes: it is never staged, the assembly copies it from the input.
+//      (flag bitmap, then data bytes; each lane writes its segment's items)
+//      is built in LDS and written to the chunk's fixed-stride staging slot.
+//      A raw chunk's payload is its input bytes: it is never staged, the
+//      assembly copies it from the input.
 // compact_kernel: one workgroup per tile of 64 chunks scans the tile's sizes,
 //   finds the tile's offset by decoupled look-back over the tiles before it
 //   and moves every payload to its place in the stream with 16-byte stores;
