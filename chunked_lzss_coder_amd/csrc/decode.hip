@@ -427,16 +427,6 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, uint32_t F, uin
   // cursor of item k: one stream, its data offset; split mode, its literal
   // index (matches: the match index m)
   const uint32_t c0 = SPLIT ? k0 - m0 : WS * (k0 - m0) + 2u * m0;
-  // output length of an item (0 if unreadable)
-  auto item_len = [&](uint32_t cur, uint32_t m, bool mt) -> uint32_t {
-    if constexpr (SPLIT) {
-      if (mt) return m < sp.M ? (uint32_t)LENB[m] : 0u;
-      return cur < NL ? 1u : 0u;
-    } else {
-      if (mt) return cur + 2u <= D ? (uint32_t)PD[cur] : 0u;
-      return cur + WS <= D ? 1u : 0u;
-    }
-  };
   auto advance = [&](uint32_t& cur, uint32_t& m, bool mt) {
     if constexpr (SPLIT) {
       if (mt) ++m;
@@ -446,94 +436,110 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, uint32_t F, uin
       m += mt ? 1u : 0u;
     }
   };
-  // an item's record: a match's length | offset << 8 (0 if unreadable), a
-  // literal's value (0 if unreadable; its length follows from cur alone)
+  // An item's record: a match's length | offset << 8, a literal's value.
+  // Reads are unconditional and unchecked, and both kinds are read so the
+  // walk has no branch: a cursor never passes its lane's last item by more
+  // than RMAX items, so every address stays inside the chunk's arena, and an
+  // item that does not fit the payload makes the totals of the live items
+  // disagree with the chunk's sizes (checked after the walk).
   auto item_rec = [&](uint32_t cur, uint32_t m, bool mt) -> uint32_t {
-    const uint32_t len = item_len(cur, m, mt);
-    if (len == 0u) return 0u;
-    if (mt) return len | ((uint32_t)(SPLIT ? OFFB[m] : PD[cur + 1u]) << 8);
-    const uint8_t* w = SPLIT ? LITB + WS * cur : PD + cur;  // 2-byte aligned for WS >= 2
-    if constexpr (WS == 4) return (uint32_t)*(const uint16_t*)w | ((uint32_t)*(const uint16_t*)(w + 2u) << 16);
-    else if constexpr (WS == 2) return (uint32_t)*(const uint16_t*)w;
-    else return (uint32_t)*w;
+    if constexpr (SPLIT) {
+      // the two kinds live in different ports: only the item's own is read
+      if (mt) return (uint32_t)LENB[m] | ((uint32_t)OFFB[m] << 8);
+      const uint8_t* w = LITB + WS * cur;
+      if constexpr (WS == 4) return *(const uint32_t*)w;  // literal words are 4-byte aligned in LDS
+      else if constexpr (WS == 2) return (uint32_t)*(const uint16_t*)w;
+      else return (uint32_t)*w;
+    } else {
+      const uint8_t* w = PD + cur;  // 2-byte aligned for WS >= 2
+      if constexpr (WS == 4) {
+        // the two aligned dwords around the item, realigned (an LDS dword
+        // read from a 2-byte boundary costs far more than two aligned ones);
+        // PD is 4-byte aligned, so cur & 3 is the item's offset in the first
+        const uint32_t* A = (const uint32_t*)(PD + (cur & ~3u));
+        const uint32_t v = __builtin_amdgcn_alignbyte(A[1], A[0], cur & 3u);
+        return mt ? (v & 0xFFFFu) : v;
+      } else if constexpr (WS == 2) {
+        return (uint32_t)*(const uint16_t*)w;
+      } else {
+        const uint32_t lo = *w, hi = w[1];
+        return mt ? (lo | (hi << 8)) : lo;
+      }
+    }
   };
   uint32_t len_total = 0, op = 0;
+  uint32_t rend = 0;  // 1 + the lane's item that ends at element E (0: none)
+  bool badm = false;  // a live match of length 0 or reaching before the chunk
   bool pad = false;
-  uint32_t K = 0, MK = 0, bad = 0, ends = 0;
-  // place one item starting at element op
-  auto place = [&](uint32_t len, bool mt, uint32_t rc) {
-    if (op < E) {  // live: starts before the chunk's end
-      ++K;
-      if (len == 0u) {
-        bad = 1u;  // unreadable, or a zero-length match
-      } else if (mt) {
-        ++MK;
-        const uint32_t O = rc >> 8;
-        if (O == 0u || O > op || op + len > E) bad = 1u;
-        else OB[op] = (uint8_t)O;
+  uint32_t* const STB32 = (uint32_t*)STB;
+  // place item r of the lane (record rc) at element op
+  auto place = [&](uint32_t r, bool mt, uint32_t rc) {
+    const uint32_t len = mt ? (rc & 0xFFu) : 1u;
+    if (r < nit && op < E) {  // live: starts before the chunk's end
+      if (mt) {
+        OB[op] = (uint8_t)(rc >> 8);
       } else {
         if constexpr (WS == 4) *(uint32_t*)(VAL + 4u * op) = rc;
         else if constexpr (WS == 2) *(uint16_t*)(VAL + 2u * op) = (uint16_t)rc;
         else VAL[op] = (uint8_t)rc;
       }
-      if (len != 0u) atomicOr((unsigned long long*)&STB[op >> 6], 1ull << (op & 63u));
-      if (op + len == E) ends = 1u;
+      atomicOr(STB32 + (op >> 5), 1u << (op & 31u));
+      badm = badm || (mt && (len == 0u || (rc >> 8) - 1u >= op));
+      if (op + len == E) rend = r + 1u;
     }
     op += len;
   };
   // split mode: the flag bits past the last item must be 0 (read before OVL
   // values may land on the flag bytes)
   auto pad_bits = [&]() { return SPLIT && (sp.K & 7u) != 0u && (FL[F - 1u] >> (sp.K & 7u)) != 0u; };
+  // the lane's output length: one element per literal (nit - popcount(fb)
+  // of them), plus the match lengths summed in the walk
+  const uint32_t lit_len = nit - (uint32_t)__builtin_popcount(fb);
   if constexpr (G::OVL) {
     // Every lane reads all its items into registers (unrolled, so the
     // records stay registers) before any value lands on the payload bytes.
-    // The walk is instantiated for 4, 8 and RMAX items per lane and the
+    // The walk is instantiated for 2, 4, 8, 12 and 16 items per lane and the
     // wave takes the smallest that holds R (a wave uniform), so a chunk with
     // few items per lane does not step through RMAX masked slots.
     auto walk = [&](auto nr) {
       constexpr uint32_t NR = decltype(nr)::value;
       uint32_t rec[NR];
-      uint32_t sum = 0, cur = c0, m = m0;
+      uint32_t sum = lit_len, cur = c0, m = m0;
 #pragma unroll
       for (uint32_t r = 0; r < NR; ++r) {
-        rec[r] = 0u;
-        if (r < nit) {
-          const bool mt = (fb >> r) & 1u;
-          rec[r] = item_rec(cur, m, mt);
-          sum += mt ? (rec[r] & 0xFFu) : item_len(cur, m, false);
-          advance(cur, m, mt);
-        }
+        const bool mt = (fb >> r) & 1u;  // 0 past the lane's items
+        rec[r] = item_rec(cur, m, mt);
+        sum += mt ? (rec[r] & 0xFFu) : 0u;
+        advance(cur, m, mt);
       }
       op = tx.scan(sum, &len_total);
       pad = pad_bits();
       wave_sync();
-      cur = c0;
-      m = m0;
+      // the flag bits again through a DPP identity move, so the compiler
+      // takes each item's kind afresh here rather than keeping all NR lane
+      // masks of the reading loop alive across the scan
+      const uint32_t fbp = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)fb, 0xE4, 0xF, 0xF, false);
 #pragma unroll
-      for (uint32_t r = 0; r < NR; ++r) {
-        if (r < nit) {
-          const bool mt = (fb >> r) & 1u;
-          place(mt ? (rec[r] & 0xFFu) : item_len(cur, m, false), mt, rec[r]);
-          advance(cur, m, mt);
-        }
-      }
+      for (uint32_t r = 0; r < NR; ++r) place(r, (fbp >> r) & 1u, rec[r]);
     };
-    static_assert(G::RMAX > 8u, "three walk sizes");
-    if (R <= 4u) walk(std::integral_constant<uint32_t, 4u>{});
+    // F <= (E + 7) / 8 was checked, so R <= 8F / 64 = E / 512 * 8 <= 16
+    static_assert(E <= 1024u, "at most 16 items per lane");
+    if (R <= 2u) walk(std::integral_constant<uint32_t, 2u>{});
+    else if (R <= 4u) walk(std::integral_constant<uint32_t, 4u>{});
     else if (R <= 8u) walk(std::integral_constant<uint32_t, 8u>{});
-    else walk(std::integral_constant<uint32_t, G::RMAX>{});
+    else if (R <= 12u) walk(std::integral_constant<uint32_t, 12u>{});
+    else walk(std::integral_constant<uint32_t, 16u>{});
   } else {
     // R (<= RMAX) bounds every lane's items
-    uint32_t sum = 0;
+    uint32_t sum = lit_len;
     {
       uint32_t cur = c0, m = m0;
 #pragma unroll 2
       for (uint32_t r = 0; r < R; ++r) {
-        if (r < nit) {
-          const bool mt = (fb >> r) & 1u;
-          sum += item_len(cur, m, mt);
-          advance(cur, m, mt);
-        }
+        const bool mt = (fb >> r) & 1u;
+        const uint32_t lb = SPLIT ? (uint32_t)LENB[m] : (uint32_t)PD[cur];  // read unconditionally
+        sum += mt ? lb : 0u;
+        advance(cur, m, mt);
       }
     }
     op = tx.scan(sum, &len_total);
@@ -541,19 +547,26 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, uint32_t F, uin
     uint32_t cur = c0, m = m0;
 #pragma unroll 2
     for (uint32_t r = 0; r < R; ++r) {
-      if (r < nit) {
-        const bool mt = (fb >> r) & 1u;
-        const uint32_t rc = item_rec(cur, m, mt);
-        place(mt ? (rc & 0xFFu) : item_len(cur, m, false), mt, rc);
-        advance(cur, m, mt);
-      }
+      const bool mt = (fb >> r) & 1u;
+      place(r, mt, item_rec(cur, m, mt));
+      advance(cur, m, mt);
     }
   }
   {
-    // K, MK <= 4103 items and bad, ends <= 256 lanes: two 16-bit fields each
-    const uint32_t r0 = tx.sum(K | (MK << 16));
-    const uint32_t r1 = tx.sum(bad | (ends << 16));
-    const uint32_t Kt = r0 & 0xFFFFu, MKt = r0 >> 16, badt = r1 & 0xFFFFu, endst = r1 >> 16;
+    // The lane holding the item that ends the chunk reports the item count,
+    // the data cursor and the match count after that item (at most one lane
+    // does, unless the items are bad).  Item counts <= 4103 (13 bits), lane
+    // counts <= 256 (9 bits), cursors <= 4 * 4103 (16 bits).
+    uint32_t endl = 0, cend = 0;
+    if (rend) {
+      const uint32_t mm = (uint32_t)__builtin_popcount(fb & ((1u << rend) - 1u));  // rend <= RMAX < 25
+      endl = (k0 + rend) | (1u << 13);
+      cend = (SPLIT ? 0u : c0 + WS * (rend - mm) + 2u * mm) | ((m0 + mm) << 16);
+    }
+    const uint32_t r0 = tx.sum(endl | ((badm ? 1u : 0u) << 22));
+    const uint32_t r1 = tx.sum(cend);
+    const uint32_t Kt = r0 & 0x1FFFu, endst = (r0 >> 13) & 0x1FFu, badt = r0 >> 22;
+    const uint32_t Dt = r1 & 0xFFFFu, MKt = r1 >> 16;
     if constexpr (SPLIT) {
       // all K items are live and cover exactly E elements, M of them are
       // matches, and the flag bits past the last item are 0
@@ -561,8 +574,7 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, uint32_t F, uin
     } else {
       // the live items cover exactly E elements, use exactly D data bytes and
       // leave no match flag set after the last of them
-      if (badt || endst != 1u || (Kt + 7u) / 8u != F || WS * (Kt - MKt) + 2u * MKt != D || MKt != mt_total)
-        return false;
+      if (badt || endst != 1u || (Kt + 7u) / 8u != F || Dt != D || MKt != mt_total) return false;
     }
   }
   team_sync<TW>();
@@ -725,7 +737,9 @@ __device__ __forceinline__ void decode_group_teams(const DecP& p, const uint8_t*
   using G = Geo<CS, WS, TEAMS>;
   constexpr uint32_t TL = G::TL;
   constexpr uint32_t CPW = kWaves / G::TW;  // chunks per workgroup
-  const uint32_t team = threadIdx.x / TL, g = threadIdx.x % TL;
+  // the team index is a wave uniform (TL is a multiple of 64): kept in a
+  // scalar register, so is every LDS base derived from it
+  const uint32_t team = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x / TL)), g = threadIdx.x % TL;
   uint8_t* arena = arena_all + team * (G::TW * kSlot);
   // The metadata of 64 of the team's chunks (size-table row and payload
   // offset) is loaded at once, one chunk per lane, and handed out by
@@ -977,7 +991,9 @@ __device__ __forceinline__ void decode_group_split(const DecP& p, const SplitDec
   using G = Geo<CS, WS>;
   constexpr uint32_t TL = G::TL;
   constexpr uint32_t CPW = kWaves / G::TW;  // chunks per workgroup
-  const uint32_t team = threadIdx.x / TL, g = threadIdx.x % TL, lane = lane_id();
+  // a wave uniform, kept in a scalar register (TL is a multiple of 64)
+  const uint32_t team = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x / TL)), g = threadIdx.x % TL,
+                 lane = lane_id();
   uint8_t* arena = arena_all + team * (G::TW * kSlot);
   const uint8_t* flags = a.meta + p.base;
   const uint64_t stride = (uint64_t)gridDim.x * CPW;
