@@ -597,10 +597,13 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, uint32_t F, uin
     // One wave: 64-element windows in order, lane i on element 64w + i.  A
     // source before the window already holds its final value; one inside it
     // is followed over the window's lanes (pointer jumping on lane indices;
-    // every link goes to a lower lane, so six rounds suffice) to a literal
-    // or to an element before the window.  The sources of four windows are
-    // found first (indices only, independent of each other), then their
-    // values are copied window by window.
+    // every link goes to a lower lane, so six rounds suffice) to an element
+    // that is final (a literal, or one whose source lies before the window).
+    // A window in which no item starts lies inside one match (items are
+    // contiguous and a literal covers one element), all of whose sources
+    // lie before it, so its sources take no start search and no jumps.  The
+    // sources of four windows are found first (indices only, independent of
+    // each other), then their values are copied window by window.
     static_assert(NB % 4u == 0u, "windows in groups of four");
 #pragma unroll 1
     for (uint32_t w0 = 0; w0 < NB; w0 += 4u) {
@@ -612,16 +615,19 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, uint32_t F, uin
       for (uint32_t j = 0; j < 4u; ++j) {
         const uint32_t w = w0 + j;
         const uint32_t base = 64u * w, q = base + lane;
-        const uint64_t m = STB[w] & upto;
-        const uint32_t st = m ? base + 63u - (uint32_t)__builtin_clzll(m)
-                              : (uint32_t)__builtin_amdgcn_readlane((int)before, (int)w);
-        const uint32_t O = OB[st];
-        const uint32_t e0 = O ? st - O + small_mod(q - st, O) : q;
-        const uint64_t lit = __ballot(O == 0u);
-        const uint32_t r = e0 - base;  // < 64 iff the source lies in this window
-        const uint32_t half = (r & 32u) ? (uint32_t)(lit >> 32) : (uint32_t)lit;
-        const bool open = O && r < 64u && __builtin_amdgcn_ubfe(half, r & 31u, 1u) == 0u;
-        x[j] = e0 | ((open ? r << 2 : 256u) << 16);
+        const uint64_t mw = STB[w];  // the same word in every lane
+        const uint32_t bw = (uint32_t)__builtin_amdgcn_readlane((int)before, (int)w);
+        if (__builtin_amdgcn_readfirstlane((int)((uint32_t)mw | (uint32_t)(mw >> 32))) == 0) {
+          const uint32_t O = OB[bw];
+          x[j] = (bw - O + small_mod(q - bw, O)) | (256u << 16);
+        } else {
+          const uint64_t m = mw & upto;
+          const uint32_t st = m ? base + 63u - (uint32_t)__builtin_clzll(m) : bw;
+          const uint32_t O = OB[st];
+          const uint32_t e0 = O ? st - O + small_mod(q - st, O) : q;
+          const uint32_t r = e0 - base;  // < 64 iff the source lies in this window
+          x[j] = e0 | ((O && r < 64u ? r << 2 : 256u) << 16);
+        }
       }
       // the four windows jump in step: one exchange per window per round
       for (uint32_t round = 0;; ++round) {
