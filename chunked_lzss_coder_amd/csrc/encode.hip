@@ -750,16 +750,32 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
                 const uint32_t pe = (uint32_t)__builtin_amdgcn_readlane((int)p, (int)e);
                 const uint32_t oe = (uint32_t)__builtin_amdgcn_readlane((int)o, (int)e);
                 const uint32_t le = (uint32_t)__builtin_amdgcn_readlane((int)lim, (int)e);
-                uint32_t re = 8u;  // its first 8 matched
-                for (uint32_t k0 = 8u; k0 < le; k0 += 64u) {
-                  const uint32_t idx = k0 + lane;
-                  const bool stop = idx >= le || XL[pe + idx] != XL[pe + idx - oe];
-                  const uint64_t sm = __ballot(stop);
-                  if (sm) {
-                    re = k0 + (uint32_t)__builtin_ctzll(sm);
-                    break;
+                // its first 8 matched; then 64 compares, and if the run goes
+                // on, the other three rounds of 64 (le <= 255) with all their
+                // words read at once, so a long run waits on two LDS latencies
+                // instead of four.  Words past the run (idx >= le) are read
+                // too, still inside the team's LDS (the regions after the
+                // words hold more than 264), and do not count.
+                uint32_t re;
+                {
+                  const uint32_t idx = 8u + lane;
+                  const uint64_t sm = __ballot(idx >= le || XL[pe + idx] != XL[pe + idx - oe]);
+                  re = sm ? 8u + (uint32_t)__builtin_ctzll(sm) : 72u;
+                }
+                if (re == 72u && le > 72u) {
+                  uint32_t xa[3], xb[3];
+#pragma unroll
+                  for (uint32_t u = 0; u < 3u; ++u) {
+                    const uint32_t idx = 72u + 64u * u + lane;
+                    xa[u] = XL[pe + idx];
+                    xb[u] = XL[pe + idx - oe];
                   }
-                  re = k0 + 64u;
+#pragma unroll
+                  for (int u = 2; u >= 0; --u) {
+                    const uint32_t idx = 72u + 64u * (uint32_t)u + lane;
+                    const uint64_t sm = __ballot(idx >= le || xa[u] != xb[u]);
+                    if (sm) re = 72u + 64u * (uint32_t)u + (uint32_t)__builtin_ctzll(sm);
+                  }
                 }
                 if (lane == e) r_end = re;
               }
