@@ -20,10 +20,14 @@
 //        items per lane): an item's data offset follows from the matches
 //        before it (flag popcounts, one team scan), its output length is 1
 //        or the token's length, and a second team scan of the lengths gives
-//        every item's output position; every token rule is checked;
+//        every item's output position; every token rule is checked (per
+//        item what only the item shows, the rest through the counts after
+//        the item that ends the chunk);
 //     b. each element of a match item points into the data before the item,
 //        start - O + (q - start) mod O, always < start; pointer jumping
-//        resolves chains in at most log2(items)+1 rounds with early exit;
+//        resolves chains in at most log2(items)+1 rounds with early exit (a
+//        one-wave chunk's 64-element windows in order, those in which no
+//        item starts without any);
 //     c. the chunk's real bytes are stored; the zero padding must have
 //        decoded to zeros.
 //   Errors only ever raise the status (and zero the length), so the kernel
