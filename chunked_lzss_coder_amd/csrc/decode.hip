@@ -448,12 +448,13 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, uint32_t F, uin
   // disagree with the chunk's sizes (checked after the walk).
   auto item_rec = [&](uint32_t cur, uint32_t m, bool mt) -> uint32_t {
     if constexpr (SPLIT) {
-      // the two kinds live in different ports: only the item's own is read
-      if (mt) return (uint32_t)LENB[m] | ((uint32_t)OFFB[m] << 8);
+      const uint32_t mr = (uint32_t)LENB[m] | ((uint32_t)OFFB[m] << 8);
       const uint8_t* w = LITB + WS * cur;
-      if constexpr (WS == 4) return *(const uint32_t*)w;  // literal words are 4-byte aligned in LDS
-      else if constexpr (WS == 2) return (uint32_t)*(const uint16_t*)w;
-      else return (uint32_t)*w;
+      uint32_t lr;
+      if constexpr (WS == 4) lr = *(const uint32_t*)w;  // literal words are 4-byte aligned in LDS
+      else if constexpr (WS == 2) lr = (uint32_t)*(const uint16_t*)w;
+      else lr = (uint32_t)*w;
+      return mt ? mr : lr;
     } else {
       const uint8_t* w = PD + cur;  // 2-byte aligned for WS >= 2
       if constexpr (WS == 4) {
