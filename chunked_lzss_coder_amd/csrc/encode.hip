@@ -715,20 +715,20 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
               lim = (uint32_t)E - p < kMaxLen ? (uint32_t)E - p : kMaxLen;
               Lnear = lo_p & 0xFFu;
               if (v != 0u && o <= kMaxFar && Lnear < lim) {
-                // One batch of loads: the word at p + Lnear (the candidate
-                // must match there to be longer) and the first 8 word pairs.
-                // Words past the chunk's end (p + 7 < E + 8) still lie in the
-                // team's LDS, since the word region is followed by other
-                // regions, and their bits are set by j >= lim anyway.
+                // The word at p + Lnear first (the candidate must match there
+                // to be longer), then, only where it does, the first 8 word
+                // pairs.  Words past the chunk's end (p + 7 < E + 8) still lie
+                // in the team's LDS, since the word region is followed by
+                // other regions, and their bits are set by j >= lim anyway.
                 const uint32_t xa = XL[p + Lnear], xb = XL[p + Lnear - o];
-                uint32_t wa[8], wb[8];
-#pragma unroll
-                for (uint32_t j = 0; j < 8u; ++j) {
-                  wa[j] = XL[p + j];
-                  wb[j] = XL[p + j - o];
-                }
                 need = xa == xb;
                 if (need) {
+                  uint32_t wa[8], wb[8];
+#pragma unroll
+                  for (uint32_t j = 0; j < 8u; ++j) {
+                    wa[j] = XL[p + j];
+                    wb[j] = XL[p + j - o];
+                  }
                   uint32_t stop = 0;
 #pragma unroll
                   for (uint32_t j = 0; j < 8u; ++j) stop |= (uint32_t)((j >= lim) | (wa[j] != wb[j])) << j;
