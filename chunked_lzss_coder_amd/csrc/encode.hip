@@ -369,11 +369,18 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
   constexpr bool PRE = L::LAZY && WS == 4 && E / ((E == 256 ? 4u : 8u) * TL) == 1u;
   for (uint32_t i = g; i < L::XPAD; i += TL) X[(int)i - (int)L::XPAD] = 0u;
   uint32_t any = 0;
+  // diff: nonzero unless every word equals the chunk's first (rep: that word
+  // repeated over 32 bits); only the aligned whole-chunk load tests it
+  uint32_t diff = 1u, rep = 0u;
   if (bc == CS && (((uintptr_t)src) & 15u) == 0) {
     const uint4* s4 = (const uint4*)src;
+    const uint32_t w0 = *(const uint32_t*)src;
+    rep = WS == 4 ? w0 : (WS == 2 ? (w0 & 0xFFFFu) * 0x10001u : (w0 & 0xFFu) * 0x01010101u);
+    diff = 0u;
     for (uint32_t i = g; i < CS / 16u; i += TL) {
       const uint4 v = s4[i];
       any |= v.x | v.y | v.z | v.w;
+      diff |= (v.x ^ rep) | (v.y ^ rep) | (v.z ^ rep) | (v.w ^ rep);
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
       if (WS == 4) {
         *(uint4*)(X + 4 * i) = v;
@@ -402,19 +409,32 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
       any |= w;
     }
   }
-  bool nonzero;
+  bool nonzero, konst;
   if (WPC == 1) {
     nonzero = __ballot(any != 0u) != 0ull;
+    konst = __ballot(diff != 0u) == 0ull;
     wave_sync();
   } else {
     nonzero = __syncthreads_or(any != 0u);
+    konst = !__syncthreads_or(diff != 0u);
   }
+  // A chunk of one repeated nonzero word (konst): the near search at every
+  // position p >= 1 finds offset 1 (the smallest) running to the cap or the
+  // chunk's end, and no farther candidate can be strictly longer, at either
+  // level and for any window.  So the greedy parse is fixed: a literal, then
+  // matches (min(255, E - p), 1) while at least MM words remain, then the
+  // remaining words as literals; its payload is written directly below.
+  konst = konst && nonzero;
 
   uint32_t K = 0, M = 0;
   // segment g's item-start and match bits, and the items (low half) and
   // matches (high half) of the segments before it
   uint32_t it8 = 0, mt8 = 0, kex = 0;
-  if (nonzero) {
+  constexpr uint32_t KN = ((uint32_t)E - 1u) / kMaxLen, KR = ((uint32_t)E - 1u) % kMaxLen;  // konst: full matches, rest
+  if (konst) {
+    M = KN + (KR >= MM ? 1u : 0u);
+    K = M + 1u + (KR >= MM ? 0u : KR);
+  } else if (nonzero) {
     // ---- 2. omask: 8 consecutive positions per lane, window in registers -------------
     Mask any_om = 0;  // OR of this lane's masks
     {
@@ -1044,7 +1064,31 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
   // realigns by DB - F bytes.
   uint32_t* STG32 = (uint32_t*)STG;
   uint32_t* slot = (uint32_t*)(staging + base);
-  if (nonzero && !raw) {
+  if (konst) {
+    // payload byte j by lane j (F + D < 64): flag bits 1 .. M set (the
+    // matches are items 1 .. M); data: the word, M tokens (255 or the rest,
+    // offset 1), then the trailing literals, each the word again
+    const uint32_t j = g;
+    if (j < F + D) {
+      uint32_t b;
+      if (j < F) {
+        const uint32_t lo = 8u * j, hi = lo + 8u;                 // items [lo, hi)
+        const uint32_t a0 = lo > 1u ? lo : 1u, a1 = hi < M + 1u ? hi : M + 1u;  // matches in it
+        b = a0 < a1 ? ((1u << (a1 - lo)) - (1u << (a0 - lo))) & 0xFFu : 0u;
+      } else {
+        const uint32_t d = j - F;
+        if (d < (uint32_t)WS) {
+          b = (rep >> (8u * d)) & 0xFFu;
+        } else if (d < (uint32_t)WS + 2u * M) {
+          const uint32_t t = d - (uint32_t)WS;
+          b = (t & 1u) ? 1u : ((t >> 1) < KN ? kMaxLen : KR);
+        } else {
+          b = (rep >> (8u * ((d - (uint32_t)WS - 2u * M) % (uint32_t)WS))) & 0xFFu;
+        }
+      }
+      (staging + base)[j] = (uint8_t)b;
+    }
+  } else if (nonzero && !raw) {
     // Lane g places the items of segment g (positions 8g .. 8g + 7): they are
     // items kex.lo .. of the chunk and their data bytes are consecutive.  The
     // segment's (L, O) and literal words are loaded before the flag words are
