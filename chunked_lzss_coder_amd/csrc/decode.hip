@@ -355,39 +355,62 @@ __device__ __forceinline__ bool decode_coded(const uint8_t* pay, uint32_t F, uin
     const uint32_t d1 = lo >> 2, d2 = mo >> 2, d3 = oo >> 2;
     const uint32_t e0 = (F + 3u) >> 2, e1 = d1 + ((WS * NL + 3u) >> 2), e2 = d2 + ((sp.M + 3u) >> 2),
                    e3 = d3 + ((sp.M + 3u) >> 2);
-#pragma unroll 1
-    for (uint32_t i0 = 0; i0 < e3; i0 += 4u * TL) {
+    if (e0 <= TL && e1 - d1 <= TL && e2 - d2 <= TL && e3 - d3 <= TL) {
+      // every region fits one dword per lane (small payloads): lane g takes
+      // dword g of each, the four regions' loads issued before any store
+      const uint8_t* const src4[4] = {sp.flags, sp.lit, sp.lens, sp.offs};
+      const uint32_t len4[4] = {F, WS * NL, sp.M, sp.M}, at4[4] = {0u, d1, d2, d3};
       uint32_t v[4];
 #pragma unroll
       for (uint32_t r = 0; r < 4u; ++r) {
-        const uint32_t i = i0 + g + r * TL;
-        const uint8_t* src = nullptr;
-        uint32_t len = 0, b = 0;
-        if (i < e0) {
-          src = sp.flags, len = F, b = i;
-        } else if (i >= d1 && i < e1) {
-          src = sp.lit, len = WS * NL, b = i - d1;
-        } else if (i >= d2 && i < e2) {
-          src = sp.lens, len = sp.M, b = i - d2;
-        } else if (i >= d3 && i < e3) {
-          src = sp.offs, len = sp.M, b = i - d3;
-        }
-        // the aligned dwords holding bytes 4b .. 4b + 3 (only those holding
-        // a byte of the region), realigned
-        uint32_t lo = 0, hi = 0, sh = 0;
-        if (src) {
-          sh = (uint32_t)((uintptr_t)src & 3u);
-          const uint32_t* A = (const uint32_t*)(src - sh);
-          const uint32_t nA = (sh + len + 3u) >> 2;
-          lo = A[b];
-          if (sh != 0u && b + 1u < nA) hi = A[b + 1u];
+        const uint32_t sh = (uint32_t)((uintptr_t)src4[r] & 3u);
+        const uint32_t* A = (const uint32_t*)(src4[r] - sh);
+        const uint32_t nA = (sh + len4[r] + 3u) >> 2;  // aligned dwords holding a byte of the region
+        uint32_t lo = 0, hi = 0;
+        if (g < ((len4[r] + 3u) >> 2)) {
+          lo = A[g];
+          if (sh != 0u && g + 1u < nA) hi = A[g + 1u];
         }
         v[r] = __builtin_amdgcn_alignbyte(hi, lo, sh);
       }
 #pragma unroll
-      for (uint32_t r = 0; r < 4u; ++r) {
-        const uint32_t i = i0 + g + r * TL;
-        if (i < e3) ((uint32_t*)PB)[i] = v[r];
+      for (uint32_t r = 0; r < 4u; ++r)
+        if (g < ((len4[r] + 3u) >> 2)) ((uint32_t*)PB)[at4[r] + g] = v[r];
+    } else {
+#pragma unroll 1
+      for (uint32_t i0 = 0; i0 < e3; i0 += 4u * TL) {
+        uint32_t v[4];
+#pragma unroll
+        for (uint32_t r = 0; r < 4u; ++r) {
+          const uint32_t i = i0 + g + r * TL;
+          const uint8_t* src = nullptr;
+          uint32_t len = 0, b = 0;
+          if (i < e0) {
+            src = sp.flags, len = F, b = i;
+          } else if (i >= d1 && i < e1) {
+            src = sp.lit, len = WS * NL, b = i - d1;
+          } else if (i >= d2 && i < e2) {
+            src = sp.lens, len = sp.M, b = i - d2;
+          } else if (i >= d3 && i < e3) {
+            src = sp.offs, len = sp.M, b = i - d3;
+          }
+          // the aligned dwords holding bytes 4b .. 4b + 3 (only those holding
+          // a byte of the region), realigned
+          uint32_t lo = 0, hi = 0, sh = 0;
+          if (src) {
+            sh = (uint32_t)((uintptr_t)src & 3u);
+            const uint32_t* A = (const uint32_t*)(src - sh);
+            const uint32_t nA = (sh + len + 3u) >> 2;
+            lo = A[b];
+            if (sh != 0u && b + 1u < nA) hi = A[b + 1u];
+          }
+          v[r] = __builtin_amdgcn_alignbyte(hi, lo, sh);
+        }
+#pragma unroll
+        for (uint32_t r = 0; r < 4u; ++r) {
+          const uint32_t i = i0 + g + r * TL;
+          if (i < e3) ((uint32_t*)PB)[i] = v[r];
+        }
       }
     }
     FL = PB;
