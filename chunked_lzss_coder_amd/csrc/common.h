@@ -303,6 +303,20 @@ __device__ __forceinline__ void zero_bytes16(uint8_t* dst, uint32_t n, uint32_t 
   if (t < n) dst[t] = 0u;
 }
 
+// Fill n bytes at dst with the 32-bit pattern rep (byte k of the run is
+// byte (k mod 4) of rep), one 16-byte block per lane of the wave per round.
+__device__ __forceinline__ void fill_bytes16(uint8_t* dst, uint32_t n, uint32_t l, uint32_t rep) {
+  const uint32_t h0 = (uint32_t)((16u - ((uintptr_t)dst & 15u)) & 15u);
+  const uint32_t h = h0 < n ? h0 : n;
+  if (l < h) dst[l] = (uint8_t)(rep >> (8u * (l & 3u)));
+  const uint32_t nb = (n - h) >> 4;
+  const uint32_t rot = __builtin_amdgcn_alignbyte(rep, rep, h & 3u);  // the pattern from byte h on
+  uint4* db = (uint4*)(dst + h);
+  for (uint32_t k = l; k < nb; k += 64u) db[k] = make_uint4(rot, rot, rot, rot);
+  const uint32_t t = h + 16u * nb + l;
+  if (t < n) dst[t] = (uint8_t)(rep >> (8u * (t & 3u)));
+}
+
 // ---- launchers (host side, one per kernel family) -------------------------
 struct EncodeArgs {
   const uint8_t* in;

@@ -837,8 +837,50 @@ __device__ __forceinline__ void decode_group_teams(const DecP& p, const uint8_t*
       else if constexpr (G::OVL) copy_bytes16_r2(dst + w0, pay + w0, len, lane);
       else copy_bytes16_r1(dst + w0, pay + w0, len, lane);
     } else {
-      if (!decode_coded<CS, WS, false, TEAMS>(pay, e.x, e.y, bc, dst, arena, sh, SplitSrc{}) && g == 0)
+      // A whole chunk of one repeated word as the encoder codes it (a
+      // literal, then matches (min(255, rest), 1) while the encoder's minimum
+      // match remains, the rest as literals) decodes to that word throughout,
+      // filled at the rate of a zero chunk.  Only a payload equal to that
+      // form byte for byte takes this route; any other is decoded and checked
+      // in full.  Every wave of the team tests the same bytes.
+      constexpr uint32_t EW = CS / WS, KN = (EW - 1u) / 255u, KR = (EW - 1u) % 255u;
+      constexpr uint32_t MMe = WS >= 4 ? 1u : (WS == 2 ? 2u : 3u);
+      constexpr uint32_t KM = KN + (KR >= MMe ? 1u : 0u), KK = KM + 1u + (KR >= MMe ? 0u : KR);
+      constexpr uint32_t KF = (KK + 7u) / 8u, KD = WS * (KK - KM) + 2u * KM;
+      static_assert(KF + KD <= 64u, "the one-word form fits one byte per lane");
+      bool one_word = false;
+      uint32_t rep = 0;
+      // (the one-wave layout of 1024-element chunks only: elsewhere the extra
+      // registers cost the coded chunks more than the shortcut saves)
+      if (G::OVL && bc == CS && e.x == KF && e.y == KD) {
+        const uint32_t j = lane;
+        const uint32_t b = j < KF + KD ? (uint32_t)pay[j] : 0u;
+        uint32_t w = 0;  // the literal word, payload bytes KF .. KF + WS
+#pragma unroll
+        for (uint32_t k = 0; k < WS; ++k) w |= (uint32_t)__builtin_amdgcn_readlane((int)b, (int)(KF + k)) << (8u * k);
+        rep = WS == 4 ? w : (WS == 2 ? w * 0x10001u : w * 0x01010101u);
+        uint32_t want;
+        if (j < KF) {
+          const uint32_t lo = 8u * j, hi = lo + 8u;
+          const uint32_t a0 = lo > 1u ? lo : 1u, a1 = hi < KM + 1u ? hi : KM + 1u;
+          want = a0 < a1 ? ((1u << (a1 - lo)) - (1u << (a0 - lo))) & 0xFFu : 0u;
+        } else {
+          const uint32_t d = j - KF;
+          if (d < WS) want = (rep >> (8u * d)) & 0xFFu;
+          else if (d < WS + 2u * KM) want = ((d - WS) & 1u) ? 1u : (((d - WS) >> 1) < KN ? 255u : KR);
+          else want = (rep >> (8u * ((d - WS - 2u * KM) % WS))) & 0xFFu;
+        }
+        one_word = __ballot(j < KF + KD && b != want) == 0ull;
+      }
+      if (one_word) {
+        constexpr uint32_t TW = G::TW;
+        const uint32_t share = ((bc + 16u * TW - 1u) / (16u * TW)) * 16u;
+        const uint32_t w0 = (g >> 6) * share;
+        const uint32_t len = w0 < bc ? (bc - w0 < share ? bc - w0 : share) : 0u;
+        fill_bytes16(dst + w0, len, lane, rep);
+      } else if (!decode_coded<CS, WS, false, TEAMS>(pay, e.x, e.y, bc, dst, arena, sh, SplitSrc{}) && g == 0) {
         raise_status(status, out_bytes, kStatusCorrupt);
+      }
     }
     team_sync<G::TW>();
   }
