@@ -31,7 +31,7 @@ def sources() -> list[str]:
 
 def build(verbose: bool = False) -> str:
     out = os.path.join(_HERE, "libgpulz.so")
-    tmp = out + ".tmp"
+    tmp = f"{out}.{os.getpid()}.tmp"  # one per process: concurrent builds do not collide
     cmd = [HIPCC, *FLAGS, "-I", os.path.join(_ROOT, "include"), "-I", os.path.join(_HERE, "csrc"),
            *sources(), "-o", tmp]
     if verbose:

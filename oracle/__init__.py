@@ -33,7 +33,7 @@ RAW_BIT = 0x80000000
 
 def build(verbose: bool = False) -> str:
     """Compile liboracle.so with gcc (always recompiles)."""
-    tmp = _LIB_PATH + ".tmp"
+    tmp = f"{_LIB_PATH}.{os.getpid()}.tmp"  # one per process: concurrent builds do not collide
     cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd))
