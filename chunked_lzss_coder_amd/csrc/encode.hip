@@ -629,15 +629,14 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
           }
           team_sync<WPC>();
         }
-        uint32_t lo[PPL];
-#pragma unroll
-        for (uint32_t i = 0; i < PPL; ++i) {
-          const uint32_t p = g + i * TL;
+        // The descent at p: digits of L in base 4, most significant first, at
+        // most 3 steps of k per round, so L <= 3 * (64 + 16 + 4 + 1) = 255, the
+        // length cap.  Without the rounds of 64 and 16 (full false) it finds
+        // exactly the lengths below 16.
+        auto descend = [&](uint32_t p, bool full) -> uint32_t {
           Mask surv = ~(Mask)0;
           uint32_t Ln = 0;
-          // digits of L in base 4, most significant first: at most 3 steps of k per
-          // round, so L <= 3 * (64 + 16 + 4 + 1) = 255, the length cap
-          {
+          if (full) {
             // round of k = 64 (Ln = 0): S_64 at p, p + 64, p + 128 from S_16,
             // reads up to p + 176, inside S_16's padding (or guarded)
             const Mask* S = LVm + L::TOFF[2] + p;
@@ -656,6 +655,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
           }
 #pragma unroll
           for (int lv = 2; lv >= 0; --lv) {
+            if (lv == 2 && !full) continue;
             const uint32_t k = 1u << (2 * lv);
             // p + Ln <= E (every surviving position is inside the chunk), so the
             // three reads end within the table's padding
@@ -666,7 +666,22 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             Ln += n << (2 * lv);
           }
           const uint32_t o = W > 32 ? (uint32_t)__builtin_ctzll((uint64_t)surv) : (uint32_t)__builtin_ctz((uint32_t)surv);
-          lo[i] = Ln ? (Ln | ((o + 1u) << 8)) : 0u;
+          return Ln ? (Ln | ((o + 1u) << 8)) : 0u;
+        };
+        // A wave none of whose positions g + i TL has S_16 non-empty (no
+        // length of 16 or more; S_64 lies inside S_16) gains nothing from the
+        // rounds of 64 and 16 and skips them there: most positions of most
+        // data have short lengths only.  The votes come first, so that each
+        // position takes one of the two descents (a wave-uniform branch).
+        uint32_t lo[PPL];
+        uint32_t longm = 0;  // bit i: the wave has a long length among positions g + i TL
+#pragma unroll
+        for (uint32_t i = 0; i < PPL; ++i)
+          if (__ballot(LVm[L::TOFF[2] + g + i * TL] != (Mask)0) != 0ull) longm |= 1u << i;
+#pragma unroll
+        for (uint32_t i = 0; i < PPL; ++i) {
+          if ((longm >> i) & 1u) lo[i] = descend(g + i * TL, true);
+          else lo[i] = descend(g + i * TL, false);
         }
         team_sync<WPC>();
 #pragma unroll
