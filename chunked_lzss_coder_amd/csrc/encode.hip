@@ -294,7 +294,7 @@ struct Lay {
   static constexpr uint32_t R =
       LAZY ? ((LZ_R + 3u) & ~3u)
            : (cmax(cmax(SEARCH, LEVEL ? (XL ? 2u : 1u) * E + TW_ : 0u), RP) + 3u) & ~3u;
-  static constexpr uint32_t MISC = (LAZY && WPC_ == 1u) ? 0u : 2u * (E / 64u + 1u) + 8u;
+  static constexpr uint32_t MISC = WPC_ > 1u ? 8u : 0u;  // a team's per-wave counts (multi-wave chunks)
   // 32 zero words ahead of X (32-offset window): every lane of the offset-mask
   // pass loads its 32 + 8 words with the same 16-byte loads, the first lanes'
   // window running into the zeros (the bits they give are masked off)
@@ -343,10 +343,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
     if constexpr (L::LAZY) return (LO[p] >> 16) | ((uint32_t)IM[p] << 16);
     else return XQ[p];
   };
-  uint32_t* MISC = LV + L::R;
-  uint32_t* KB = MISC;                   // items before 64-position word w
-  uint32_t* MB = MISC + (E / 64u + 1u);  // matches before word w
-  uint32_t* SC = MB + (E / 64u + 1u);    // scalars
+  uint32_t* KB = LV + L::R;  // per wave of a multi-wave team: its item and match counts
   uint8_t* table = out + kHeaderBytes;
 
   // ---- chunk of this team -----------------------------------------------------------
@@ -861,39 +858,36 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
           const uint4 a = *(const uint4*)(LO + p0);
           const uint4 b = *(const uint4*)(LO + p0 + 4);
           const uint32_t l8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-          uint32_t ex[8], im[8], lmb = 0;
+          // pk[q]: the exit of the walk from entry q, and its item-start bits
+          // << 16 (the exit table's own format)
+          uint32_t pk[8], lmb = 0;
 #pragma unroll
           for (int q = 7; q >= 0; --q) {
             const uint32_t len = l8[q] & 0xFFu;
             const bool mt = len >= MM;
             lmb |= (mt ? 1u : 0u) << q;
             const uint32_t nq = (uint32_t)q + (mt ? len : 1u);
-            uint32_t e = p0 + nq, m = 1u << q;
+            uint32_t v = p0 + nq;  // leaves the segment at once
 #pragma unroll
             for (int r = q + 1; r < 8; ++r)
-              if (nq == (uint32_t)r) {
-                e = ex[r];
-                m = (1u << q) | im[r];
-              }
+              if (nq == (uint32_t)r) v = pk[r];
             // a long match starts here: its length is found when the parse
             // gets here, so the exit names this position
-            if (L::LAZY && l8[q] == kLongMark) e = (p0 + (uint32_t)q) | kLongExit;
-            ex[q] = e;
-            im[q] = m;
+            if (L::LAZY && l8[q] == kLongMark) v = (p0 + (uint32_t)q) | kLongExit;
+            pk[q] = v | (1u << (16 + q));
           }
           if constexpr (L::LAZY) {
             // the exit beside (L, O), the bits in their own bytes
-            *(uint4*)(LO + p0) = make_uint4((l8[0] & 0xFFFFu) | (ex[0] << 16), (l8[1] & 0xFFFFu) | (ex[1] << 16),
-                                            (l8[2] & 0xFFFFu) | (ex[2] << 16), (l8[3] & 0xFFFFu) | (ex[3] << 16));
-            *(uint4*)(LO + p0 + 4) = make_uint4((l8[4] & 0xFFFFu) | (ex[4] << 16), (l8[5] & 0xFFFFu) | (ex[5] << 16),
-                                                (l8[6] & 0xFFFFu) | (ex[6] << 16), (l8[7] & 0xFFFFu) | (ex[7] << 16));
-            *(uint2*)(IM + p0) = make_uint2(im[0] | (im[1] << 8) | (im[2] << 16) | (im[3] << 24),
-                                            im[4] | (im[5] << 8) | (im[6] << 16) | (im[7] << 24));
+            *(uint4*)(LO + p0) = make_uint4((l8[0] & 0xFFFFu) | (pk[0] << 16), (l8[1] & 0xFFFFu) | (pk[1] << 16),
+                                            (l8[2] & 0xFFFFu) | (pk[2] << 16), (l8[3] & 0xFFFFu) | (pk[3] << 16));
+            *(uint4*)(LO + p0 + 4) = make_uint4((l8[4] & 0xFFFFu) | (pk[4] << 16), (l8[5] & 0xFFFFu) | (pk[5] << 16),
+                                                (l8[6] & 0xFFFFu) | (pk[6] << 16), (l8[7] & 0xFFFFu) | (pk[7] << 16));
+            *(uint2*)(IM + p0) = make_uint2(
+                ((pk[0] >> 16) & 0xFFu) | ((pk[1] >> 8) & 0xFF00u) | (pk[2] & 0xFF0000u) | ((pk[3] << 8) & 0xFF000000u),
+                ((pk[4] >> 16) & 0xFFu) | ((pk[5] >> 8) & 0xFF00u) | (pk[6] & 0xFF0000u) | ((pk[7] << 8) & 0xFF000000u));
           } else {
-            *(uint4*)(XQ + p0) = make_uint4(ex[0] | (im[0] << 16), ex[1] | (im[1] << 16), ex[2] | (im[2] << 16),
-                                            ex[3] | (im[3] << 16));
-            *(uint4*)(XQ + p0 + 4) = make_uint4(ex[4] | (im[4] << 16), ex[5] | (im[5] << 16),
-                                                ex[6] | (im[6] << 16), ex[7] | (im[7] << 16));
+            *(uint4*)(XQ + p0) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+            *(uint4*)(XQ + p0 + 4) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
           }
           ((uint8_t*)LMB)[sg] = (uint8_t)lmb;
           if (WPC > 1) ((uint8_t*)ISB)[sg] = 0;
@@ -979,7 +973,10 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             // idle for E / 8 hops): two levels of hops.  First, for every
             // position p, where the parse leaves p's 64-position word if it
             // enters the word at p (at most 8 segment hops: a segment's exit
-            // lies past its end), all positions at once.  Then the first wave
+            // lies past its end), all positions at once: a wave holds one
+            // word's segment exits at a time, lane j position 64w + j, so a
+            // hop is a lane exchange, and three rounds of pointer doubling
+            // cover the 8 hops.  Then the first wave
             // follows the real parse one word at a time (at most NR hops, one
             // readlane each) and lane w rebuilds word w's item-start bits from
             // its real entry (at most 8 hops).  WX, a u16 per position, uses
@@ -989,15 +986,19 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             static_assert(WS >= 2 || L::RP + E / 2u <= L::R, "word exits fit past the parse region");
             uint16_t* WX = (uint16_t*)(WS >= 2 ? (uint32_t*)STG : LV + L::RP);
             {
+              // P[i]: where the parse is after 2^r segment hops from
+              // position g + i TL, or the word exit once it has left the
+              // word (every exit inside the word lies in this wave's lanes)
               uint32_t P[PPL];
 #pragma unroll
-              for (uint32_t i = 0; i < PPL; ++i) P[i] = g + i * TL;
+              for (uint32_t i = 0; i < PPL; ++i) P[i] = XQ[g + i * TL] & 0xFFFFu;
 #pragma unroll
-              for (uint32_t h = 0; h < 8u; ++h) {
+              for (uint32_t r = 0; r < 3u; ++r) {
 #pragma unroll
                 for (uint32_t i = 0; i < PPL; ++i) {
                   const uint32_t wend = ((g + i * TL) | 63u) + 1u;
-                  if (P[i] < wend) P[i] = XQ[P[i]] & 0xFFFFu;
+                  const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((P[i] & 63u) << 2), (int)P[i]);
+                  if (P[i] < wend) P[i] = y;
                 }
               }
 #pragma unroll
@@ -1005,15 +1006,22 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             }
             team_sync<WPC>();
             if (g < 64u) {
+              // every word's exits in registers first, two to a register
+              // (word w in half w & 1 of register w / 2, lane j: position
+              // 64w + j), so that each hop is one readlane and no hop waits
+              // for a load
+              static_assert(NR % 2u == 0u, "word exits in pairs");
+              uint32_t wxp[NR / 2u];
+#pragma unroll
+              for (uint32_t k = 0; k < NR / 2u; ++k)
+                wxp[k] = (uint32_t)WX[128u * k + lane] | ((uint32_t)WX[128u * k + 64u + lane] << 16);
               uint32_t P = 0, ent = 0xFFFFu;  // lane w: the parse's entry into word w
-              uint32_t wx_next = WX[lane];
-#pragma unroll 1
+#pragma unroll
               for (uint32_t w = 0; w < NR; ++w) {
-                const uint32_t wx = wx_next;
-                if (w + 1u < NR) wx_next = WX[64u * (w + 1u) + lane];
                 if (P < 64u * (w + 1u)) {  // else a match spans the whole word
                   if (lane == w) ent = P;
-                  P = (uint32_t)__builtin_amdgcn_readlane((int)wx, (int)(P & 63u));
+                  const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)wxp[w / 2u], (int)(P & 63u));
+                  P = (w & 1u) ? v >> 16 : v & 0xFFFFu;
                 }
               }
               uint64_t acc = 0;
