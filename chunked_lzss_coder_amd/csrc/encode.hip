@@ -890,157 +890,146 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             *(uint4*)(XQ + p0 + 4) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
           }
           ((uint8_t*)LMB)[sg] = (uint8_t)lmb;
-          if (WPC > 1) ((uint8_t*)ISB)[sg] = 0;
         }
         team_sync<WPC>();
         // (b) hops: the parse's real entry into every segment it passes through
-        if constexpr (WPC == 1) {
-          // exits held in registers (lane j of word i = position 64i + j); the hop
-          // position P is uniform, so each hop is one readlane
-          uint32_t xqr[NR];
+        if constexpr (WPC < 4) {
+          // One or two waves (up to 16 words): the first wave does it all, in
+          // three steps.  First, for every position p, where the parse leaves
+          // p's 64-position word if it enters the word at p: one word at a
+          // time, lane j on position 64w + j, a segment hop is a lane
+          // exchange and three rounds of pointer doubling cover the word's 8
+          // segments.  A long-match exit (level 0: flagged, past every word
+          // bound) ends a chain like a word exit.  The exits stay in
+          // registers, two 16-bit ones to a register.  Second, the parse
+          // itself, a word at a time (one readlane per hop; where a long
+          // match starts, the wave finds its exact length, stores it and
+          // goes on after it).  Third, lane w rebuilds word w's item-start
+          // bits from the parse's first entry into the word (at most 8 hops,
+          // the lengths of long matches read back).
+          static_assert(NR % 2u == 0u && NR <= 64u, "word exits in pairs, one lane per word");
+          if (g < 64u) {
+            uint32_t wxp[NR / 2u];
 #pragma unroll
-          for (uint32_t i = 0; i < NR; ++i) {
-            const uint32_t p = 64u * i + lane;
-            xqr[i] = xq_at(p);
-          }
-          // The walk only records where it enters each segment (one scalar
-          // bit per hop); each segment's item starts are then read from its
-          // exit table by the lanes of the segment, all words at once.  A
-          // long-match exit (flagged, so past every word bound) leaves the
-          // inner walk to have the match's length found.
-          uint32_t P = 0;
-#pragma unroll
-          for (uint32_t i = 0; i < NR; ++i) {
-            uint64_t ent = 0;
-            while (true) {
-              while (P < 64u * (i + 1u)) {
-                ent |= 1ull << (P & 63u);
-                P = __builtin_amdgcn_readlane(xqr[i], P & 63u) & 0xFFFFu;
-              }
-              if (!(L::LAZY && (P & kLongExit))) break;
-              const uint32_t r = P & ~kLongExit;  // a long match starts at r
-              const uint32_t v = long_match(LV, r, (uint32_t)E);
-              if (lane == 0u) *(uint16_t*)(LO + r) = (uint16_t)v;  // (L, O); the exit half stays
-              P = r + ((v & 0xFFu) ? (v & 0xFFu) : 1u);  // L >= 16 here; the select only guards progress
-            }
-            // lane j: segment j >> 3 of the word, entered at most once
-            const uint32_t sb = lane & 56u;
-            const uint32_t se = (uint32_t)(ent >> sb) & 0xFFu;
-            const uint32_t q0 = se ? (uint32_t)__builtin_ctz(se) : 0u;
-            const uint32_t xe = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((sb + q0) << 2), (int)xqr[i]);
-            // the segment's item-start bits: those of its walk from the entry
-            if ((lane & 7u) == 0u) ((uint8_t*)ISB)[8u * i + (lane >> 3)] = se ? (uint8_t)(xe >> 16) : (uint8_t)0;
-          }
-          wave_sync();
-        } else {
-          if constexpr (WPC < 4) {
-            // two waves: the first wave hops word by word (the other's chunk
-            // work is done; other workgroups keep the CU busy meanwhile): the
-            // exits of 64 positions in one VGPR (the next word's load in
-            // flight), one readlane per hop
-            if (g < 64u) {
-              uint64_t* IS64w = (uint64_t*)ISB;
-              uint32_t P = 0;
-              uint32_t xq_next = xq_at(lane);
-#pragma unroll 1
-              for (uint32_t i = 0; i < NR; ++i) {
-                const uint32_t xqr = xq_next;
-                if (i + 1u < NR) xq_next = xq_at(64u * (i + 1u) + lane);
-                // entries only, as in the one-wave walk
-                uint64_t ent = 0;
-                while (true) {
-                  while (P < 64u * (i + 1u)) {
-                    ent |= 1ull << (P & 63u);
-                    P = __builtin_amdgcn_readlane(xqr, P & 63u) & 0xFFFFu;
-                  }
-                  if (!(L::LAZY && (P & kLongExit))) break;
-                  const uint32_t r = P & ~kLongExit;  // a long match starts at r
-                  const uint32_t v = long_match(LV, r, (uint32_t)E);
-                  if (lane == 0u) *(uint16_t*)(LO + r) = (uint16_t)v;  // (L, O); the exit half stays
-                  P = r + ((v & 0xFFu) ? (v & 0xFFu) : 1u);  // L >= 16 here; the select only guards progress
-                }
-                const uint32_t sb = lane & 56u;
-                const uint32_t se = (uint32_t)(ent >> sb) & 0xFFu;
-                const uint32_t q0 = se ? (uint32_t)__builtin_ctz(se) : 0u;
-                const uint32_t xe = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((sb + q0) << 2), (int)xqr);
-                const uint64_t acc = __ballot(se != 0u && ((xe >> (16u + (lane & 7u))) & 1u));
-                if (lane == 0u) IS64w[i] = acc;
-              }
-            }
-            team_sync<WPC>();
-          } else {
-            // four or more waves (a serial walk would leave all but one of them
-            // idle for E / 8 hops): two levels of hops.  First, for every
-            // position p, where the parse leaves p's 64-position word if it
-            // enters the word at p (at most 8 segment hops: a segment's exit
-            // lies past its end), all positions at once: a wave holds one
-            // word's segment exits at a time, lane j position 64w + j, so a
-            // hop is a lane exchange, and three rounds of pointer doubling
-            // cover the 8 hops.  Then the first wave
-            // follows the real parse one word at a time (at most NR hops, one
-            // readlane each) and lane w rebuilds word w's item-start bits from
-            // its real entry (at most 8 hops).  WX, a u16 per position, uses
-            // space that is free here: the staging area (word sizes 2 and 4)
-            // or the dead search tables past the parse region (word size 1).
-            static_assert(NR <= 64u, "one lane per 64-position word");
-            static_assert(WS >= 2 || L::RP + E / 2u <= L::R, "word exits fit past the parse region");
-            uint16_t* WX = (uint16_t*)(WS >= 2 ? (uint32_t*)STG : LV + L::RP);
-            {
-              // P[i]: where the parse is after 2^r segment hops from
-              // position g + i TL, or the word exit once it has left the
-              // word (every exit inside the word lies in this wave's lanes)
-              uint32_t P[PPL];
-#pragma unroll
-              for (uint32_t i = 0; i < PPL; ++i) P[i] = XQ[g + i * TL] & 0xFFFFu;
+            for (uint32_t k = 0; k < NR; ++k) {
+              const uint32_t wend = 64u * (k + 1u);
+              uint32_t x = xq_at(64u * k + lane) & 0xFFFFu;
 #pragma unroll
               for (uint32_t r = 0; r < 3u; ++r) {
-#pragma unroll
-                for (uint32_t i = 0; i < PPL; ++i) {
-                  const uint32_t wend = ((g + i * TL) | 63u) + 1u;
-                  const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((P[i] & 63u) << 2), (int)P[i]);
-                  if (P[i] < wend) P[i] = y;
-                }
+                const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((x & 63u) << 2), (int)x);
+                if (x < wend) x = y;
               }
-#pragma unroll
-              for (uint32_t i = 0; i < PPL; ++i) WX[g + i * TL] = (uint16_t)P[i];
+              if (k & 1u) wxp[k / 2u] |= x << 16;
+              else wxp[k / 2u] = x;
             }
-            team_sync<WPC>();
-            if (g < 64u) {
-              // every word's exits in registers first, two to a register
-              // (word w in half w & 1 of register w / 2, lane j: position
-              // 64w + j), so that each hop is one readlane and no hop waits
-              // for a load
-              static_assert(NR % 2u == 0u, "word exits in pairs");
-              uint32_t wxp[NR / 2u];
+            uint32_t P = 0, ent = 0xFFFFu;  // lane w: the parse's first entry into word w
 #pragma unroll
-              for (uint32_t k = 0; k < NR / 2u; ++k)
-                wxp[k] = (uint32_t)WX[128u * k + lane] | ((uint32_t)WX[128u * k + 64u + lane] << 16);
-              uint32_t P = 0, ent = 0xFFFFu;  // lane w: the parse's entry into word w
-#pragma unroll
-              for (uint32_t w = 0; w < NR; ++w) {
-                if (P < 64u * (w + 1u)) {  // else a match spans the whole word
-                  if (lane == w) ent = P;
-                  const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)wxp[w / 2u], (int)(P & 63u));
-                  P = (w & 1u) ? v >> 16 : v & 0xFFFFu;
+            for (uint32_t w = 0; w < NR; ++w) {
+              if (lane == w && P < 64u * (w + 1u)) ent = P;
+              while (P < 64u * (w + 1u)) {
+                const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)wxp[w / 2u], (int)(P & 63u));
+                const uint32_t X = (w & 1u) ? v >> 16 : v & 0xFFFFu;
+                if (L::LAZY && (X & kLongExit)) {
+                  const uint32_t r = X & ~kLongExit;  // a long match starts at r
+                  const uint32_t lv = long_match(LV, r, (uint32_t)E);
+                  if (lane == 0u) *(uint16_t*)(LO + r) = (uint16_t)lv;  // (L, O); the exit half stays
+                  P = r + ((lv & 0xFFu) ? (lv & 0xFFu) : 1u);  // L >= 16 here; the select only guards progress
+                } else {
+                  P = X;
                 }
               }
-              uint64_t acc = 0;
-              if (lane < NR && ent != 0xFFFFu) {
-                const uint32_t wend = 64u * (lane + 1u);
-                uint32_t Q = ent;
+            }
+            wave_sync();  // the long matches' lengths, before the rebuild reads them
+            uint64_t acc = 0;
+            if (lane < NR && ent != 0xFFFFu) {
+              // a segment's exit lies past its end, and a long match found in
+              // a segment ends at least 16 positions on: each hop passes a
+              // segment
+              const uint32_t wend = 64u * (lane + 1u);
+              uint32_t Q = ent;
 #pragma unroll
-                for (uint32_t h = 0; h < 8u; ++h) {
-                  if (Q < wend) {
-                    const uint32_t xq = XQ[Q];
-                    acc |= (uint64_t)(xq >> 16) << (Q & 56u);
-                    Q = xq & 0xFFFFu;
+              for (uint32_t h = 0; h < 8u; ++h) {
+                if (Q < wend) {
+                  const uint32_t xq = xq_at(Q);
+                  acc |= (uint64_t)((xq >> 16) & 0xFFu) << (Q & 56u);
+                  uint32_t X = xq & 0xFFFFu;
+                  if (L::LAZY && (X & kLongExit)) {
+                    const uint32_t r = X & ~kLongExit;
+                    const uint32_t Lr = LO[r] & 0xFFu;
+                    X = r + (Lr ? Lr : 1u);
                   }
+                  Q = X;
                 }
               }
-              if (lane < NR) ((uint64_t*)ISB)[lane] = acc;
             }
-            team_sync<WPC>();
+            if (lane < NR) ((uint64_t*)ISB)[lane] = acc;
           }
+          team_sync<WPC>();
+        } else {
+          // four or more waves: the same three steps, the first one shared by
+          // all waves (a wave takes one word at a time, all positions at
+          // once), its exits passed to the first wave through WX, a u16 per
+          // position (there are no long-match exits here).  WX uses
+          // space that is free here: the staging area (word sizes 2 and 4)
+          // or the dead search tables past the parse region (word size 1).
+          static_assert(NR <= 64u, "one lane per 64-position word");
+          static_assert(WS >= 2 || L::RP + E / 2u <= L::R, "word exits fit past the parse region");
+          uint16_t* WX = (uint16_t*)(WS >= 2 ? (uint32_t*)STG : LV + L::RP);
+          {
+            // P[i]: where the parse is after 2^r segment hops from
+            // position g + i TL, or the word exit once it has left the
+            // word (every exit inside the word lies in this wave's lanes)
+            uint32_t P[PPL];
+#pragma unroll
+            for (uint32_t i = 0; i < PPL; ++i) P[i] = XQ[g + i * TL] & 0xFFFFu;
+#pragma unroll
+            for (uint32_t r = 0; r < 3u; ++r) {
+#pragma unroll
+              for (uint32_t i = 0; i < PPL; ++i) {
+                const uint32_t wend = ((g + i * TL) | 63u) + 1u;
+                const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((P[i] & 63u) << 2), (int)P[i]);
+                if (P[i] < wend) P[i] = y;
+              }
+            }
+#pragma unroll
+            for (uint32_t i = 0; i < PPL; ++i) WX[g + i * TL] = (uint16_t)P[i];
+          }
+          team_sync<WPC>();
+          if (g < 64u) {
+            // every word's exits in registers first, two to a register
+            // (word w in half w & 1 of register w / 2, lane j: position
+            // 64w + j), so that each hop is one readlane and no hop waits
+            // for a load
+            static_assert(NR % 2u == 0u, "word exits in pairs");
+            uint32_t wxp[NR / 2u];
+#pragma unroll
+            for (uint32_t k = 0; k < NR / 2u; ++k)
+              wxp[k] = (uint32_t)WX[128u * k + lane] | ((uint32_t)WX[128u * k + 64u + lane] << 16);
+            uint32_t P = 0, ent = 0xFFFFu;  // lane w: the parse's entry into word w
+#pragma unroll
+            for (uint32_t w = 0; w < NR; ++w) {
+              if (P < 64u * (w + 1u)) {  // else a match spans the whole word
+                if (lane == w) ent = P;
+                const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)wxp[w / 2u], (int)(P & 63u));
+                P = (w & 1u) ? v >> 16 : v & 0xFFFFu;
+              }
+            }
+            uint64_t acc = 0;
+            if (lane < NR && ent != 0xFFFFu) {
+              const uint32_t wend = 64u * (lane + 1u);
+              uint32_t Q = ent;
+#pragma unroll
+              for (uint32_t h = 0; h < 8u; ++h) {
+                if (Q < wend) {
+                  const uint32_t xq = XQ[Q];
+                  acc |= (uint64_t)(xq >> 16) << (Q & 56u);
+                  Q = xq & 0xFFFFu;
+                }
+              }
+            }
+            if (lane < NR) ((uint64_t*)ISB)[lane] = acc;
+          }
+          team_sync<WPC>();
         }
         // ---- 6. counts: lane g takes segment g (there are never more
         // segments than lanes); one packed scan gives the items and matches
