@@ -909,18 +909,20 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
           // the lengths of long matches read back).
           static_assert(NR % 2u == 0u && NR <= 64u, "word exits in pairs, one lane per word");
           if (g < 64u) {
+            // (positions are carried times 4, the byte address of their lane:
+            // ds_bpermute ignores the bits above the lane index)
             uint32_t wxp[NR / 2u];
 #pragma unroll
             for (uint32_t k = 0; k < NR; ++k) {
-              const uint32_t wend = 64u * (k + 1u);
-              uint32_t x = xq_at(64u * k + lane) & 0xFFFFu;
+              const uint32_t wend4 = 256u * (k + 1u);
+              uint32_t x4 = (xq_at(64u * k + lane) & 0xFFFFu) << 2;
 #pragma unroll
               for (uint32_t r = 0; r < 3u; ++r) {
-                const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((x & 63u) << 2), (int)x);
-                if (x < wend) x = y;
+                const uint32_t y4 = (uint32_t)__builtin_amdgcn_ds_bpermute((int)x4, (int)x4);
+                if (x4 < wend4) x4 = y4;
               }
-              if (k & 1u) wxp[k / 2u] |= x << 16;
-              else wxp[k / 2u] = x;
+              if (k & 1u) wxp[k / 2u] |= (x4 >> 2) << 16;
+              else wxp[k / 2u] = x4 >> 2;
             }
             uint32_t P = 0, ent = 0xFFFFu;  // lane w: the parse's first entry into word w
 #pragma unroll
@@ -978,21 +980,22 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
           {
             // P[i]: where the parse is after 2^r segment hops from
             // position g + i TL, or the word exit once it has left the
-            // word (every exit inside the word lies in this wave's lanes)
+            // word (every exit inside the word lies in this wave's lanes);
+            // carried times 4, the byte address of the lane, as above
             uint32_t P[PPL];
 #pragma unroll
-            for (uint32_t i = 0; i < PPL; ++i) P[i] = XQ[g + i * TL] & 0xFFFFu;
+            for (uint32_t i = 0; i < PPL; ++i) P[i] = (XQ[g + i * TL] & 0xFFFFu) << 2;
 #pragma unroll
             for (uint32_t r = 0; r < 3u; ++r) {
 #pragma unroll
               for (uint32_t i = 0; i < PPL; ++i) {
-                const uint32_t wend = ((g + i * TL) | 63u) + 1u;
-                const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute((int)((P[i] & 63u) << 2), (int)P[i]);
-                if (P[i] < wend) P[i] = y;
+                const uint32_t wend4 = (((g + i * TL) | 63u) + 1u) << 2;
+                const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute((int)P[i], (int)P[i]);
+                if (P[i] < wend4) P[i] = y;
               }
             }
 #pragma unroll
-            for (uint32_t i = 0; i < PPL; ++i) WX[g + i * TL] = (uint16_t)P[i];
+            for (uint32_t i = 0; i < PPL; ++i) WX[g + i * TL] = (uint16_t)(P[i] >> 2);
           }
           team_sync<WPC>();
           if (g < 64u) {
