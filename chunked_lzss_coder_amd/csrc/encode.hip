@@ -858,36 +858,80 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
           const uint4 a = *(const uint4*)(LO + p0);
           const uint4 b = *(const uint4*)(LO + p0 + 4);
           const uint32_t l8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-          // pk[q]: the exit of the walk from entry q, and its item-start bits
-          // << 16 (the exit table's own format)
-          uint32_t pk[8], lmb = 0;
+          // Byte q of a lo / hi pair of words describes position p0 + q (q < 4
+          // in lo).  perm(h, l, s) is v_perm_b32: byte i of the result is byte
+          // s_i of the 8-byte table {h:l} (0-7), or 0 for s_i = 12, so it
+          // looks up eight bytes at once by a word of byte indices.
+          auto perm = [](uint32_t h, uint32_t l, uint32_t sel) -> uint32_t {
+            return __builtin_amdgcn_perm(h, l, sel);
+          };
+          constexpr uint32_t H = 0x80808080u;
+          // per-byte unsigned a >= b for bytes b < 128: bit 7 of each byte
+          auto ge = [](uint32_t a, uint32_t b) -> uint32_t { return (((a | H) - b) | a) & H; };
+          auto full = [](uint32_t t) -> uint32_t { return (t - (t >> 7)) | t; };  // bit 7 -> 0xFF
+          // the lengths (low byte of each (L, O))
+          const uint32_t LEN[2] = {perm(l8[1], l8[0], 0x0c0c0400u) | perm(l8[3], l8[2], 0x04000c0cu),
+                                   perm(l8[5], l8[4], 0x0c0c0400u) | perm(l8[7], l8[6], 0x04000c0cu)};
+          constexpr uint32_t THR[2] = {0x05060708u, 0x01020304u};  // 8 - q
+          constexpr uint32_t QI[2] = {0x03020100u, 0x07060504u};   // q
+          uint32_t MT[2], STEP[2], N[2], I[2] = {0x08040201u, 0x80402010u}, LG[2];
 #pragma unroll
-          for (int q = 7; q >= 0; --q) {
-            const uint32_t len = l8[q] & 0xFFu;
-            const bool mt = len >= MM;
-            lmb |= (mt ? 1u : 0u) << q;
-            const uint32_t nq = (uint32_t)q + (mt ? len : 1u);
-            uint32_t v = p0 + nq;  // leaves the segment at once
-#pragma unroll
-            for (int r = q + 1; r < 8; ++r)
-              if (nq == (uint32_t)r) v = pk[r];
-            // a long match starts here: its length is found when the parse
-            // gets here, so the exit names this position
-            if (L::LAZY && l8[q] == kLongMark) v = (p0 + (uint32_t)q) | kLongExit;
-            pk[q] = v | (1u << (16 + q));
+          for (uint32_t h = 0; h < 2u; ++h) {
+            MT[h] = full(ge(LEN[h], MM * 0x01010101u));                       // a match starts here
+            STEP[h] = (MT[h] & LEN[h]) | (~MT[h] & 0x01010101u);              // its item's length
+            const uint32_t out = full(ge(STEP[h], THR[h]));                   // the item leaves the segment
+            N[h] = QI[h] + (STEP[h] & ~out);                                  // next entry (itself if out)
+            // level 0: a long mark (length byte 0xFF, all others below 16)
+            // ends the walk at its own position with a flagged exit
+            LG[h] = L::LAZY ? full(LEN[h] & H) : 0u;
           }
+          // pointer doubling on the segment: after round r, N = the entry
+          // 2^r items on (or the last one, whose item leaves), I = the item
+          // starts passed on the way (7 items at most: three rounds)
+#pragma unroll
+          for (uint32_t r = 0; r < 3u; ++r) {
+            const uint32_t i0 = I[0] | perm(I[1], I[0], N[0]), i1 = I[1] | perm(I[1], I[0], N[1]);
+            const uint32_t n0 = perm(N[1], N[0], N[0]), n1 = perm(N[1], N[0], N[1]);
+            I[0] = i0, I[1] = i1, N[0] = n0, N[1] = n1;
+          }
+          // exit = p0 + last + its length (long mark: p0 + last, flagged);
+          // two exits per word, one in each 16-bit half
+          const uint32_t SX[2] = {STEP[0] & ~LG[0], STEP[1] & ~LG[1]};
+          const uint32_t P0P0 = p0 | (p0 << 16);
+          uint32_t ex2[4];
+#pragma unroll
+          for (uint32_t h = 0; h < 2u; ++h) {
+            const uint32_t sf = perm(SX[1], SX[0], N[h]);
+            const uint32_t lf = L::LAZY ? perm(LG[1], LG[0], N[h]) : 0u;
+#pragma unroll
+            for (uint32_t k = 0; k < 2u; ++k) {
+              const uint32_t sel = k ? 0x0c030c02u : 0x0c010c00u;  // bytes 2k, 2k + 1 to the halves
+              uint32_t e = perm(0u, N[h], sel) + perm(0u, sf, sel) + P0P0;
+              if constexpr (L::LAZY) e |= perm(0u, lf, k ? 0x030c020cu : 0x010c000cu) & 0x80008000u;
+              ex2[2u * h + k] = e;
+            }
+          }
+          const uint32_t lmb = __builtin_amdgcn_sad_u8(MT[1] & 0x80402010u, 0u,
+                                                       __builtin_amdgcn_sad_u8(MT[0] & 0x08040201u, 0u, 0u));
           if constexpr (L::LAZY) {
             // the exit beside (L, O), the bits in their own bytes
-            *(uint4*)(LO + p0) = make_uint4((l8[0] & 0xFFFFu) | (pk[0] << 16), (l8[1] & 0xFFFFu) | (pk[1] << 16),
-                                            (l8[2] & 0xFFFFu) | (pk[2] << 16), (l8[3] & 0xFFFFu) | (pk[3] << 16));
-            *(uint4*)(LO + p0 + 4) = make_uint4((l8[4] & 0xFFFFu) | (pk[4] << 16), (l8[5] & 0xFFFFu) | (pk[5] << 16),
-                                                (l8[6] & 0xFFFFu) | (pk[6] << 16), (l8[7] & 0xFFFFu) | (pk[7] << 16));
-            *(uint2*)(IM + p0) = make_uint2(
-                ((pk[0] >> 16) & 0xFFu) | ((pk[1] >> 8) & 0xFF00u) | (pk[2] & 0xFF0000u) | ((pk[3] << 8) & 0xFF000000u),
-                ((pk[4] >> 16) & 0xFFu) | ((pk[5] >> 8) & 0xFF00u) | (pk[6] & 0xFF0000u) | ((pk[7] << 8) & 0xFF000000u));
+            uint32_t w[8];
+#pragma unroll
+            for (uint32_t q = 0; q < 8u; ++q) w[q] = perm(ex2[q / 2u], l8[q], (q & 1u) ? 0x07060100u : 0x05040100u);
+            *(uint4*)(LO + p0) = make_uint4(w[0], w[1], w[2], w[3]);
+            *(uint4*)(LO + p0 + 4) = make_uint4(w[4], w[5], w[6], w[7]);
+            *(uint2*)(IM + p0) = make_uint2(I[0], I[1]);
           } else {
-            *(uint4*)(XQ + p0) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-            *(uint4*)(XQ + p0 + 4) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+            // exit | item-start bits << 16
+            uint32_t w[8];
+#pragma unroll
+            for (uint32_t q = 0; q < 8u; ++q) {
+              const uint32_t eb = (q & 1u) ? 0x0302u : 0x0100u;           // the exit's two bytes
+              const uint32_t ib = 0x04u + (q & 3u);                        // byte q & 3 of I
+              w[q] = perm(I[q / 4u], ex2[q / 2u], 0x0c000000u | (ib << 16) | eb);
+            }
+            *(uint4*)(XQ + p0) = make_uint4(w[0], w[1], w[2], w[3]);
+            *(uint4*)(XQ + p0 + 4) = make_uint4(w[4], w[5], w[6], w[7]);
           }
           ((uint8_t*)LMB)[sg] = (uint8_t)lmb;
         }
