@@ -934,6 +934,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             *(uint4*)(XQ + p0 + 4) = make_uint4(w[4], w[5], w[6], w[7]);
           }
           ((uint8_t*)LMB)[sg] = (uint8_t)lmb;
+          ((uint8_t*)ISB)[sg] = 0;  // segments the parse passes get their bits in step (iii)
         }
         team_sync<WPC>();
         // (b) hops: the parse's real entry into every segment it passes through
@@ -986,18 +987,17 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
               }
             }
             wave_sync();  // the long matches' lengths, before the rebuild reads them
-            uint64_t acc = 0;
             if (lane < NR && ent != 0xFFFFu) {
               // a segment's exit lies past its end, and a long match found in
               // a segment ends at least 16 positions on: each hop passes a
-              // segment
+              // segment, whose item-start byte it writes
               const uint32_t wend = 64u * (lane + 1u);
               uint32_t Q = ent;
 #pragma unroll
               for (uint32_t h = 0; h < 8u; ++h) {
                 if (Q < wend) {
                   const uint32_t xq = xq_at(Q);
-                  acc |= (uint64_t)((xq >> 16) & 0xFFu) << (Q & 56u);
+                  ((uint8_t*)ISB)[Q >> 3] = (uint8_t)(xq >> 16);
                   uint32_t X = xq & 0xFFFFu;
                   if (L::LAZY && (X & kLongExit)) {
                     const uint32_t r = X & ~kLongExit;
@@ -1008,7 +1008,6 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
                 }
               }
             }
-            if (lane < NR) ((uint64_t*)ISB)[lane] = acc;
           }
           team_sync<WPC>();
         } else {
@@ -1061,7 +1060,6 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
                 P = (w & 1u) ? v >> 16 : v & 0xFFFFu;
               }
             }
-            uint64_t acc = 0;
             if (lane < NR && ent != 0xFFFFu) {
               const uint32_t wend = 64u * (lane + 1u);
               uint32_t Q = ent;
@@ -1069,12 +1067,11 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
               for (uint32_t h = 0; h < 8u; ++h) {
                 if (Q < wend) {
                   const uint32_t xq = XQ[Q];
-                  acc |= (uint64_t)(xq >> 16) << (Q & 56u);
+                  ((uint8_t*)ISB)[Q >> 3] = (uint8_t)(xq >> 16);
                   Q = xq & 0xFFFFu;
                 }
               }
             }
-            if (lane < NR) ((uint64_t*)ISB)[lane] = acc;
           }
           team_sync<WPC>();
         }
