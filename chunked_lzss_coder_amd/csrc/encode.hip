@@ -934,7 +934,7 @@ __global__ __launch_bounds__(64 * WPC * CPW) void encode_kernel(const uint8_t* _
             *(uint4*)(XQ + p0 + 4) = make_uint4(w[4], w[5], w[6], w[7]);
           }
           ((uint8_t*)LMB)[sg] = (uint8_t)lmb;
-          ((uint8_t*)ISB)[sg] = 0;  // segments the parse passes get their bits in step (iii)
+          ((uint8_t*)ISB)[sg] = 0;  // the rebuild below sets the bytes of the segments the parse passes
         }
         team_sync<WPC>();
         // (b) hops: the parse's real entry into every segment it passes through
