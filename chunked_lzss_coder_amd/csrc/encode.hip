@@ -279,7 +279,7 @@ struct Lay {
   //       from each position, a byte each
   //   ISB | LMB (E/32 each) the item-start and match bits of each segment,
   //       a byte each
-  // so a two-chunk workgroup of 512-element chunks takes under 10 KB of LDS.
+  // so a 512-element chunk takes under 5 KB of LDS.
   static constexpr bool LAZY = LEVEL == 0 && W == 32 && E <= 1024;
   static constexpr uint32_t WPC_ = E <= 512 ? 1u : (uint32_t)E / 512u;  // waves per chunk (launch_one)
   static constexpr uint32_t LZ_T4 = E + 16u;
@@ -1697,10 +1697,12 @@ hipError_t launch_advancing(const EncodeArgs& a, hipStream_t stream) {
 
 template <int WS, int E, int LEVEL, int W>
 hipError_t launch_one(const EncodeArgs& a, hipStream_t stream) {
-  // waves per chunk: one up to 512 elements (two chunks per workgroup), then
-  // one per 512 elements, so LDS per wave stays the same and occupancy holds
+  // waves per chunk: one up to 512 elements (four chunks per workgroup at
+  // level 0, two at level 1, whose larger layout would leave fewer waves per
+  // CU in four-chunk workgroups), then one per 512 elements, so LDS per wave
+  // stays the same and occupancy holds
   constexpr int WPC = E <= 512 ? 1 : E / 512;
-  constexpr int CPW = E <= 512 ? 2 : 1;
+  constexpr int CPW = E <= 512 ? (LEVEL == 0 ? 4 : 2) : 1;
   constexpr uint32_t threads = 64u * WPC * CPW;
   const uint32_t grid = (a.num_chunks + CPW - 1) / CPW;  // one chunk per team
   hipLaunchKernelGGL((encode_kernel<WS, E, LEVEL, W, WPC, CPW>), dim3(grid), dim3(threads), 0, stream, a.in, a.n,
